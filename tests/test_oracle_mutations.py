@@ -1,0 +1,159 @@
+"""Planted mistakes in the oracle (CPU only): each plausible slip must fail at least one pin.
+
+Every case swaps one oracle function for a copy carrying a single mistake, runs the pins
+that should catch it, and asserts that at least one of them fails.  Nothing here touches
+the HIP path.
+"""
+import numpy as np
+import pytest
+
+import oracle.attention as att
+import oracle.pool as opool
+import tests.test_oracle_attention as TA
+import tests.test_oracle_pool as TP
+
+
+def _fails(*pins):
+    failed = 0
+    for pin in pins:
+        try:
+            pin()
+        except (AssertionError, IndexError, ValueError, opool.OutOfBlocks, opool.InvalidOp):
+            failed += 1
+    return failed
+
+
+def _softmax_no_scale(q, K, V, scale):
+    s = K @ q
+    s = s - s.max()
+    e = np.exp(s)
+    w = e / e.sum()
+    return w @ V, w
+
+
+def _softmax_sign_flip(q, K, V, scale):
+    s = -scale * (K @ q)
+    s = s - s.max()
+    e = np.exp(s)
+    w = e / e.sum()
+    return w @ V, w
+
+
+def _gather_v_untransposed(cache, table, L):
+    bs = cache.bs
+    nb = -(-int(L) // bs)
+    blocks = np.asarray(table[:nb], dtype=np.int64)
+    k = cache.k[blocks]
+    v = cache.v[blocks]
+    K = k.transpose(1, 0, 2, 3).reshape(cache.H, nb * bs, cache.D)[:, :L]
+    V = v.transpose(1, 0, 2, 3).reshape(cache.H, nb * bs, cache.D)[:, :L]  # wrong axis order
+    return att.bits_to_f64(K, cache.dtype), att.bits_to_f64(V, cache.dtype)
+
+
+def _decode_gqa_modulo(q_bits, cache, tables, lens, scale, return_weights=False):
+    q = att.bits_to_f64(q_bits, cache.dtype)
+    B, Hq, D = q.shape
+    out = np.zeros((B, Hq, D))
+    for b in range(B):
+        K, V = att.gather(cache, tables[b], int(lens[b]))
+        for h in range(Hq):
+            g = h % cache.H  # wrong head mapping
+            out[b, h], _ = att.softmax_attention(q[b, h], K[g], V[g], scale)
+    return out
+
+
+def _prefill_off_by_one(q_bits, cache, table, ctx_start, scale):
+    q = att.bits_to_f64(q_bits, cache.dtype)
+    C, Hq, D = q.shape
+    G = Hq // cache.H
+    K, V = att.gather(cache, table, ctx_start + C)
+    out = np.zeros((C, Hq, D))
+    for i in range(C):
+        n = max(1, ctx_start + i)  # drops the diagonal
+        for h in range(Hq):
+            out[i, h], _ = att.softmax_attention(q[i, h], K[h // G, :n], V[h // G, :n], scale)
+    return out
+
+
+@pytest.mark.parametrize("mutant", [_softmax_no_scale, _softmax_sign_flip])
+def test_softmax_mutants_caught(monkeypatch, mutant):
+    monkeypatch.setattr(att, "softmax_attention", mutant)
+    assert _fails(TA.test_matches_torch_sdpa_fp64, TA.test_two_token_closed_form,
+                  TA.test_huge_scale_selects_argmax_token) >= 1
+
+
+def test_untransposed_v_caught(monkeypatch):
+    monkeypatch.setattr(att, "gather", _gather_v_untransposed)
+    assert _fails(TA.test_gather_round_trip_recovers_tokens_in_order,
+                  lambda: TA.test_numpy_oracle_equals_brute_force("bf16", 4, 2, 8)) >= 1
+
+
+def test_tail_read_caught(monkeypatch):
+    orig = att.gather
+
+    def reads_tail(cache, table, L):
+        nb = -(-int(L) // cache.bs)
+        return orig(cache, list(table) + [], nb * cache.bs)
+
+    monkeypatch.setattr(att, "gather", reads_tail)
+    assert _fails(TA.test_stale_tail_slots_are_never_read, TA.test_matches_torch_sdpa_fp64) >= 1
+
+
+def test_gqa_mapping_mutant_caught(monkeypatch):
+    monkeypatch.setattr(att, "paged_decode", _decode_gqa_modulo)
+    assert _fails(TA.test_gqa_equals_mha_on_repeated_kv,
+                  lambda: TA.test_numpy_oracle_equals_brute_force("bf16", 8, 2, 4)) >= 1
+
+
+def test_causal_off_by_one_caught(monkeypatch):
+    monkeypatch.setattr(att, "prefill_chunk", _prefill_off_by_one)
+    assert _fails(TA.test_prefill_rows_equal_decodes_and_sdpa_causal,
+                  TA.test_prefill_first_row_of_empty_context_returns_v) >= 1
+
+
+def test_fifo_free_list_caught(monkeypatch):
+    def fifo_alloc(self):
+        if not self.free:
+            raise opool.OutOfBlocks()
+        b = self.free.pop(0)
+        self.refcnt[b] = 1
+        return b
+
+    monkeypatch.setattr(opool.PoolModel, "_alloc", fifo_alloc)
+    assert _fails(TP.test_alloc_pops_from_end_of_free_list, TP.test_tiny_step_worked_tables,
+                  TP.test_free_returns_blocks_in_table_order) >= 1
+
+
+def test_missing_copy_on_write_caught(monkeypatch):
+    def blocks_needed_no_cow(self, seq, n):
+        start = self.lens[seq]
+        return sum(1 for pos in range(start, start + n) if pos % self.block_size == 0)
+
+    def append_in_place(self, seq, n):
+        need = blocks_needed_no_cow(self, seq, n)
+        if need > len(self.free):
+            raise opool.OutOfBlocks()
+        table = self.tables[seq]
+        slots = []
+        for _ in range(n):
+            pos = self.lens[seq]
+            if pos % self.block_size == 0:
+                table.append(self._alloc())
+            slots.append(table[pos // self.block_size] * self.block_size + pos % self.block_size)
+            self.lens[seq] = pos + 1
+        return slots, []
+
+    monkeypatch.setattr(opool.PoolModel, "append", append_in_place)
+    monkeypatch.setattr(opool.PoolModel, "blocks_needed", blocks_needed_no_cow)
+    assert _fails(TP.test_fork_shares_and_cow_isolates, TP.test_sixteen_samples_on_partial_prefix) >= 1
+
+
+def test_free_order_reversed_caught(monkeypatch):
+    def free_reversed(self, seq):
+        for b in reversed(self.tables[seq]):
+            self._release(b)
+        del self.tables[seq]
+        del self.lens[seq]
+
+    monkeypatch.setattr(opool.PoolModel, "free_seq", free_reversed)
+    assert _fails(TP.test_free_returns_blocks_in_table_order) >= 1

@@ -1,0 +1,273 @@
+"""Pins for the oracle's block pool and cache model (CPU).
+
+Each test checks the oracle against something other than itself: the worked numbers in
+tests/golden/ (derived by hand from the pages), closed forms, and invariants that hold for
+any operation sequence.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import CacheModel, InvalidOp, OutOfBlocks, PoolModel
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def test_alloc_pops_from_end_of_free_list():
+    # Serving, Step 4: the free list starts as every id and alloc takes the last one.
+    p = PoolModel(5)
+    s = p.new_seq()
+    slots, _ = p.append(s, 1)
+    assert p.tables[s] == [4]
+    assert slots == [4 * 16]
+    p.append(s, 16)
+    assert p.tables[s] == [4, 3]
+
+
+def test_free_returns_blocks_in_table_order():
+    # Serving, Step 4: finishing walks the page table in order and pushes each page back.
+    p = PoolModel(6, free_order=[0, 1, 2, 3, 4, 5])
+    s = p.new_seq()
+    p.append(s, 40)  # blocks 5, 4, 3
+    assert p.tables[s] == [5, 4, 3]
+    p.free_seq(s)
+    assert p.free == [0, 1, 2, 5, 4, 3]
+    t = p.new_seq()
+    p.append(t, 1)
+    assert p.tables[t] == [3]  # the last page pushed is the first handed out again
+
+
+def test_tiny_step_worked_tables():
+    g = _golden("pool_worked_examples.json")["tiny_step_tables"]
+    rng = np.random.default_rng(1)
+    P = rng.permutation(32)
+    pool = PoolModel(32, free_order=P)
+    seqs = [pool.new_seq() for _ in g["lens"]]
+    for s, L in zip(seqs, g["lens"]):
+        pool.append(s, L - 1)
+    step = [pool.append(s, 1)[0][0] for s in seqs]
+    tables, lens = pool.block_tables(seqs, 3)
+    want = [[int(P[i]) for i in row] for row in g["tables_as_free_order_index"]]
+    assert [[b for b in r if b >= 0] for r in tables] == want
+    assert lens == g["lens"]
+    assert pool.num_free() == g["free_after"]
+    assert step == [int(P[i]) * 16 + off for i, off in g["step_slots_as_index_and_offset"]]
+
+
+def test_contiguous_vs_paged_accounting():
+    g = _golden("pool_worked_examples.json")["contiguous_vs_paged"]
+    assert g["requests"] * g["max_len"] == g["reserved_tokens_contiguous"]
+    pool = PoolModel(2000)
+    for _ in range(g["requests"]):
+        s = pool.new_seq()
+        pool.append(s, g["mean_len"])
+    stored = sum(pool.lens.values())
+    allocated = (2000 - pool.num_free()) * 16
+    assert stored == g["stored_tokens"]
+    assert stored / g["reserved_tokens_contiguous"] == g["fraction_used_contiguous"]
+    assert abs(g["fraction_used_contiguous"] - g["page_fraction_used_printed"]) < 0.0013
+    assert allocated == g["paged_slots_allocated_when_every_len_is_200"]
+
+
+def test_tail_waste_bound_is_block_size_minus_one():
+    g = _golden("pool_worked_examples.json")["tail_waste_bound"]
+    worst = 0
+    for L in range(1, 200):
+        pool = PoolModel(20)
+        s = pool.new_seq()
+        pool.append(s, L)
+        waste = len(pool.tables[s]) * 16 - L
+        worst = max(worst, waste)
+        assert waste == (-L) % 16
+        if L % 16 == 1:
+            assert waste == g["max_waste_per_sequence"]
+    assert worst == g["max_waste_per_sequence"]
+    assert 100 * worst == g["max_waste_per_100_sequences"]
+
+
+def test_reserve_32k_use_2k():
+    g = _golden("pool_worked_examples.json")["reserve_32k_use_2k"]
+    assert 1 - g["used"] / g["reserved"] == g["fraction_empty"]
+    pool = PoolModel(200)
+    s = pool.new_seq()
+    pool.append(s, g["used"])
+    assert len(pool.tables[s]) == g["paged_blocks"]
+    assert len(pool.tables[s]) * 16 - g["used"] == g["paged_waste"]
+
+
+def test_out_of_blocks_is_all_or_nothing():
+    pool = PoolModel(3)
+    a = pool.new_seq()
+    pool.append(a, 20)  # 2 blocks
+    b = pool.new_seq()
+    before = (list(pool.free), list(pool.refcnt), {k: list(v) for k, v in pool.tables.items()}, dict(pool.lens))
+    with pytest.raises(OutOfBlocks):
+        pool.append(b, 17)  # needs 2, one free
+    after = (list(pool.free), list(pool.refcnt), {k: list(v) for k, v in pool.tables.items()}, dict(pool.lens))
+    assert before == after
+    pool.append(b, 16)  # exactly one block fits
+    with pytest.raises(OutOfBlocks):
+        pool.append(b, 1)
+
+
+def test_fork_shares_and_cow_isolates():
+    pool = PoolModel(10, free_order=list(range(10)))
+    p = pool.new_seq()
+    pool.append(p, 20)  # blocks 9 (full) and 8 (4 tokens)
+    c = pool.fork(p)
+    assert pool.tables[c] == [9, 8] and pool.refcnt[9] == 2 and pool.refcnt[8] == 2
+    slots, cow = pool.append(c, 1)
+    assert cow == [(8, 7)]
+    assert pool.tables[c] == [9, 7] and pool.tables[p] == [9, 8]
+    assert slots == [7 * 16 + 4]
+    assert pool.refcnt[8] == 1 and pool.refcnt[7] == 1 and pool.refcnt[9] == 2
+    # the parent now owns its partial block alone and writes in place
+    slots, cow = pool.append(p, 1)
+    assert cow == [] and slots == [8 * 16 + 4]
+
+
+def test_fork_on_block_boundary_never_copies():
+    pool = PoolModel(8)
+    p = pool.new_seq()
+    pool.append(p, 32)
+    c = pool.fork(p)
+    slots, cow = pool.append(c, 1)
+    assert cow == [] and len(pool.tables[c]) == 3 and pool.tables[c][:2] == pool.tables[p]
+
+
+def test_sixteen_samples_on_partial_prefix():
+    # 2,040-token prefix (last block 8/16 full) forked to 16 samples; appending in batch order,
+    # samples 0..14 copy the shared block and the last one finds refcount 1 and writes in place.
+    pool = PoolModel(200)
+    s0 = pool.new_seq()
+    pool.append(s0, 2040)
+    samples = [s0] + [pool.fork(s0) for _ in range(15)]
+    shared_last = pool.tables[s0][-1]
+    assert pool.refcnt[shared_last] == 16
+    cows = [pool.append(s, 1)[1] for s in samples]
+    assert all(len(c) == 1 and c[0][0] == shared_last for c in cows[:15])
+    assert cows[15] == []
+    assert pool.tables[samples[15]][-1] == shared_last
+    assert pool.refcnt[shared_last] == 1
+
+
+def test_blocks_needed_matches_append():
+    rng = np.random.default_rng(7)
+    pool = PoolModel(400, free_order=rng.permutation(400))
+    seqs = [pool.new_seq() for _ in range(4)]
+    for _ in range(200):
+        s = seqs[rng.integers(len(seqs))]
+        n = int(rng.integers(0, 40))
+        need = pool.blocks_needed(s, n)
+        free0 = pool.num_free()
+        try:
+            pool.append(s, n)
+            assert free0 - pool.num_free() == need
+        except OutOfBlocks:
+            assert need > free0
+        if rng.random() < 0.2:
+            seqs.append(pool.fork(s))
+        if rng.random() < 0.1 and len(seqs) > 1:
+            v = seqs.pop(int(rng.integers(len(seqs))))
+            pool.free_seq(v)
+
+
+def _check_invariants(pool):
+    N = pool.num_blocks
+    free = pool.free
+    assert len(set(free)) == len(free)
+    held = set()
+    ref = [0] * N
+    for t in pool.tables.values():
+        for b in t:
+            ref[b] += 1
+            held.add(b)
+    assert held.isdisjoint(free)
+    assert held | set(free) == set(range(N))
+    assert ref == pool.refcnt
+    for s, t in pool.tables.items():
+        assert len(t) == -(-pool.lens[s] // pool.block_size)
+
+
+def test_random_operation_invariants():
+    rng = np.random.default_rng(11)
+    pool = PoolModel(64, free_order=rng.permutation(64))
+    live = []
+    for step in range(3000):
+        r = rng.random()
+        if r < 0.15 or not live:
+            live.append(pool.new_seq())
+        elif r < 0.25:
+            live.append(pool.fork(live[int(rng.integers(len(live)))]))
+        elif r < 0.40:
+            pool.free_seq(live.pop(int(rng.integers(len(live)))))
+        else:
+            s = live[int(rng.integers(len(live)))]
+            try:
+                _, cow = pool.append(s, int(rng.integers(1, 24)))
+                for old, new in cow:
+                    assert pool.refcnt[new] == 1
+            except OutOfBlocks:
+                pass
+        _check_invariants(pool)
+    for s in list(live):
+        pool.free_seq(s)
+    assert sorted(pool.free) == list(range(64))
+    assert all(c == 0 for c in pool.refcnt)
+
+
+def test_sequence_ids_lowest_free():
+    pool = PoolModel(4)
+    a, b, c = pool.new_seq(), pool.new_seq(), pool.new_seq()
+    assert (a, b, c) == (0, 1, 2)
+    pool.free_seq(b)
+    assert pool.new_seq() == 1
+    assert pool.fork(a) == 3
+
+
+def test_invalid_ops():
+    pool = PoolModel(4)
+    with pytest.raises(InvalidOp):
+        pool.append(5, 1)
+    with pytest.raises(InvalidOp):
+        pool.free_seq(0)
+    with pytest.raises(InvalidOp):
+        PoolModel(3, free_order=[0, 0, 1])
+    s = pool.new_seq()
+    pool.append(s, 3)
+    with pytest.raises(InvalidOp):
+        pool.block_tables([s], 0)
+
+
+def test_cache_layout_fixture():
+    g = _golden("cache_layout.json")
+    c = CacheModel(g["num_blocks"], g["num_kv_heads"], g["head_dim"], "f32", g["block_size"], fill_nan=True)
+    keys = np.array([t["k"] for t in g["tokens"]], dtype=np.float32).view(np.uint32)
+    vals = np.array([t["v"] for t in g["tokens"]], dtype=np.float32).view(np.uint32)
+    c.append(keys, vals, [t["slot"] for t in g["tokens"]])
+    kf, vf = c.k.view(np.float32), c.v.view(np.float32)
+    for e in g["expect_k"]:
+        assert kf[tuple(e["index"])] == e["value"]
+    for e in g["expect_v"]:
+        assert vf[tuple(e["index"])] == e["value"]
+    assert (~np.isnan(kf)).sum() == g["written_elements_per_tensor"]
+    assert (~np.isnan(vf)).sum() == g["written_elements_per_tensor"]
+    assert not (kf == 99).any() and not (vf == 99).any()
+
+
+def test_copy_blocks_whole_block():
+    rng = np.random.default_rng(3)
+    c = CacheModel(4, 2, 8, "bf16")
+    c.k[1] = rng.integers(0, 1 << 16, size=c.k[1].shape, dtype=np.uint16)
+    c.v[1] = rng.integers(0, 1 << 16, size=c.v[1].shape, dtype=np.uint16)
+    k1, v1, k2 = c.k[1].copy(), c.v[1].copy(), c.k[2].copy()
+    c.copy_blocks([(1, 3)])
+    assert (c.k[3] == k1).all() and (c.v[3] == v1).all()
+    assert (c.k[1] == k1).all() and (c.k[2] == k2).all()
