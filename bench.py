@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode-attention hot path on one MI355X.
+
+A step is one continuous-batching decode step of one attention layer over a batch that is
+already resident in HBM: the cache append of every sequence's new token (paged_cache_append)
+followed by paged decode attention over all cached tokens (partition kernel + log-sum-exp
+reduce).  Default workload: Llama-3-8B-shaped layer, 32 q / 8 kv heads of 128, bf16, batch 64,
+context lengths ~ U[128, 2048], 16-token blocks scattered through a shuffled pool, split-K over
+512-token partitions.
+
+Metric: effective KV+Q bytes per step / step time (GB/s), with KV = sum_b L_b * Hkv * D * 2 * 2 B
+(each cached token's K and V once per KV head) and Q = B * Hq * D * 2 B; also seqs*steps/s.
+Inputs rotate over R replicas of the caches (>= 1 GiB in total) so that the 256 MB last-level
+cache cannot serve repeated reads.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload llama|long]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attn: effective KV HBM GB/s (% of peak); seqs*steps/s"
+PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partitions_traffic.json")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", choices=["llama", "long"], default="llama")
+    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB of caches")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    p = os.path.join(ROOT, "paged_kv_cache_404_amd", "csrc", "decode.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the partition kernel from rocprofv3 counters, when they were taken
+    on the current kernel source; else None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    entry = rec.get(workload)
+    if not entry or entry.get("decode_hip_sha256") != source_digest():
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, seconds: float):
+    """The oracle (numpy fp64 gather + softmax attention) on a bounded sample of the same workload:
+    the first S sequences, inputs drawn on the host with the same generators."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import workloads as wl
+    from oracle import CacheModel, PoolModel
+    from oracle import attention as oatt
+
+    S = 8 if w.B >= 8 else w.B
+    lens = w.lens[:S]
+    need = sum(wl.blocks_for(int(L)) for L in lens)
+    rng = np.random.default_rng(1000 + w.seed)
+    N = need + 1
+    pool = PoolModel(N, 16, rng.permutation(N))
+    cache = CacheModel(N, w.Hkv, w.D, w.dtype, fill_nan=True)
+    seqs = []
+    for L in lens:
+        s = pool.new_seq()
+        slots, _ = pool.append(s, int(L))
+        cache.append(wl.normal_bits(rng, (int(L), w.Hkv, w.D), w.dtype),
+                     wl.normal_bits(rng, (int(L), w.Hkv, w.D), w.dtype), slots)
+        seqs.append(s)
+    q = wl.normal_bits(rng, (S, w.Hq, w.D), w.dtype)
+    tables, tl = pool.block_tables(seqs, max(len(pool.tables[s]) for s in seqs))
+    eb = wl.elem_bytes(w.dtype)
+    sample_bytes = int(np.sum(lens.astype(np.int64))) * w.Hkv * w.D * 2 * eb + S * w.Hq * w.D * eb
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oatt.paged_decode(q, cache, tables, tl, w.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    per_call = el / reps
+    return {
+        "value": round(sample_bytes / per_call / 1e9, 4),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{S} of {w.B} sequences ({int(np.sum(lens))} cached tokens, {sample_bytes} B KV+Q), numpy fp64 "
+                   f"gather + softmax attention, {reps} calls in {el:.1f} s; host has "
+                   f"{len(os.sched_getaffinity(0))} usable cores"),
+        "seqs_steps_per_s": round(S / per_call, 3),
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); this library "
+              "has no multi-GPU path in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_404_amd import BlockPool, ops
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.workload == "llama":
+        w = wl.llama_decode(2, partition_size=args.partition_size)
+    else:
+        w = wl.long_context_decode(4, partition_size=args.partition_size)
+
+    # Host pool + builders: the cached prefix, then this step's append (timed on the host).
+    pool = BlockPool(w.num_blocks, 16, w.free_order)
+    seqs = [pool.new_seq() for _ in range(w.B)]
+    st, _, _, _ = pool.append_many(seqs, [int(L) - 1 for L in w.lens])
+    assert st == 0
+    t0 = time.perf_counter()
+    st, _, step_slots, cow = pool.append_many(seqs, [1] * w.B)
+    tables, lens = pool.block_tables(seqs, w.max_blocks_per_seq)
+    host_us = (time.perf_counter() - t0) * 1e6
+    assert st == 0 and len(cow) == 0 and np.array_equal(lens, w.lens)
+
+    eb = wl.elem_bytes(w.dtype)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float16
+    cache_bytes = 2 * w.num_blocks * w.Hkv * 16 * w.D * eb
+    R = args.replicas or max(1, math.ceil((1 << 30) / cache_bytes))
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    tables_t = torch.from_numpy(tables).to(dev)
+    lens_t = torch.from_numpy(lens).to(dev)
+    slots_t = torch.from_numpy(step_slots).to(dev)
+    maxL = int(lens.max())
+    reps = []
+    for r in range(R):
+        k = torch.randn((w.num_blocks, w.Hkv, 16, w.D), generator=g, device=dev, dtype=torch.float32).to(tdt)
+        v = torch.randn((w.num_blocks, w.Hkv, w.D, 16), generator=g, device=dev, dtype=torch.float32).to(tdt)
+        q = torch.randn((w.B, w.Hq, w.D), generator=g, device=dev, dtype=torch.float32).to(tdt)
+        sk = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev, dtype=torch.float32).to(tdt)
+        sv = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev, dtype=torch.float32).to(tdt)
+        out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+        ws = ops.decode_workspace(w.B, w.Hq, w.D, maxL, w.partition_size, device=dev)
+        reps.append((ops.PreparedAppend(k, v, sk, sv, slots_t),
+                     ops.PreparedDecode(out, q, k, v, tables_t, lens_t, maxL, w.scale, w.partition_size, ws)))
+    torch.cuda.synchronize()
+
+    def step(i):
+        app, dec = reps[i % R]
+        app()
+        dec.partitions()
+        dec.reduce()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # Timed region: exactly K steps bracketed by synchronisation (one GPU: the barrier is a no-op).
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    # Per-kernel durations with HIP events on the launch stream (a second pass of K steps).
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        app, dec = reps[i % R]
+        e0, e1, e2, e3 = ev[i]
+        e0.record(stream)
+        app()
+        e1.record(stream)
+        dec.partitions()
+        e2.record(stream)
+        dec.reduce()
+        e3.record(stream)
+    torch.cuda.synchronize()
+    t_app = np.array([a.elapsed_time(b) for a, b, _, _ in ev]) * 1e3
+    t_part = np.array([b.elapsed_time(c) for _, b, c, _ in ev]) * 1e3
+    t_red = np.array([c.elapsed_time(d) for _, _, c, d in ev]) * 1e3
+
+    kv = w.kv_bytes()
+    qb = w.q_bytes()
+    step_bytes = kv + qb
+    ms_per_step = wall / args.steps * 1e3
+    value = step_bytes / (wall / args.steps) / 1e9
+    part_us = float(np.mean(t_part))
+    achieved = step_bytes / (part_us * 1e-6) / 1e9
+    traffic = measured_traffic(args.workload)
+
+    # Achievable streaming bandwidth: a plain device copy of 1 GiB.
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    c0 = time.perf_counter()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * (1 << 30) * 5 / (time.perf_counter() - c0) / 1e9
+    del src, dst
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": w.B,
+            "num_q_heads": w.Hq,
+            "num_kv_heads": w.Hkv,
+            "head_dim": w.D,
+            "block_size": 16,
+            "context_lens": f"seeded U[{int(w.lens.min())}..{int(w.lens.max())}] sum {int(w.lens.sum())}"
+            if args.workload == "llama" else f"{int(w.lens[0])} each",
+            "num_blocks": w.num_blocks,
+            "partition_size": w.partition_size,
+            "replicas": R,
+            "parallelism": "none (one GPU)",
+        },
+        "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
+        "seqs_steps_per_s": round(w.B / (wall / args.steps), 1),
+        "kv_plus_q_bytes_per_step": step_bytes,
+        "kernel_us": {"append": round(float(np.mean(t_app)), 3), "decode_partitions": round(part_us, 3),
+                      "decode_reduce": round(float(np.mean(t_red)), 3)},
+        "host_pool_and_builders_us_per_step": round(host_us, 1),
+        "device_copy_probe_gbs": round(copy_gbs, 1),
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "decode_mfma_kernel (partition pass)",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,242 @@
+/*
+ * pagedkv.h - C ABI of libpagedkv: paged KV-cache decode attention for AMD MI355X (gfx950).
+ *
+ * The method is PagedAttention as described in three pages on continuous batching:
+ *   [Serving] "Production Serving: Continuous Batching and PagedAttention" (llm-under-the-hood,
+ *             project 17), The Concept; The Build, Step 4 (paged KV cache), Step 6 (attention
+ *             over paged storage), Step 8 (prefix caching).
+ *   [Chapter] "Continuous batching and PagedAttention" (how-ai-works, chapter 7),
+ *             "How the scheduler works", "PagedAttention: KV cache memory".
+ *   [Notes]   "Continuous batching and PagedAttention: serving many users from one GPU"
+ *             (trefon notes), "Fragmentation: PagedAttention", "Prefill gets in the way".
+ *
+ * Every cached token of a sequence lives in a fixed 16-token physical block; a per-sequence block
+ * table maps logical block j to a physical block id; each continuous-batching step appends the
+ * step's K/V into slots and then attends over all cached tokens.
+ *
+ * Conventions shared by every call
+ *   - Return value: PKV_OK (0) or a negative status.  pkv_last_error() returns a thread-local
+ *     message for the last non-zero status of the calling thread.
+ *   - Device calls take device pointers owned by the caller, enqueue work on `stream` (a
+ *     hipStream_t; NULL = the default stream) and return without synchronising.  The library
+ *     never allocates or frees device memory.  Argument checks happen on the host before any
+ *     launch; a failed check launches nothing.  Launch failures return PKV_EHIP.
+ *   - Device array CONTENTS (block ids, lengths, slots) are preconditions that the host cannot
+ *     check without a synchronisation: block ids must lie in [0, num_blocks), 1 <= context length
+ *     <= max_context_len, and the slots of one append call must be distinct.
+ *   - Element types: PKV_F32, PKV_F16, PKV_BF16.  Queries, keys, values and caches of one call
+ *     share one element type (`dtype`).
+ *   - Cache layout (one layer; K and V are separate tensors, both indexed by physical block id):
+ *         k_cache [num_blocks][num_kv_heads][block_size][head_dim]   token rows
+ *         v_cache [num_blocks][num_kv_heads][head_dim][block_size]   head-dim rows
+ *     Slot s means block s / block_size, offset s % block_size.  One (block, head) tile of either
+ *     tensor is contiguous (4 KiB at 16 x 128 bf16), and a whole block is one contiguous span.
+ *   - Grouped-query attention: query head h reads KV head h / (num_q_heads / num_kv_heads).
+ *   - Supported kernel shapes: block_size 16, head_dim 64 or 128, num_q_heads / num_kv_heads in
+ *     {1, 2, 4, 8}.  Other values return PKV_EUNSUPPORTED.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_OK 0
+#define PKV_EINVAL (-1)       /* bad argument (null pointer, inconsistent sizes, unknown sequence) */
+#define PKV_ENOMEM (-2)       /* the block pool cannot cover an allocation ([Serving] Step 4's out-of-pages error) */
+#define PKV_EUNSUPPORTED (-3) /* shape or type the kernels do not implement */
+#define PKV_EHIP (-4)         /* a HIP runtime call or kernel launch failed */
+
+#define PKV_F32 0
+#define PKV_F16 1
+#define PKV_BF16 2
+
+typedef void* pkv_stream_t; /* hipStream_t */
+
+/* Thread-local message describing the last non-zero status returned to this thread. */
+const char* pkv_last_error(void);
+
+/* Library version, as major * 10000 + minor * 100 + patch. */
+int32_t pkv_version(void);
+
+/* ============================== device operations ============================== */
+
+/*
+ * paged_cache_append - scatter one call's K/V tokens into their slots.
+ * [Serving] Step 4: token `pos` of a sequence is written at (page, pos % block_size) of the
+ * page its page table names.  The slot of every token is computed on the host
+ * (pkv_seq_append / pkv_build_slot_mapping); this call only moves bytes.
+ *
+ *   k_cache, v_cache  device, layout above; written at the given slots only.
+ *   key, value        device, token t at key + t * key_stride elements, laid out [num_kv_heads][head_dim]
+ *                     (a stride of 0 means num_kv_heads * head_dim, i.e. contiguous [T][Hkv][D]).
+ *   slot_mapping      device int32 [T]; slot = block * block_size + offset; -1 skips the token.
+ *   T                 tokens in this call (0 is a no-op).
+ * Bit-exact copy; no arithmetic.  Slots must be distinct and < num_blocks * block_size.
+ */
+int paged_cache_append(void* k_cache, void* v_cache, const void* key, const void* value,
+                       int64_t key_stride, int64_t value_stride, const int32_t* slot_mapping,
+                       int32_t T, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                       int32_t num_blocks, int32_t dtype, pkv_stream_t stream);
+
+/*
+ * paged_cache_copy_blocks - whole-block copy of K and V for copy-on-write.
+ * [Chapter] "PagedAttention: KV cache memory" and [Notes] "Fragmentation: PagedAttention":
+ * sequences share physical blocks until they diverge; the block a sequence is about to write
+ * while others still hold it is first copied (pkv_seq_append reports the pair).
+ *
+ *   src_dst   device int32 [n][2] = (source block, destination block) pairs, applied as one
+ *             batch: no destination may be the source of another pair in the same call.
+ * Copies every head and every slot of the block (stale tail slots included).  Bit-exact.
+ */
+int paged_cache_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst, int32_t n,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                            int32_t num_blocks, int32_t dtype, pkv_stream_t stream);
+
+/*
+ * paged_attention_decode_workspace_bytes - device workspace paged_attention_decode needs.
+ * 0 when partition_size is 0 (single pass).  Otherwise room for one (max, sum, unnormalised
+ * output) partial per (sequence, query head, partition).
+ */
+size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                              int32_t max_context_len, int32_t partition_size);
+
+/*
+ * paged_attention_decode - one decode step of attention over the paged cache.
+ * [Serving] Step 6: for every query head, score every cached token of its sequence (query . key
+ * times `scale`), softmax the scores, and sum the values with those weights.  Only the first
+ * context_lens[b] tokens take part; the unused tail of the last block is never read.
+ *
+ *   out            device [B][num_q_heads][head_dim] of out_dtype (PKV_F32 or `dtype`).
+ *   query          device [B][num_q_heads][head_dim] of `dtype`.
+ *   k_cache/v_cache device, layout above.
+ *   block_tables   device int32 [B][max_blocks_per_seq]; row b lists sequence b's physical blocks
+ *                  in logical order; entries past ceil(context_lens[b] / block_size) are not read.
+ *   context_lens   device int32 [B]; tokens of sequence b, counting this step's appended token.
+ *   max_context_len host-known upper bound of context_lens (sizes the grid without a sync);
+ *                  must not exceed max_blocks_per_seq * block_size.
+ *   scale          score multiplier (1 / sqrt(head_dim) in the usual case).
+ *   partition_size 0: one pass per (sequence, KV head).  Otherwise a multiple of block_size:
+ *                  the context is cut into fixed partitions of that many tokens, each processed
+ *                  independently, and the partial softmaxes are merged exactly (log-sum-exp).
+ *                  Partition boundaries depend only on the token position, never on the batch.
+ *   workspace      device scratch of at least paged_attention_decode_workspace_bytes(...) bytes
+ *                  (may be NULL when that is 0); contents on entry do not matter.
+ * Accumulation is fp32 whatever the input type.
+ */
+int paged_attention_decode(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                           const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                           int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                           int32_t max_context_len, float scale, int32_t partition_size,
+                           void* workspace, size_t workspace_bytes, int32_t dtype, pkv_stream_t stream);
+
+/*
+ * paged_attention_decode_partitions / paged_attention_decode_reduce - the two launches of
+ * paged_attention_decode when partition_size > 0, exposed separately (same arguments) so that a
+ * caller can time or overlap them.  _partitions writes out[b] directly for every sequence that
+ * fits in one partition and writes partials to the workspace for the others; _reduce merges the
+ * partials of those others.  Calling _partitions then _reduce on one stream equals
+ * paged_attention_decode.
+ */
+int paged_attention_decode_partitions(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables,
+                                      const int32_t* context_lens, int32_t B, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                      int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+                                      float scale, int32_t partition_size, void* workspace,
+                                      size_t workspace_bytes, int32_t dtype, pkv_stream_t stream);
+int paged_attention_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, int32_t B,
+                                  int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                                  int32_t partition_size, const void* workspace, size_t workspace_bytes,
+                                  pkv_stream_t stream);
+
+/*
+ * paged_attention_prefill_chunk - causal attention of one prompt chunk against the paged cache.
+ * [Chapter] "How the scheduler works" and [Notes] "Prefill gets in the way": a long prompt is
+ * prefilled in chunks that fit a per-step token budget.  Row i of the chunk sits at absolute
+ * position ctx_start + i and attends to positions 0 .. ctx_start + i of its sequence.  The
+ * chunk's own K/V must already be appended (paged_cache_append) before this call.
+ *
+ *   out         device [C][num_q_heads][head_dim] of out_dtype (PKV_F32 or `dtype`).
+ *   query       device [C][num_q_heads][head_dim] of `dtype` (PKV_F16 or PKV_BF16).
+ *   block_table device int32 [>= ceil((ctx_start + C) / block_size)] of the one sequence.
+ * Accumulation is fp32; the products run on the matrix cores.
+ */
+int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                  const void* v_cache, const int32_t* block_table, int32_t ctx_start,
+                                  int32_t C, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t block_size, int32_t num_blocks, float scale, int32_t dtype,
+                                  pkv_stream_t stream);
+
+/* ============================== host block pool ============================== */
+/*
+ * [Serving] Step 4: a pool of physical block ids with a free list; allocation takes the id at the
+ * END of the free list and fails when it is empty; freeing puts the id back at the end; a
+ * sequence owns a block table and a token count; the token at position pos opens a new block when
+ * pos % block_size == 0.  Sharing with copy-on-write per [Chapter] "PagedAttention: KV cache
+ * memory" and [Notes] "Fragmentation: PagedAttention":
+ *   - fork gives a new sequence the parent's table and length and one more reference per block;
+ *   - an append whose first token lands in a partially filled last block with refcount > 1 takes
+ *     a fresh block, reports (old, new) for paged_cache_copy_blocks, and drops one reference of old;
+ *   - free drops one reference per block in table order and returns a block to the free list
+ *     when its count reaches 0.
+ * Appends are all-or-nothing: PKV_ENOMEM leaves the pool unchanged.  Sequence ids are the lowest
+ * id not currently live.  The pool is host memory only, synchronous, and not thread-safe per
+ * handle (different handles are independent).  It never touches the GPU.
+ */
+typedef struct pkv_pool pkv_pool;
+
+/* free_order: NULL = 0..num_blocks-1, else a permutation of 0..num_blocks-1 (copied). */
+int pkv_pool_create(int32_t num_blocks, int32_t block_size, const int32_t* free_order, pkv_pool** out);
+void pkv_pool_destroy(pkv_pool* pool);
+int pkv_pool_num_free(const pkv_pool* pool, int32_t* out);
+/* Copies the free list (bottom to top; the next allocation takes the last entry); *n = its length. */
+int pkv_pool_free_list(const pkv_pool* pool, int32_t* out, int32_t capacity, int32_t* n);
+int pkv_pool_refcount(const pkv_pool* pool, int32_t block, int32_t* out);
+
+int pkv_seq_new(pkv_pool* pool, int32_t* seq_id);
+int pkv_seq_fork(pkv_pool* pool, int32_t parent, int32_t* child);
+/* Fresh blocks an append of n tokens would take, including a copy-on-write block. */
+int pkv_seq_blocks_needed(const pkv_pool* pool, int32_t seq, int32_t n, int32_t* out);
+/*
+ * Reserve slots for n tokens of seq.  slots_out: host int32 [n].  cow_src_dst_out: host int32 [2],
+ * written when *n_cow == 1 (at most one copy per append).  n == 0 is a no-op.
+ */
+int pkv_seq_append(pkv_pool* pool, int32_t seq, int32_t n, int32_t* slots_out, int32_t* cow_src_dst_out,
+                   int32_t* n_cow);
+/*
+ * Batched append, sequence by sequence in the given order; each append is all-or-nothing.  On
+ * PKV_ENOMEM, *done = the index of the sequence that did not fit (earlier ones are applied).
+ * slots_out: host int32 [sum(counts)] in batch order; cow_out: host int32 [n][2];
+ * *n_cow = pairs written.
+ */
+int pkv_seqs_append(pkv_pool* pool, const int32_t* seqs, const int32_t* counts, int32_t n,
+                    int32_t* slots_out, int32_t* cow_out, int32_t* n_cow, int32_t* done);
+int pkv_seq_free(pkv_pool* pool, int32_t seq);
+int pkv_seq_len(const pkv_pool* pool, int32_t seq, int32_t* out);
+int pkv_seq_num_blocks(const pkv_pool* pool, int32_t seq, int32_t* out);
+
+/*
+ * Block tables: tables_out host int32 [n][max_blocks], row b = the physical blocks of seqs[b] in
+ * logical order padded with -1; lens_out host int32 [n] (may be NULL) = tokens of each.
+ * PKV_EINVAL if a table is longer than max_blocks.
+ */
+int pkv_build_block_tables(const pkv_pool* pool, const int32_t* seqs, int32_t n, int32_t max_blocks,
+                           int32_t* tables_out, int32_t* lens_out);
+/*
+ * Slot mapping: for each b, the slots of positions [starts[b], starts[b] + counts[b]) of seqs[b],
+ * concatenated in batch order into slots_out (host int32 [sum(counts)]):
+ * slot = table[pos / block_size] * block_size + pos % block_size.  Positions must be stored.
+ */
+int pkv_build_slot_mapping(const pkv_pool* pool, const int32_t* seqs, const int32_t* starts,
+                           const int32_t* counts, int32_t n, int32_t* slots_out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PAGEDKV_H */

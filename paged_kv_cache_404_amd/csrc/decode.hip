@@ -1,0 +1,618 @@
+// Paged decode attention: block-table gather, scaled Q.K, online softmax, P.V, GQA groups, and a
+// split-K partition + log-sum-exp reduce for long contexts.
+//
+// What is computed ([Serving] "Production Serving: Continuous Batching and PagedAttention", The
+// Build, Step 6): for each sequence b and query head h, every cached token t < L_b is scored
+// s_t = scale * <q_{b,h}, K_{g,t}> against KV head g = h / (Hq / Hkv); the scores are
+// softmaxed and the output is sum_t w_t V_{g,t}.  Tokens are found through the block table;
+// the unused tail of the last block is skipped, never multiplied by zero (stale slots may hold
+// NaN).
+//
+// Split-K: the context is cut into fixed partitions of `part_size` tokens (boundaries depend on
+// the position only).  Each partition keeps the usual online-softmax state (reference maximum m,
+// sum l, unnormalised output o); partitions of one (sequence, head) are merged exactly:
+// M = max_p m_p, out = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+//
+// MI355X mapping (bf16 / fp16): one wavefront handles 32 tokens (two 16-token blocks) of one KV
+// head per step.  The GQA group's query rows share every K/V tile load.  Both products run on the
+// matrix cores with v_mfma_f32_16x16x32_{bf16,f16}:
+//   S^T[token][head] = K[token][:] . Q[head][:]      (A = K rows, B = Q^T, heads padded to 16)
+//   O[row][d]       += P[row][token] . V[token][d]    (A = P rows, B = V^T tile)
+// The V cache is stored dim-major per block ([D][16]) so that eight consecutive tokens of one
+// dimension are one 16-byte load, which is what the P.V operand wants.  The softmax weights are
+// fed as two 16-bit rows, hi = round(p) and lo = round(p - hi), in the padding rows of the same
+// MFMA, so P.V keeps ~16 mantissa bits at no extra matrix instruction.  Scores use exp2 with
+// log2(e) folded into the scale; the running maximum is only raised when a score exceeds it by
+// more than 2^8 (lazy rescaling: exact, and p stays <= 256), which makes rescaling rare.
+#include <cmath>
+#include <type_traits>
+
+#include "device.h"
+
+namespace pkv {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyRescaleLog2 = 8.0f;
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* part_ml;  // [B][Hq][max_parts][2] (m, l)
+  float* part_o;   // [B][Hq][max_parts][D]
+  int32_t Hq;
+  int32_t Hkv;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t max_parts;
+  int32_t part_size;  // tokens per partition, multiple of 16
+  float scale_log2;   // scale * log2(e)
+};
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Float -> 16-bit pattern of the MFMA input type (round to nearest even) and back.
+template <int DT>
+__device__ __forceinline__ uint32_t to16(float x) {
+  if constexpr (DT == PKV_BF16) {
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+  } else {
+    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  }
+}
+template <int DT>
+__device__ __forceinline__ float from16(uint32_t b) {
+  if constexpr (DT == PKV_BF16) {
+    return bf16_bits_to_float(b);
+  } else {
+    return f16_bits_to_float(b);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == PKV_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+}
+
+// Zero the 16-bit elements i >= n of an 8-element fragment (n in [0, 8]).
+__device__ __forceinline__ u32x4 keep_first(u32x4 v, int n) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t m = (2 * w + 1 < n) ? 0xFFFFFFFFu : ((2 * w < n) ? 0x0000FFFFu : 0u);
+    v[w] &= m;
+  }
+  return v;
+}
+
+// Context length and block ids come from device arrays the host cannot check without a sync.
+// Out-of-contract values are clamped so that a bad input yields a wrong number, never a fault.
+__device__ __forceinline__ int clamp_len(const DecodeArgs& a, int b) {
+  return min(a.lens[b], min(a.max_parts * a.part_size, a.max_blocks * kBlock));
+}
+__device__ __forceinline__ int clamp_blk(const DecodeArgs& a, int blk) { return min(max(blk, 0), a.num_blocks - 1); }
+
+// Writes the merged state of one (sequence, query head) partition: the final output when the
+// sequence has a single partition, a partial otherwise.
+template <int DT_OUT>
+__device__ __forceinline__ void emit(const DecodeArgs& a, int b, int hq, int p, int nparts, int d, int D, float m,
+                                     float l, float acc) {
+  if (nparts == 1) {
+    store_from_float<DT_OUT>(a.out, (static_cast<int64_t>(b) * a.Hq + hq) * D + d, acc / l);
+  } else {
+    const int64_t row = (static_cast<int64_t>(b) * a.Hq + hq) * a.max_parts + p;
+    a.part_o[row * D + d] = acc;
+    if (d == 0) {
+      a.part_ml[row * 2] = m;
+      a.part_ml[row * 2 + 1] = l;
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Matrix-core kernel (bf16 / fp16).  grid = (max_parts, Hkv, B); NW waves share one partition.
+// ------------------------------------------------------------------------------------------
+template <int DT, int DT_OUT, int D, int G, int NW>
+__global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
+  constexpr int KS = D / 32;  // k-steps of Q.K
+  constexpr int NB = D / 16;  // 16-column blocks of P.V
+  constexpr int TILE = kBlock * D;  // elements of one (block, head) tile
+
+  const int p = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int L = clamp_len(a, b);
+  const int pstart = p * a.part_size;
+  if (pstart >= L) return;
+  const int pend = min(pstart + a.part_size, L);
+  const int nparts = (L + a.part_size - 1) / a.part_size;
+
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int n16 = lane & 15;
+  const int q4 = lane >> 4;
+
+  const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k);
+  const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v);
+  const int32_t* __restrict__ table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
+
+  // Q^T fragments: lane (head n16, group q4) holds Q[head][ks*32 + 8*q4 .. +8]; padded heads are 0.
+  u32x4 qf[KS];
+  {
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + (static_cast<int64_t>(b) * a.Hq + g * G + min(n16, G - 1)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = (n16 < G) ? *reinterpret_cast<const u32x4*>(qrow + ks * 32 + q4 * 8) : u32x4{0, 0, 0, 0};
+    }
+  }
+
+  // Token order inside a 32-token step: Q.K product #1 row m holds step token 8*(m/4) + m%4,
+  // product #2 row m holds that token + 4.  Then lane (head, q4) ends up with the scores of step
+  // tokens 8*q4 .. 8*q4+7, exactly the k-range its P row covers in P.V.
+  const int tok1 = 8 * (n16 >> 2) + (n16 & 3);
+  const int khalf = tok1 >> 4;  // which of the step's two blocks this lane's K rows live in
+  const int krow = tok1 & 15;
+  const int vhalf = q4 >> 1;  // which block this lane's V tokens live in
+  const int vcol = (q4 & 1) * 8;
+
+  f32x4 o[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // reference maximum (log2 domain), meaningful in lanes n16 < G
+  float l_run = 0.f;        // this lane's share of sum p
+
+  const int nsteps = (pend - pstart + 31) >> 5;
+  for (int st = w; st < nsteps; st += NW) {
+    const int t0 = pstart + st * 32;
+    const int nvalid = min(32, pend - t0);
+    const int lb = t0 >> 4;
+    const int blkA = clamp_blk(a, table[lb]);
+    const int blkB = nvalid > 16 ? clamp_blk(a, table[lb + 1]) : blkA;
+    const int64_t tileA = (static_cast<int64_t>(blkA) * a.Hkv + g) * TILE;
+    const int64_t tileB = (static_cast<int64_t>(blkB) * a.Hkv + g) * TILE;
+
+    const uint16_t* krow1 = kc + (khalf ? tileB : tileA) + krow * D + q4 * 8;
+    const uint16_t* krow2 = krow1 + 4 * D;
+    u32x4 k1[KS], k2[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      k1[ks] = *reinterpret_cast<const u32x4*>(krow1 + ks * 32);
+      k2[ks] = *reinterpret_cast<const u32x4*>(krow2 + ks * 32);
+    }
+    const uint16_t* vbase = vc + (vhalf ? tileB : tileA) + n16 * kBlock + vcol;
+    u32x4 vf[NB];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) vf[nb] = *reinterpret_cast<const u32x4*>(vbase + nb * 16 * kBlock);
+
+    f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s1 = mfma16x16x32<DT>(k1[ks], qf[ks], s1);
+      s2 = mfma16x16x32<DT>(k2[ks], qf[ks], s2);
+    }
+
+    // Lane (head n16, q4) now holds scores of step tokens 8*q4 + i, i = 0..7.
+    const int tb = 8 * q4;
+    float sc[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      sc[j] = (n16 < G && tb + j < nvalid) ? s1[j] * a.scale_log2 : -INFINITY;
+      sc[4 + j] = (n16 < G && tb + 4 + j < nvalid) ? s2[j] * a.scale_log2 : -INFINITY;
+    }
+    float bmax = sc[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sc[i]);
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+
+    const bool need = (n16 < G) && (bmax > m_run + kLazyRescaleLog2);
+    if (__any(need)) {
+      const float m_new = need ? bmax : m_run;
+      const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;
+      l_run *= alpha;
+      m_run = m_new;
+      // O row r = 4*q4 + j belongs to head r % G (hi rows r < G, lo rows G <= r < 2G).
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float f = __shfl(alpha, (4 * q4 + j) % G);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) o[nb][j] *= f;
+      }
+    }
+
+    float pv[8];
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      pv[i] = (n16 < G) ? fast_exp2(sc[i] - m_run) : 0.f;
+      psum += pv[i];
+    }
+    l_run += psum;
+
+    u32x4 hi, lo;
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      const uint32_t h0 = to16<DT>(pv[2 * wd]);
+      const uint32_t h1 = to16<DT>(pv[2 * wd + 1]);
+      const uint32_t l0 = to16<DT>(pv[2 * wd] - from16<DT>(h0));
+      const uint32_t l1 = to16<DT>(pv[2 * wd + 1] - from16<DT>(h1));
+      hi[wd] = h0 | (h1 << 16);
+      lo[wd] = l0 | (l1 << 16);
+    }
+    u32x4 pa;
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      const uint32_t lo_src = static_cast<uint32_t>(__shfl(static_cast<int>(lo[wd]), lane - G));
+      pa[wd] = (n16 < G) ? hi[wd] : ((n16 < 2 * G) ? lo_src : 0u);
+    }
+
+    if (nvalid < 32) {
+      const int keep = min(8, max(0, nvalid - tb));
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) vf[nb] = keep_first(vf[nb], keep);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[nb] = mfma16x16x32<DT>(pa, vf[nb], o[nb]);
+  }
+
+  // Per-head sums over the four lane groups.
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+
+  __shared__ float sO[NW][2 * G][D];
+  __shared__ float sM[NW][G];
+  __shared__ float sL[NW][G];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * q4 + j;
+      if (r < 2 * G) sO[w][r][nb * 16 + n16] = o[nb][j];
+    }
+  }
+  if (q4 == 0 && n16 < G) {
+    sM[w][n16] = m_run;
+    sL[w][n16] = l_run;
+  }
+  __syncthreads();
+
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int h = idx / D;
+    const int d = idx % D;
+    float M = sM[0][h];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sM[ww][h]);
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = fast_exp2(sM[ww][h] - M);  // waves without a step hold m = -inf -> 0
+      acc += f * (sO[ww][h][d] + sO[ww][G + h][d]);
+      lsum += f * sL[ww][h];
+    }
+    emit<DT_OUT>(a, b, g * G + h, p, nparts, d, D, M, lsum, acc);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Vector-ALU kernel (any element type; used for fp32).  grid = (max_parts, Hq, B), one wave.
+// Lane i scores token c0 + i of each 64-token chunk; each lane owns dims lane and lane + 64.
+// ------------------------------------------------------------------------------------------
+template <int DT, int DT_OUT, int D>
+__global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
+  const int p = blockIdx.x;
+  const int hq = blockIdx.y;
+  const int b = blockIdx.z;
+  const int G = a.Hq / a.Hkv;
+  const int g = hq / G;
+  const int L = clamp_len(a, b);
+  const int pstart = p * a.part_size;
+  if (pstart >= L) return;
+  const int pend = min(pstart + a.part_size, L);
+  const int nparts = (L + a.part_size - 1) / a.part_size;
+  const int lane = threadIdx.x;
+  const int32_t* table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
+
+  __shared__ float qs[D];
+  for (int d = lane; d < D; d += 64)
+    qs[d] = elem_to_float<DT>(a.q, (static_cast<int64_t>(b) * a.Hq + hq) * D + d) * a.scale_log2;
+  __syncthreads();
+
+  constexpr int DPL = (D + 63) / 64;  // dims per lane
+  float o[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) o[i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  for (int c0 = pstart; c0 < pend; c0 += 64) {
+    const int t = c0 + lane;
+    const bool valid = t < pend;
+    int64_t tile = 0;
+    int off = 0;
+    float s = -INFINITY;
+    if (valid) {
+      tile = (static_cast<int64_t>(clamp_blk(a, table[t / kBlock])) * a.Hkv + g) * kBlock * D;
+      off = t % kBlock;
+      float acc = 0.f;
+      for (int d = 0; d < D; ++d) acc += qs[d] * elem_to_float<DT>(a.k, tile + static_cast<int64_t>(off) * D + d);
+      s = acc;
+    }
+    const float m_new = fmaxf(m_run, wave_max(s));
+    const float alpha = fast_exp2(m_run - m_new);
+    const float pt = valid ? fast_exp2(s - m_new) : 0.f;
+    l_run = l_run * alpha + wave_sum(pt);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) o[i] *= alpha;
+    const int n = min(64, pend - c0);
+    for (int i = 0; i < n; ++i) {
+      const float pi = __shfl(pt, i);
+      const int64_t ti = __shfl(tile, i);
+      const int oi = __shfl(off, i);
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const int d = lane + 64 * k;
+        if (d < D) o[k] += pi * elem_to_float<DT>(a.v, ti + static_cast<int64_t>(d) * kBlock + oi);
+      }
+    }
+    m_run = m_new;
+  }
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) {
+    const int d = lane + 64 * k;
+    if (d < D) emit<DT_OUT>(a, b, hq, p, nparts, d, D, m_run, l_run, o[k]);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// Log-sum-exp merge of partitions.  grid = (Hq, B), D threads.
+// ------------------------------------------------------------------------------------------
+template <int DT_OUT>
+__global__ void __launch_bounds__(128) decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ part_ml,
+                                                            const float* __restrict__ part_o,
+                                                            const int32_t* __restrict__ lens, int32_t Hq, int32_t D,
+                                                            int32_t max_parts, int32_t part_size) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int d = threadIdx.x;
+  const int L = min(lens[b], max_parts * part_size);
+  const int nparts = (L + part_size - 1) / part_size;
+  if (nparts <= 1 || d >= D) return;
+  const int64_t row0 = (static_cast<int64_t>(b) * Hq + h) * max_parts;
+  const float* ml = part_ml + row0 * 2;
+  float M = -INFINITY;
+  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
+  float acc = 0.f, lsum = 0.f;
+  for (int p = 0; p < nparts; ++p) {
+    const float f = fast_exp2(ml[2 * p] - M);
+    acc += f * part_o[(row0 + p) * D + d];
+    lsum += f * ml[2 * p + 1];
+  }
+  store_from_float<DT_OUT>(out, (static_cast<int64_t>(b) * Hq + h) * D + d, acc / lsum);
+}
+
+// ------------------------------------------------------------------------------------------
+// Host side
+// ------------------------------------------------------------------------------------------
+struct Plan {
+  int32_t part_size;
+  int32_t max_parts;
+  size_t ml_bytes;
+  size_t need_bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+Plan make_plan(int32_t B, int32_t Hq, int32_t D, int32_t max_ctx, int32_t partition_size) {
+  Plan pl{};
+  if (partition_size <= 0) {
+    pl.part_size = ((max_ctx + kBlock - 1) / kBlock) * kBlock;
+    if (pl.part_size < kBlock) pl.part_size = kBlock;
+    pl.max_parts = 1;
+    pl.ml_bytes = 0;
+    pl.need_bytes = 0;
+  } else {
+    pl.part_size = partition_size;
+    pl.max_parts = (max_ctx + partition_size - 1) / partition_size;
+    pl.ml_bytes = align256(static_cast<size_t>(B) * Hq * pl.max_parts * 2 * sizeof(float));
+    pl.need_bytes = pl.ml_bytes + static_cast<size_t>(B) * Hq * pl.max_parts * D * sizeof(float);
+  }
+  return pl;
+}
+
+int validate(const char* fn, void* out, int32_t out_dtype, const void* query, const void* k_cache,
+             const void* v_cache, const int32_t* block_tables, const int32_t* context_lens, int32_t B, int32_t Hq,
+             int32_t Hkv, int32_t D, int32_t bs, int32_t max_blocks, int32_t num_blocks, int32_t max_ctx,
+             int32_t partition_size, const void* workspace, size_t workspace_bytes, int32_t dtype) {
+  if (!valid_dtype(dtype)) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
+  if (out_dtype != PKV_F32 && out_dtype != dtype)
+    return fail(PKV_EINVAL, "%s: out_dtype must be PKV_F32 or the input dtype", fn);
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || max_blocks < 0 || num_blocks <= 0 || max_ctx < 0)
+    return fail(PKV_EINVAL, "%s: bad sizes", fn);
+  if (Hq % Hkv != 0) return fail(PKV_EINVAL, "%s: num_q_heads %d not a multiple of num_kv_heads %d", fn, Hq, Hkv);
+  if (bs != kBlock) return fail(PKV_EUNSUPPORTED, "%s: block_size %d (kernels implement 16)", fn, bs);
+  if (D != 64 && D != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, D);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PKV_EUNSUPPORTED, "%s: group size %d", fn, G);
+  if (B > 65535 || Hq > 65535) return fail(PKV_EUNSUPPORTED, "%s: batch or head count above 65535", fn);
+  if (partition_size < 0 || partition_size % bs != 0)
+    return fail(PKV_EINVAL, "%s: partition_size %d must be 0 or a multiple of block_size", fn, partition_size);
+  if (static_cast<int64_t>(max_ctx) > static_cast<int64_t>(max_blocks) * bs)
+    return fail(PKV_EINVAL, "%s: max_context_len %d exceeds max_blocks_per_seq * block_size", fn, max_ctx);
+  if (B == 0) return PKV_OK;
+  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens)
+    return fail(PKV_EINVAL, "%s: NULL pointer", fn);
+  const Plan pl = make_plan(B, Hq, D, max_ctx, partition_size);
+  if (pl.need_bytes > 0 && (!workspace || workspace_bytes < pl.need_bytes))
+    return fail(PKV_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, pl.need_bytes, workspace_bytes);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(query) | reinterpret_cast<uintptr_t>(k_cache) |
+                       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(workspace);
+  if (al % 16 != 0) return fail(PKV_EINVAL, "%s: query, caches and workspace must be 16-byte aligned", fn);
+  return PKV_OK;
+}
+
+template <int DT, int DT_OUT, int D>
+int launch_valu(const DecodeArgs& a, int B, hipStream_t s) {
+  hipLaunchKernelGGL((decode_valu_kernel<DT, DT_OUT, D>), dim3(a.max_parts, a.Hq, B), dim3(64), 0, s, a);
+  return PKV_OK;
+}
+
+constexpr int kWavesPerWG = 4;
+
+template <int DT, int DT_OUT, int D, int G>
+int launch_mfma(const DecodeArgs& a, int B, hipStream_t s) {
+  hipLaunchKernelGGL((decode_mfma_kernel<DT, DT_OUT, D, G, kWavesPerWG>), dim3(a.max_parts, a.Hkv, B),
+                     dim3(kWavesPerWG * 64), 0, s, a);
+  return PKV_OK;
+}
+
+template <int DT, int DT_OUT, int D>
+int dispatch_group(const DecodeArgs& a, int B, hipStream_t s) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return launch_mfma<DT, DT_OUT, D, 1>(a, B, s);
+    case 2: return launch_mfma<DT, DT_OUT, D, 2>(a, B, s);
+    case 4: return launch_mfma<DT, DT_OUT, D, 4>(a, B, s);
+    default: return launch_mfma<DT, DT_OUT, D, 8>(a, B, s);
+  }
+}
+
+template <int DT, int DT_OUT>
+int dispatch_dim(const DecodeArgs& a, int D, int B, hipStream_t s) {
+  if constexpr (DT == PKV_F32) {
+    return D == 64 ? launch_valu<DT, DT_OUT, 64>(a, B, s) : launch_valu<DT, DT_OUT, 128>(a, B, s);
+  } else {
+    return D == 64 ? dispatch_group<DT, DT_OUT, 64>(a, B, s) : dispatch_group<DT, DT_OUT, 128>(a, B, s);
+  }
+}
+
+int launch_partitions(const DecodeArgs& a, int32_t dtype, int32_t out_dtype, int D, int B, hipStream_t s) {
+  const bool f32out = out_dtype == PKV_F32;
+  switch (dtype) {
+    case PKV_BF16:
+      return f32out ? dispatch_dim<PKV_BF16, PKV_F32>(a, D, B, s) : dispatch_dim<PKV_BF16, PKV_BF16>(a, D, B, s);
+    case PKV_F16:
+      return f32out ? dispatch_dim<PKV_F16, PKV_F32>(a, D, B, s) : dispatch_dim<PKV_F16, PKV_F16>(a, D, B, s);
+    default:
+      return dispatch_dim<PKV_F32, PKV_F32>(a, D, B, s);
+  }
+}
+
+int launch_reduce(void* out, int32_t out_dtype, const float* ml, const float* po, const int32_t* lens, int B, int Hq,
+                  int D, int max_parts, int part_size, hipStream_t s) {
+  const dim3 grid(Hq, B), block(D);
+  switch (out_dtype) {
+    case PKV_BF16:
+      hipLaunchKernelGGL(decode_reduce_kernel<PKV_BF16>, grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
+                         part_size);
+      break;
+    case PKV_F16:
+      hipLaunchKernelGGL(decode_reduce_kernel<PKV_F16>, grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
+                         part_size);
+      break;
+    default:
+      hipLaunchKernelGGL(decode_reduce_kernel<PKV_F32>, grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
+                         part_size);
+      break;
+  }
+  return PKV_OK;
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
+                                                         int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_context_len <= 0 || partition_size <= 0) return 0;
+  return make_plan(num_seqs, num_q_heads, head_dim, max_context_len, partition_size).need_bytes;
+}
+
+extern "C" int paged_attention_decode_partitions(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                                 const void* v_cache, const int32_t* block_tables,
+                                                 const int32_t* context_lens, int32_t B, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                 int32_t max_blocks_per_seq, int32_t num_blocks,
+                                                 int32_t max_context_len, float scale, int32_t partition_size,
+                                                 void* workspace, size_t workspace_bytes, int32_t dtype,
+                                                 pkv_stream_t stream) {
+  int st = validate("paged_attention_decode_partitions", out, out_dtype, query, k_cache, v_cache, block_tables,
+                    context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                    max_context_len, partition_size, workspace, workspace_bytes, dtype);
+  if (st != PKV_OK || B == 0 || max_context_len == 0) return st;
+  const Plan pl = make_plan(B, num_q_heads, head_dim, max_context_len, partition_size);
+  DecodeArgs a{};
+  a.out = out;
+  a.q = query;
+  a.k = k_cache;
+  a.v = v_cache;
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.part_ml = pl.need_bytes ? static_cast<float*>(workspace) : nullptr;
+  a.part_o = pl.need_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + pl.ml_bytes) : nullptr;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.max_blocks = max_blocks_per_seq;
+  a.num_blocks = num_blocks;
+  a.max_parts = pl.max_parts;
+  a.part_size = pl.part_size;
+  a.scale_log2 = scale * kLog2e;
+  launch_partitions(a, dtype, out_dtype, head_dim, B, as_stream(stream));
+  return check_launch("paged_attention_decode_partitions");
+}
+
+extern "C" int paged_attention_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, int32_t B,
+                                             int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
+                                             int32_t partition_size, const void* workspace, size_t workspace_bytes,
+                                             pkv_stream_t stream) {
+  if (B < 0 || num_q_heads <= 0 || (head_dim != 64 && head_dim != 128) || max_context_len < 0 || partition_size < 0)
+    return fail(PKV_EINVAL, "paged_attention_decode_reduce: bad sizes");
+  if (out_dtype != PKV_F32 && out_dtype != PKV_F16 && out_dtype != PKV_BF16)
+    return fail(PKV_EINVAL, "paged_attention_decode_reduce: unknown out_dtype %d", out_dtype);
+  if (partition_size % kBlock != 0)
+    return fail(PKV_EINVAL, "paged_attention_decode_reduce: partition_size must be a multiple of 16");
+  if (B == 0 || max_context_len == 0 || partition_size == 0) return PKV_OK;
+  const Plan pl = make_plan(B, num_q_heads, head_dim, max_context_len, partition_size);
+  if (pl.max_parts <= 1) return PKV_OK;
+  if (!out || !context_lens || !workspace || workspace_bytes < pl.need_bytes)
+    return fail(PKV_EINVAL, "paged_attention_decode_reduce: NULL pointer or workspace too small");
+  const float* ml = static_cast<const float*>(workspace);
+  const float* po = reinterpret_cast<const float*>(static_cast<const uint8_t*>(workspace) + pl.ml_bytes);
+  launch_reduce(out, out_dtype, ml, po, context_lens, B, num_q_heads, head_dim, pl.max_parts, pl.part_size,
+                as_stream(stream));
+  return check_launch("paged_attention_decode_reduce");
+}
+
+extern "C" int paged_attention_decode(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                      const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                      int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+                                      size_t workspace_bytes, int32_t dtype, pkv_stream_t stream) {
+  int st = paged_attention_decode_partitions(out, out_dtype, query, k_cache, v_cache, block_tables, context_lens, B,
+                                             num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                                             num_blocks, max_context_len, scale, partition_size, workspace,
+                                             workspace_bytes, dtype, stream);
+  if (st != PKV_OK) return st;
+  return paged_attention_decode_reduce(out, out_dtype, context_lens, B, num_q_heads, head_dim, max_context_len,
+                                       partition_size, workspace, workspace_bytes, stream);
+}

@@ -1,0 +1,169 @@
+"""torch-tensor wrappers over the device calls of libpagedkv (argument marshalling only).
+
+Every computation happens in the HIP kernels; these functions check dtype, device and
+contiguity, then pass raw pointers and the current HIP stream to the C ABI.
+"""
+from __future__ import annotations
+
+import torch
+
+from ._lib import PKV_BF16, PKV_F16, PKV_F32, check, lib
+
+_DT = {torch.float32: PKV_F32, torch.float16: PKV_F16, torch.bfloat16: PKV_BF16}
+
+
+def dtype_code(t: torch.dtype) -> int:
+    if t not in _DT:
+        raise TypeError(f"unsupported dtype {t}")
+    return _DT[t]
+
+
+def _dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def paged_cache_append(k_cache, v_cache, key, value, slot_mapping, stream=None) -> None:
+    """k_cache [N][Hkv][16][D], v_cache [N][Hkv][D][16]; key/value [T][Hkv][D]; slot_mapping int32 [T]."""
+    _dev(k_cache, v_cache, key, value, slot_mapping)
+    N, H, bs, D = k_cache.shape
+    if tuple(v_cache.shape) != (N, H, D, bs):
+        raise ValueError("v_cache must be [N][Hkv][D][block_size]")
+    if key.dtype != k_cache.dtype or value.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("key, value and caches must share one dtype")
+    if slot_mapping.dtype != torch.int32:
+        raise TypeError("slot_mapping must be int32")
+    T = slot_mapping.numel()
+    if key.shape != (T, H, D) or value.shape != (T, H, D):
+        raise ValueError("key/value must be [T][Hkv][D]")
+    check(lib.paged_cache_append(k_cache.data_ptr(), v_cache.data_ptr(), key.data_ptr(), value.data_ptr(), 0, 0,
+                                 slot_mapping.data_ptr(), T, H, D, bs, N, dtype_code(k_cache.dtype), _stream(stream)))
+
+
+def paged_cache_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
+    """src_dst int32 [n][2] on the GPU."""
+    _dev(k_cache, v_cache, src_dst)
+    N, H, bs, D = k_cache.shape
+    if src_dst.dtype != torch.int32 or src_dst.dim() != 2 or src_dst.shape[1] != 2:
+        raise ValueError("src_dst must be int32 [n][2]")
+    check(lib.paged_cache_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src_dst.data_ptr(), src_dst.shape[0],
+                                      H, D, bs, N, dtype_code(k_cache.dtype), _stream(stream)))
+
+
+def decode_workspace_bytes(B: int, Hq: int, D: int, max_context_len: int, partition_size: int) -> int:
+    return int(lib.paged_attention_decode_workspace_bytes(B, Hq, D, max_context_len, partition_size))
+
+
+def decode_workspace(B: int, Hq: int, D: int, max_context_len: int, partition_size: int, device="cuda"):
+    n = decode_workspace_bytes(B, Hq, D, max_context_len, partition_size)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale, partition_size,
+                 workspace):
+    _dev(out, query, k_cache, v_cache, block_tables, context_lens)
+    B, Hq, D = query.shape
+    N, Hkv, bs, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != (N, Hkv, D, bs):
+        raise ValueError("cache shapes do not match the query")
+    if out.shape != query.shape:
+        raise ValueError("out must be [B][Hq][D]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B][max_blocks], context_lens [B]")
+    if query.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("query and caches must share one dtype")
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    return (out.data_ptr(), dtype_code(out.dtype), query.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, bs, block_tables.shape[1], N,
+            int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes, dtype_code(k_cache.dtype))
+
+
+def paged_attention_decode(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                           partition_size=0, workspace=None, stream=None) -> None:
+    args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                        partition_size, workspace)
+    check(lib.paged_attention_decode(*args, _stream(stream)))
+
+
+def paged_attention_decode_partitions(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                                      partition_size, workspace, stream=None) -> None:
+    args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                        partition_size, workspace)
+    check(lib.paged_attention_decode_partitions(*args, _stream(stream)))
+
+
+def paged_attention_decode_reduce(out, context_lens, max_context_len, partition_size, workspace, stream=None) -> None:
+    _dev(out, context_lens, workspace)
+    B, Hq, D = out.shape
+    check(lib.paged_attention_decode_reduce(out.data_ptr(), dtype_code(out.dtype), context_lens.data_ptr(), B, Hq, D,
+                                            int(max_context_len), int(partition_size), workspace.data_ptr(),
+                                            workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def paged_attention_prefill_chunk(out, query, k_cache, v_cache, block_table, ctx_start, scale, stream=None) -> None:
+    """query/out [C][Hq][D]; block_table int32 [>= ceil((ctx_start + C) / 16)] of one sequence."""
+    _dev(out, query, k_cache, v_cache, block_table)
+    C, Hq, D = query.shape
+    N, Hkv, bs, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != (N, Hkv, D, bs) or out.shape != query.shape:
+        raise ValueError("shape mismatch")
+    if block_table.dtype != torch.int32:
+        raise TypeError("block_table must be int32")
+    if block_table.numel() * bs < ctx_start + C:
+        raise ValueError("block_table too short for ctx_start + C")
+    check(lib.paged_attention_prefill_chunk(out.data_ptr(), dtype_code(out.dtype), query.data_ptr(),
+                                            k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
+                                            int(ctx_start), C, Hq, Hkv, D, bs, N, float(scale),
+                                            dtype_code(k_cache.dtype), _stream(stream)))
+
+
+class PreparedDecode:
+    """Decode call with its arguments marshalled once, for tight step loops: each call is one
+    C-ABI call (the tensors must stay alive and unchanged in shape)."""
+
+    def __init__(self, out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                 partition_size=0, workspace=None, stream=None):
+        self._keep = (out, query, k_cache, v_cache, block_tables, context_lens, workspace)
+        self.args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                                 partition_size, workspace)
+        self.stream = _stream(stream)
+        B, Hq, D = query.shape
+        self.reduce_args = (out.data_ptr(), dtype_code(out.dtype), context_lens.data_ptr(), B, Hq, D,
+                            int(max_context_len), int(partition_size), self.args[17], self.args[18])
+
+    def __call__(self) -> None:
+        check(lib.paged_attention_decode(*self.args, self.stream))
+
+    def partitions(self) -> None:
+        check(lib.paged_attention_decode_partitions(*self.args, self.stream))
+
+    def reduce(self) -> None:
+        check(lib.paged_attention_decode_reduce(*self.reduce_args, self.stream))
+
+
+class PreparedAppend:
+    """paged_cache_append with its arguments marshalled once."""
+
+    def __init__(self, k_cache, v_cache, key, value, slot_mapping, stream=None):
+        _dev(k_cache, v_cache, key, value, slot_mapping)
+        self._keep = (k_cache, v_cache, key, value, slot_mapping)
+        N, H, bs, D = k_cache.shape
+        T = slot_mapping.numel()
+        if key.shape != (T, H, D) or value.shape != (T, H, D) or slot_mapping.dtype != torch.int32:
+            raise ValueError("key/value must be [T][Hkv][D], slot_mapping int32 [T]")
+        self.args = (k_cache.data_ptr(), v_cache.data_ptr(), key.data_ptr(), value.data_ptr(), 0, 0,
+                     slot_mapping.data_ptr(), T, H, D, bs, N, dtype_code(k_cache.dtype))
+        self.stream = _stream(stream)
+
+    def __call__(self) -> None:
+        check(lib.paged_cache_append(*self.args, self.stream))

@@ -1,0 +1,120 @@
+"""Helpers for the GPU parity tests: run every pool/cache operation on the library (C ABI via
+the binding) and on the oracle side by side, and compare what must be bit-exact as it goes."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import workloads as wl
+from oracle import CacheModel, PoolModel
+from paged_kv_cache_404_amd import BlockPool, ops
+
+TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
+INT_VIEW = {"bf16": (np.int16, torch.int16), "f16": (np.int16, torch.int16), "f32": (np.int32, torch.int32)}
+
+ATOL = 2e-3  # max-abs tolerance for attention outputs compared in fp32
+
+
+def to_dev(bits: np.ndarray, dtype: str) -> torch.Tensor:
+    npi, _ = INT_VIEW[dtype]
+    return torch.from_numpy(np.ascontiguousarray(bits).view(npi)).cuda().view(TORCH_DT[dtype])
+
+
+def to_bits(t: torch.Tensor, dtype: str) -> np.ndarray:
+    _, ti = INT_VIEW[dtype]
+    return t.contiguous().view(ti).cpu().numpy().view(wl.storage_np_dtype(dtype))
+
+
+def i32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(np.asarray(a, dtype=np.int32))).cuda()
+
+
+class Mirror:
+    """One paged cache held twice: library pool + GPU caches, oracle pool + numpy cache."""
+
+    def __init__(self, N: int, Hkv: int, D: int, dtype: str, free_order, Hq: int | None = None):
+        self.N, self.Hkv, self.D, self.dtype = N, Hkv, D, dtype
+        self.pool = BlockPool(N, 16, free_order)
+        self.opool = PoolModel(N, 16, free_order)
+        _, ti = INT_VIEW[dtype]
+        sentinel = int(np.array(wl.NAN_BITS[dtype], dtype=wl.storage_np_dtype(dtype)).view(INT_VIEW[dtype][0]))
+        self.k = torch.full((N, Hkv, 16, D), sentinel, dtype=ti, device="cuda").view(TORCH_DT[dtype])
+        self.v = torch.full((N, Hkv, D, 16), sentinel, dtype=ti, device="cuda").view(TORCH_DT[dtype])
+        self.cache = CacheModel(N, Hkv, D, dtype)
+
+    def new_seq(self) -> int:
+        a, b = self.pool.new_seq(), self.opool.new_seq()
+        assert a == b
+        return a
+
+    def fork(self, parent: int) -> int:
+        a, b = self.pool.fork(parent), self.opool.fork(parent)
+        assert a == b
+        return a
+
+    def free(self, seq: int) -> None:
+        self.pool.free(seq)
+        self.opool.free_seq(seq)
+
+    def append(self, seqs, counts, key_bits: np.ndarray, value_bits: np.ndarray, check_pool: bool = True):
+        """Reserve slots on both pools (must agree), copy-on-write copies, then scatter K/V."""
+        st, done, slots, cow = self.pool.append_many(seqs, counts)
+        assert st == 0, (st, done)
+        oslots, ocow = [], []
+        for s, c in zip(seqs, counts):
+            sl, cw = self.opool.append(s, c)
+            oslots += sl
+            ocow += cw
+        if check_pool:
+            assert slots.tolist() == oslots
+            assert [tuple(x) for x in cow.tolist()] == ocow
+        if len(cow):
+            ops.paged_cache_copy_blocks(self.k, self.v, i32(cow))
+            self.cache.copy_blocks(ocow)
+        if len(slots):
+            ops.paged_cache_append(self.k, self.v, to_dev(key_bits, self.dtype), to_dev(value_bits, self.dtype),
+                                   i32(slots))
+            self.cache.append(key_bits, value_bits, oslots)
+        return slots, cow
+
+    def tables(self, seqs, max_blocks: int | None = None):
+        if max_blocks is None:
+            max_blocks = max(1, max(len(self.opool.tables[s]) for s in seqs))
+        t, lens = self.pool.block_tables(seqs, max_blocks)
+        ot, olens = self.opool.block_tables(seqs, max_blocks)
+        assert t.tolist() == ot and lens.tolist() == olens
+        return t, lens
+
+    def assert_cache_bit_exact(self) -> None:
+        torch.cuda.synchronize()
+        step = max(1, (1 << 26) // (self.Hkv * 16 * self.D))  # compare ~64M elements at a time
+        for b0 in range(0, self.N, step):
+            b1 = min(self.N, b0 + step)
+            assert np.array_equal(to_bits(self.k[b0:b1], self.dtype), self.cache.k[b0:b1]), f"K blocks {b0}:{b1}"
+            assert np.array_equal(to_bits(self.v[b0:b1], self.dtype), self.cache.v[b0:b1]), f"V blocks {b0}:{b1}"
+
+
+def build_decode(w: wl.DecodeWorkload, t: wl.DecodeTensors):
+    """Cache the prefix of every sequence, then run the step's append.  Returns (mirror, seqs)."""
+    m = Mirror(w.num_blocks, w.Hkv, w.D, w.dtype, w.free_order)
+    seqs = [m.new_seq() for _ in range(w.B)]
+    counts = [int(L) - 1 for L in w.lens]
+    pk = np.concatenate([x.reshape(-1, w.Hkv, w.D) for x in t.prefix_k]) if sum(counts) else \
+        np.zeros((0, w.Hkv, w.D), dtype=wl.storage_np_dtype(w.dtype))
+    pv = np.concatenate([x.reshape(-1, w.Hkv, w.D) for x in t.prefix_v]) if sum(counts) else pk
+    m.append(seqs, counts, pk, pv)
+    m.append(seqs, [1] * w.B, t.step_k, t.step_v)
+    return m, seqs
+
+
+def run_decode(m: Mirror, seqs, q_bits: np.ndarray, Hq: int, scale: float, partition_size: int,
+               out_dtype=torch.float32, max_blocks: int | None = None, max_context_len: int | None = None):
+    tables, lens = m.tables(seqs, max_blocks)
+    q = to_dev(q_bits, m.dtype)
+    B = len(seqs)
+    out = torch.full((B, Hq, m.D), float("nan"), dtype=out_dtype, device="cuda")
+    mcl = int(lens.max()) if max_context_len is None else max_context_len
+    ws = ops.decode_workspace(B, Hq, m.D, mcl, partition_size)
+    ops.paged_attention_decode(out, q, m.k, m.v, i32(tables), i32(lens), mcl, scale, partition_size, ws)
+    torch.cuda.synchronize()
+    return out, tables, lens
