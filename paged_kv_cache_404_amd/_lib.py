@@ -30,6 +30,11 @@ class OutOfBlocksError(PagedKVError):
     """The block pool cannot cover an allocation (PKV_ENOMEM)."""
 
 
+# torch bundles its own HIP runtime with the same SONAME as ROCm's.  Loading torch first makes the
+# library bind to that runtime instead of pulling a second copy into the process (two runtimes in
+# one process do not share devices, streams or memory).
+import torch  # noqa: E402,F401
+
 if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is not built; run `python -m paged_kv_cache_404_amd.build` (hipcc, gfx950). "
