@@ -37,7 +37,7 @@ import torch  # noqa: E402,F401
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m paged_kv_cache_404_amd.build` (hipcc, gfx950). "
+        f"{LIB_PATH} is not built; run `python paged_kv_cache_404_amd/build.py` (hipcc, gfx950). "
         "This package has no non-HIP fallback.")
 
 lib = C.CDLL(LIB_PATH)

@@ -1,6 +1,6 @@
 """Builds libpagedkv.so in-tree: HIP kernels for gfx950 with hipcc, host pool with g++.
 
-Usage: python -m paged_kv_cache_404_amd.build [--verbose]
+Usage: python paged_kv_cache_404_amd/build.py [--verbose]   (or __graft_entry__.build())
 """
 from __future__ import annotations
 
