@@ -97,7 +97,7 @@ def cpu_baseline(w, seconds: float):
         oatt.paged_decode(q, cache, tables, tl, w.scale)
         reps += 1
         el = time.perf_counter() - t0
-        if el >= seconds or reps >= 50:
+        if el >= seconds and reps >= 3:
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     per_call = el / reps

@@ -27,13 +27,21 @@
  *   - Element types: PKV_F32, PKV_F16, PKV_BF16.  Queries, keys, values and caches of one call
  *     share one element type (`dtype`).
  *   - Cache layout (one layer; K and V are separate tensors, both indexed by physical block id):
- *         k_cache [num_blocks][num_kv_heads][block_size][head_dim]   token rows
+ *         k_cache [num_blocks][num_kv_heads][K tile]                 see below
  *         v_cache [num_blocks][num_kv_heads][head_dim][block_size]   head-dim rows
  *     Slot s means block s / block_size, offset s % block_size.  One (block, head) tile of either
  *     tensor is contiguous (4 KiB at 16 x 128 bf16), and a whole block is one contiguous span.
+ *     K tile: the 16 x head_dim elements of one (block, head) are stored as 16-byte chunks
+ *     (E = 16 / element size elements each, so head_dim * element size must be a multiple of 64
+ *     bytes).  With token t = 8*hi + 4*set + low and chunk c = 4*cq + cr of the token's head
+ *     vector, the chunks are stored in the nested order [cq][set][cr][hi][low], i.e. element d of
+ *     token t is at tile offset (((cq*2 + set)*4 + cr)*8 + hi*4 + low)*E + d % E with c = d / E.
+ *     This is the matrix-core operand order of the decode and prefill kernels: one 32-dimension
+ *     k-step of eight tokens of a block is one contiguous 512-byte run.
  *   - Grouped-query attention: query head h reads KV head h / (num_q_heads / num_kv_heads).
  *   - Supported kernel shapes: block_size 16, head_dim 64 or 128, num_q_heads / num_kv_heads in
- *     {1, 2, 4, 8}.  Other values return PKV_EUNSUPPORTED.
+ *     {1, 2, 4, 8}.  Other values return PKV_EUNSUPPORTED (paged_cache_append and
+ *     paged_cache_copy_blocks accept any head_dim whose row is a multiple of 64 bytes).
  */
 #ifndef PAGEDKV_H
 #define PAGEDKV_H
@@ -123,7 +131,9 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_he
  *   partition_size 0: one pass per (sequence, KV head).  Otherwise a multiple of block_size:
  *                  the context is cut into fixed partitions of that many tokens, each processed
  *                  independently, and the partial softmaxes are merged exactly (log-sum-exp).
- *                  Partition boundaries depend only on the token position, never on the batch.
+ *                  Partition boundaries depend only on the token position, never on the batch,
+ *                  so a sequence's output bits do not depend on the rest of the batch.  At most
+ *                  65535 partitions per sequence (PKV_EUNSUPPORTED beyond).
  *   workspace      device scratch of at least paged_attention_decode_workspace_bytes(...) bytes
  *                  (may be NULL when that is 0); contents on entry do not matter.
  * Accumulation is fp32 whatever the input type.

@@ -27,7 +27,7 @@ Modules:
   brute      pure-Python per-page / per-token loops for tiny inputs (pins the numpy path)
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against values the pages
-fix, closed forms, invariants and brute force (see the design doc for the list).  Parity unpinned:
+fix, closed forms, invariants and brute force.  Parity unpinned:
 none of the pages prints an attention value or a worked attention example, so no attention
 output is pinned to a printed number; attention is pinned to closed forms, invariants,
 brute force and an independent library routine instead.

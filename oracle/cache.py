@@ -5,8 +5,16 @@ id and writes token ``pos`` of a sequence at (page, pos % block_size).  This lib
 stores one layer's K and V as two such tensors.  Layout (a fixed part of the library's
 interface, restated here independently):
 
-    K: [num_blocks][num_kv_heads][block_size][head_dim]   (token rows, dims contiguous)
     V: [num_blocks][num_kv_heads][head_dim][block_size]   (dim rows, tokens contiguous)
+    K: [num_blocks][num_kv_heads][tile], one tile of block_size (16) tokens x head_dim
+       elements per (block, head), in 16-byte chunks (E = 16 / element size elements each).
+       Number the tokens t = 8*hi + 4*set + low and the chunks of a token's head vector
+       c = 4*cq + cr; the tile stores the chunks in the nested order
+       [cq][set][cr][hi][low], each chunk's E elements in order.
+
+``self.k`` holds K in the logical order [num_blocks][num_kv_heads][block_size][head_dim]
+(what attention reads); ``k_physical()`` rearranges it into the stored byte order above,
+which is what the library's device tensor must hold byte for byte.
 
 Slot ``s`` means block ``s // block_size``, offset ``s % block_size``; slot -1 is skipped.
 Values are held as raw storage bits (uint16 for bf16/fp16, uint32 for fp32), so append and
@@ -46,6 +54,18 @@ class CacheModel:
         for src, dst in pairs:
             self.k[dst] = self.k[src]
             self.v[dst] = self.v[src]
+
+    def k_physical(self, blocks=slice(None)) -> np.ndarray:
+        """K of the given blocks in stored byte order: [n][num_kv_heads][block_size * head_dim]."""
+        k = self.k[blocks]
+        n, H, bs, D = k.shape
+        E = 16 // k.dtype.itemsize
+        if bs != 16 or D % (4 * E):
+            raise ValueError("the K tile order needs 16-token blocks and head_dim * elem_size % 64 == 0")
+        # token axis -> (hi, set, low); dim axis -> (cq, cr, e)
+        t = k.reshape(n, H, 2, 2, 4, D // (4 * E), 4, E)
+        # stored order [cq][set][cr][hi][low][e]
+        return np.ascontiguousarray(t.transpose(0, 1, 5, 3, 6, 2, 4, 7)).reshape(n, H, bs * D)
 
     def token_k(self, slot: int) -> np.ndarray:
         blk, off = divmod(int(slot), self.bs)

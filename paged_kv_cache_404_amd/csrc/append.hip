@@ -3,10 +3,11 @@
 // [Serving] "Production Serving: Continuous Batching and PagedAttention", The Build, Step 4:
 // token pos of a sequence is stored at (page, pos % block_size) of one big tensor indexed by
 // physical page id.  Here the slot of every token is computed on the host by the block pool, so
-// the kernels only move bytes.  Layout: K [N][Hkv][bs][D] (a token is one 16-byte-aligned row per
-// head, written with 16-byte stores), V [N][Hkv][D][bs] (a token is one column per head, written
-// element by element).  Copy-on-write ([Chapter] "PagedAttention: KV cache memory"): a shared
-// block that a sequence is about to write is first copied whole.
+// the kernels only move bytes.  Layout: K [N][Hkv][tile] with each token's head vector cut into
+// 16-byte chunks placed in the matrix-core tile order of k_chunk_pos (16-byte stores), V
+// [N][Hkv][D][bs] (a token is one column per head, written element by element).
+// Copy-on-write ([Chapter] "PagedAttention: KV cache memory"): a shared block that a sequence is
+// about to write is first copied whole.
 #include "device.h"
 
 namespace pkv {
@@ -36,7 +37,7 @@ __global__ void __launch_bounds__(256) append_kernel(uint8_t* __restrict__ k_cac
   const u32x4 kv = *reinterpret_cast<const u32x4*>(key + t * key_stride_b + src_off);
   const u32x4 vv = *reinterpret_cast<const u32x4*>(value + t * value_stride_b + src_off);
   const int64_t head = blk * H + h;
-  *reinterpret_cast<u32x4*>(k_cache + ((head * bs + off) * D + static_cast<int64_t>(c) * EPC) * ESIZE) = kv;
+  *reinterpret_cast<u32x4*>(k_cache + (head * bs * D) * ESIZE + static_cast<int64_t>(k_chunk_pos(off, c)) * 16) = kv;
   uint8_t* vcol = v_cache + ((head * D + static_cast<int64_t>(c) * EPC) * bs + off) * ESIZE;
   if constexpr (ESIZE == 2) {
     const uint16_t* e = reinterpret_cast<const uint16_t*>(&vv);
@@ -77,8 +78,9 @@ extern "C" int paged_cache_append(void* k_cache, void* v_cache, const void* key,
     return fail(PKV_EINVAL, "paged_cache_append: bad sizes T=%d Hkv=%d D=%d bs=%d N=%d", T, num_kv_heads, head_dim,
                 block_size, num_blocks);
   const int es = elem_size(dtype);
-  if ((static_cast<int64_t>(head_dim) * es) % 16 != 0)
-    return fail(PKV_EUNSUPPORTED, "paged_cache_append: head_dim*elem_size must be a multiple of 16 bytes");
+  if (block_size != kBlock) return fail(PKV_EUNSUPPORTED, "paged_cache_append: block_size %d (16 only)", block_size);
+  if ((static_cast<int64_t>(head_dim) * es) % 64 != 0)
+    return fail(PKV_EUNSUPPORTED, "paged_cache_append: head_dim*elem_size must be a multiple of 64 bytes");
   if (T == 0) return PKV_OK;
   if (!k_cache || !v_cache || !key || !value || !slot_mapping)
     return fail(PKV_EINVAL, "paged_cache_append: NULL pointer");

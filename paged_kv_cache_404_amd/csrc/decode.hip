@@ -128,33 +128,45 @@ __device__ __forceinline__ void emit(const DecodeArgs& a, int b, int hq, int p, 
 }
 
 // ------------------------------------------------------------------------------------------
-// Matrix-core kernel (bf16 / fp16).  grid = (max_parts, Hkv, B); NW waves share one partition.
+// Matrix-core kernel (bf16 / fp16).  grid = (Hkv, B, max_parts): the partition index varies
+// slowest, so every sequence's full leading partitions are dispatched before the ragged last
+// ones (longest work first, short work in the tail).  NW waves share one partition; wave w takes
+// the 32-token steps w, w + NW, ...
+//
+// Memory pipeline: each wave keeps exactly one step of K/V in flight while it computes the
+// previous one.  The next step's K fragments are loaded into the K registers as soon as the
+// current Q.K products have consumed them, and the next V fragments right after P.V; only the
+// last step of a wave is issued without a successor, so every wait inside the loop leaves the
+// successor's loads outstanding.  The partition's block ids are loaded one per lane together with
+// the context length (64 blocks per load), so a step's tile addresses come from a lane read.
 // ------------------------------------------------------------------------------------------
 template <int DT, int DT_OUT, int D, int G, int NW>
 __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
-  constexpr int KS = D / 32;  // k-steps of Q.K
-  constexpr int NB = D / 16;  // 16-column blocks of P.V
+  constexpr int KS = D / 32;        // k-steps of Q.K
+  constexpr int NB = D / 16;        // 16-column blocks of P.V
   constexpr int TILE = kBlock * D;  // elements of one (block, head) tile
+  constexpr int kTableSteps = 32;   // steps covered by one block-id load (64 blocks, one per lane)
 
-  const int p = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const int L = clamp_len(a, b);
+  const int g = blockIdx.x;
+  const int b = blockIdx.y;
+  const int p = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pstart = p * a.part_size;
+  const int32_t* __restrict__ table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
+  // Issued before the length is known: its index is bounded by the table row, not by L.
+  const int tab_first = table[min((pstart >> 4) + lane, a.max_blocks - 1)];
+  const int L = clamp_len(a, b);
   if (pstart >= L) return;
   const int pend = min(pstart + a.part_size, L);
   const int nparts = (L + a.part_size - 1) / a.part_size;
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
   const int n16 = lane & 15;
   const int q4 = lane >> 4;
-
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v);
-  const int32_t* __restrict__ table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
 
   // Q^T fragments: lane (head n16, group q4) holds Q[head][ks*32 + 8*q4 .. +8]; padded heads are 0.
   u32x4 qf[KS];
@@ -167,14 +179,15 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
     }
   }
 
-  // Token order inside a 32-token step: Q.K product #1 row m holds step token 8*(m/4) + m%4,
-  // product #2 row m holds that token + 4.  Then lane (head, q4) ends up with the scores of step
-  // tokens 8*q4 .. 8*q4+7, exactly the k-range its P row covers in P.V.
-  const int tok1 = 8 * (n16 >> 2) + (n16 & 3);
-  const int khalf = tok1 >> 4;  // which of the step's two blocks this lane's K rows live in
-  const int krow = tok1 & 15;
-  const int vhalf = q4 >> 1;  // which block this lane's V tokens live in
-  const int vcol = (q4 & 1) * 8;
+  // Token order inside a 32-token step (blocks A = tokens 0..15, B = 16..31): Q.K product #s
+  // (s = 0, 1) row m holds token 8*(m/4) + m%4 + 4s of block m/8 (the K tile order puts exactly
+  // these rows of one k-step in one 512-byte run per block).  Lane (head, q4) then holds the
+  // scores of step tokens 8*q4 .. 8*q4+7, the k-range its P row covers in P.V, whose V operand
+  // (8 consecutive tokens of one dimension) is one 16-byte load from the dim-major V tile.
+  const int k_in_tile = (q4 * 8 + (n16 & 7)) * 8;  // chunk (k-step 0, set 0) of this lane, in elements
+  const bool k_from_b = n16 >= 8;
+  const bool v_from_b = q4 >= 2;
+  const int v_in_tile = n16 * kBlock + (q4 & 1) * 8;
 
   f32x4 o[NB];
 #pragma unroll
@@ -183,104 +196,150 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
   float l_run = 0.f;        // this lane's share of sum p
 
   const int nsteps = (pend - pstart + 31) >> 5;
-  for (int st = w; st < nsteps; st += NW) {
-    const int t0 = pstart + st * 32;
-    const int nvalid = min(32, pend - t0);
-    const int lb = t0 >> 4;
-    const int blkA = clamp_blk(a, table[lb]);
-    const int blkB = nvalid > 16 ? clamp_blk(a, table[lb + 1]) : blkA;
-    const int64_t tileA = (static_cast<int64_t>(blkA) * a.Hkv + g) * TILE;
-    const int64_t tileB = (static_cast<int64_t>(blkB) * a.Hkv + g) * TILE;
+  for (int c0 = 0; c0 < nsteps; c0 += kTableSteps) {
+    const int cend = min(nsteps, c0 + kTableSteps);
+    int st = c0 + w;
+    if (st >= cend) continue;
+    const int cb0 = (pstart >> 4) + 2 * c0;                   // first block of this table chunk
+    const int cnb = min(2 * kTableSteps, ((pend + 15) >> 4) - cb0);  // blocks of the chunk
+    const int tab = clamp_blk(a, c0 == 0 ? tab_first : table[min(cb0 + lane, a.max_blocks - 1)]);
 
-    const uint16_t* krow1 = kc + (khalf ? tileB : tileA) + krow * D + q4 * 8;
-    const uint16_t* krow2 = krow1 + 4 * D;
-    u32x4 k1[KS], k2[KS];
+    u32x4 kf[2 * KS], vf[NB];
+    auto tiles = [&](int s, int64_t& tA, int64_t& tB) {
+      const int j = 2 * (s - c0);
+      const int bA = __builtin_amdgcn_readlane(tab, j);
+      const int bB = __builtin_amdgcn_readlane(tab, min(j + 1, cnb - 1));  // a lone last block pairs with itself
+      tA = (static_cast<int64_t>(bA) * a.Hkv + g) * TILE;
+      tB = (static_cast<int64_t>(bB) * a.Hkv + g) * TILE;
+    };
+    auto load_k = [&](int s) {
+      int64_t tA, tB;
+      tiles(s, tA, tB);
+      const uint16_t* kp = kc + (k_from_b ? tB : tA) + k_in_tile;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      k1[ks] = *reinterpret_cast<const u32x4*>(krow1 + ks * 32);
-      k2[ks] = *reinterpret_cast<const u32x4*>(krow2 + ks * 32);
-    }
-    const uint16_t* vbase = vc + (vhalf ? tileB : tileA) + n16 * kBlock + vcol;
-    u32x4 vf[NB];
+      for (int ks = 0; ks < KS; ++ks) {
+        kf[ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (2 * ks) * 256));
+        kf[KS + ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (2 * ks + 1) * 256));
+      }
+    };
+    auto load_v = [&](int s) {
+      int64_t tA, tB;
+      tiles(s, tA, tB);
+      const uint16_t* vp = vc + (v_from_b ? tB : tA) + v_in_tile;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) vf[nb] = *reinterpret_cast<const u32x4*>(vbase + nb * 16 * kBlock);
+      for (int nb = 0; nb < NB; ++nb)
+        vf[nb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + nb * 16 * kBlock));
+    };
 
-    f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+    // One 32-token step; with `prefetch` the successor's loads are issued as registers free up.
+    // The empty asm statements keep those loads where they are written.
+    auto step = [&](int s, const bool prefetch) {
+      const int nvalid = min(32, pend - (pstart + s * 32));
+      f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s1 = mfma16x16x32<DT>(k1[ks], qf[ks], s1);
-      s2 = mfma16x16x32<DT>(k2[ks], qf[ks], s2);
-    }
+      for (int ks = 0; ks < KS; ++ks) {
+        s1 = mfma16x16x32<DT>(kf[ks], qf[ks], s1);
+        s2 = mfma16x16x32<DT>(kf[KS + ks], qf[ks], s2);
+      }
+      if (prefetch) {
+        asm volatile("" ::: "memory");
+        load_k(s + NW);
+        asm volatile("" ::: "memory");
+      }
 
-    // Lane (head n16, q4) now holds scores of step tokens 8*q4 + i, i = 0..7.
-    const int tb = 8 * q4;
-    float sc[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sc[j] = (n16 < G && tb + j < nvalid) ? s1[j] * a.scale_log2 : -INFINITY;
-      sc[4 + j] = (n16 < G && tb + 4 + j < nvalid) ? s2[j] * a.scale_log2 : -INFINITY;
-    }
-    float bmax = sc[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sc[i]);
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-
-    const bool need = (n16 < G) && (bmax > m_run + kLazyRescaleLog2);
-    if (__any(need)) {
-      const float m_new = need ? bmax : m_run;
-      const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;
-      l_run *= alpha;
-      m_run = m_new;
-      // O row r = 4*q4 + j belongs to head r % G (hi rows r < G, lo rows G <= r < 2G).
+      // Lane (head n16, q4) now holds scores of step tokens 8*q4 + i, i = 0..7.
+      const int tb = 8 * q4;
+      float sc[8];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float f = __shfl(alpha, (4 * q4 + j) % G);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[nb][j] *= f;
+        sc[j] = (n16 < G && tb + j < nvalid) ? s1[j] * a.scale_log2 : -INFINITY;
+        sc[4 + j] = (n16 < G && tb + 4 + j < nvalid) ? s2[j] * a.scale_log2 : -INFINITY;
       }
-    }
+      float bmax = sc[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sc[i]);
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
 
-    float pv[8];
-    float psum = 0.f;
+      const bool need = (n16 < G) && (bmax > m_run + kLazyRescaleLog2);
+      if (__any(need)) {
+        const float m_new = need ? bmax : m_run;
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;
+        l_run *= alpha;
+        m_run = m_new;
+        // O row r = 4*q4 + j belongs to head r % G (hi rows r < G, lo rows G <= r < 2G).
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pv[i] = (n16 < G) ? fast_exp2(sc[i] - m_run) : 0.f;
-      psum += pv[i];
-    }
-    l_run += psum;
+        for (int j = 0; j < 4; ++j) {
+          const float f = __shfl(alpha, (4 * q4 + j) % G);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) o[nb][j] *= f;
+        }
+      }
 
-    u32x4 hi, lo;
+      float pv[8];
+      float psum = 0.f;
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      const uint32_t h0 = to16<DT>(pv[2 * wd]);
-      const uint32_t h1 = to16<DT>(pv[2 * wd + 1]);
-      const uint32_t l0 = to16<DT>(pv[2 * wd] - from16<DT>(h0));
-      const uint32_t l1 = to16<DT>(pv[2 * wd + 1] - from16<DT>(h1));
-      hi[wd] = h0 | (h1 << 16);
-      lo[wd] = l0 | (l1 << 16);
-    }
-    u32x4 pa;
-#pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      const uint32_t lo_src = static_cast<uint32_t>(__shfl(static_cast<int>(lo[wd]), lane - G));
-      pa[wd] = (n16 < G) ? hi[wd] : ((n16 < 2 * G) ? lo_src : 0u);
-    }
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = (n16 < G) ? fast_exp2(sc[i] - m_run) : 0.f;
+        psum += pv[i];
+      }
+      l_run += psum;
 
-    if (nvalid < 32) {
-      const int keep = min(8, max(0, nvalid - tb));
+      u32x4 hi, lo;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vf[nb] = keep_first(vf[nb], keep);
-    }
+      for (int wd = 0; wd < 4; ++wd) {
+        const uint32_t h0 = to16<DT>(pv[2 * wd]);
+        const uint32_t h1 = to16<DT>(pv[2 * wd + 1]);
+        const uint32_t l0 = to16<DT>(pv[2 * wd] - from16<DT>(h0));
+        const uint32_t l1 = to16<DT>(pv[2 * wd + 1] - from16<DT>(h1));
+        hi[wd] = h0 | (h1 << 16);
+        lo[wd] = l0 | (l1 << 16);
+      }
+      u32x4 pa;
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) o[nb] = mfma16x16x32<DT>(pa, vf[nb], o[nb]);
+      for (int wd = 0; wd < 4; ++wd) {
+        const uint32_t lo_src = static_cast<uint32_t>(__shfl(static_cast<int>(lo[wd]), lane - G));
+        pa[wd] = (n16 < G) ? hi[wd] : ((n16 < 2 * G) ? lo_src : 0u);
+      }
+
+      if (nvalid < 32) {
+        // Tokens past the context are stale (possibly NaN): zero them in V, never multiply them.
+        const int keep = min(8, max(0, nvalid - tb));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) vf[nb] = keep_first(vf[nb], keep);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) o[nb] = mfma16x16x32<DT>(pa, vf[nb], o[nb]);
+      if (prefetch) {
+        asm volatile("" ::: "memory");
+        load_v(s + NW);
+        asm volatile("" ::: "memory");
+      }
+    };
+
+    load_k(st);
+    load_v(st);
+    for (; st + NW < cend; st += NW) step(st, true);
+    step(st, false);
   }
 
   // Per-head sums over the four lane groups.
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
+  // Fold each head's lo row (G + h) into its hi row (h): afterwards O row h = 4*q4 + j, h < G.
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (G >= 4) {
+        o[nb][j] += __shfl_down(o[nb][j], 16 * (G / 4));
+      } else if (j + G < 4) {
+        o[nb][j] += o[nb][j + G];
+      }
+    }
+  }
 
-  __shared__ float sO[NW][2 * G][D];
+  __shared__ float sO[NW][G][D];
   __shared__ float sM[NW][G];
   __shared__ float sL[NW][G];
 #pragma unroll
@@ -288,7 +347,7 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 4 * q4 + j;
-      if (r < 2 * G) sO[w][r][nb * 16 + n16] = o[nb][j];
+      if (r < G) sO[w][r][nb * 16 + n16] = o[nb][j];
     }
   }
   if (q4 == 0 && n16 < G) {
@@ -307,7 +366,7 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
 #pragma unroll
     for (int ww = 0; ww < NW; ++ww) {
       const float f = fast_exp2(sM[ww][h] - M);  // waves without a step hold m = -inf -> 0
-      acc += f * (sO[ww][h][d] + sO[ww][G + h][d]);
+      acc += f * sO[ww][h][d];
       lsum += f * sL[ww][h];
     }
     emit<DT_OUT>(a, b, g * G + h, p, nparts, d, D, M, lsum, acc);
@@ -315,14 +374,15 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Vector-ALU kernel (any element type; used for fp32).  grid = (max_parts, Hq, B), one wave.
+// Vector-ALU kernel (any element type; used for fp32).  grid = (Hq, B, max_parts), one wave.
 // Lane i scores token c0 + i of each 64-token chunk; each lane owns dims lane and lane + 64.
 // ------------------------------------------------------------------------------------------
 template <int DT, int DT_OUT, int D>
 __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
-  const int p = blockIdx.x;
-  const int hq = blockIdx.y;
-  const int b = blockIdx.z;
+  constexpr int E = DT == PKV_F32 ? 4 : 8;  // elements per 16-byte chunk of the K tile
+  const int hq = blockIdx.x;
+  const int b = blockIdx.y;
+  const int p = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int g = hq / G;
   const int L = clamp_len(a, b);
@@ -354,7 +414,8 @@ __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
       tile = (static_cast<int64_t>(clamp_blk(a, table[t / kBlock])) * a.Hkv + g) * kBlock * D;
       off = t % kBlock;
       float acc = 0.f;
-      for (int d = 0; d < D; ++d) acc += qs[d] * elem_to_float<DT>(a.k, tile + static_cast<int64_t>(off) * D + d);
+      for (int d = 0; d < D; ++d)
+        acc += qs[d] * elem_to_float<DT>(a.k, tile + static_cast<int64_t>(k_chunk_pos(off, d / E)) * E + d % E);
       s = acc;
     }
     const float m_new = fmaxf(m_run, wave_max(s));
@@ -456,6 +517,8 @@ int validate(const char* fn, void* out, int32_t out_dtype, const void* query, co
   if (B > 65535 || Hq > 65535) return fail(PKV_EUNSUPPORTED, "%s: batch or head count above 65535", fn);
   if (partition_size < 0 || partition_size % bs != 0)
     return fail(PKV_EINVAL, "%s: partition_size %d must be 0 or a multiple of block_size", fn, partition_size);
+  if (partition_size > 0 && (max_ctx + static_cast<int64_t>(partition_size) - 1) / partition_size > 65535)
+    return fail(PKV_EUNSUPPORTED, "%s: more than 65535 partitions per sequence", fn);
   if (static_cast<int64_t>(max_ctx) > static_cast<int64_t>(max_blocks) * bs)
     return fail(PKV_EINVAL, "%s: max_context_len %d exceeds max_blocks_per_seq * block_size", fn, max_ctx);
   if (B == 0) return PKV_OK;
@@ -472,16 +535,18 @@ int validate(const char* fn, void* out, int32_t out_dtype, const void* query, co
 
 template <int DT, int DT_OUT, int D>
 int launch_valu(const DecodeArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL((decode_valu_kernel<DT, DT_OUT, D>), dim3(a.max_parts, a.Hq, B), dim3(64), 0, s, a);
+  hipLaunchKernelGGL((decode_valu_kernel<DT, DT_OUT, D>), dim3(a.Hq, B, a.max_parts), dim3(64), 0, s, a);
   return PKV_OK;
 }
 
-constexpr int kWavesPerWG = 4;
-
+// Waves per workgroup: 4 for partitions up to 512 tokens (<= 4 steps per wave), 8 above.
 template <int DT, int DT_OUT, int D, int G>
 int launch_mfma(const DecodeArgs& a, int B, hipStream_t s) {
-  hipLaunchKernelGGL((decode_mfma_kernel<DT, DT_OUT, D, G, kWavesPerWG>), dim3(a.max_parts, a.Hkv, B),
-                     dim3(kWavesPerWG * 64), 0, s, a);
+  const dim3 grid(a.Hkv, B, a.max_parts);
+  if (a.part_size <= 512)
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, DT_OUT, D, G, 4>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_mfma_kernel<DT, DT_OUT, D, G, 8>), grid, dim3(512), 0, s, a);
   return PKV_OK;
 }
 

@@ -63,4 +63,15 @@ __device__ __forceinline__ void store_from_float(void* base, int64_t i, float x)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// K tile order.  A (block, head) K tile holds 16 tokens x head_dim elements as 16-byte chunks;
+// chunk c of token t (elements [c*E, c*E + E) of that token's head vector, E = 16 / elem_size)
+// sits at chunk index
+//     ((c / 4) * 2 + (t / 4) % 2) * 32 + (c % 4) * 8 + (t / 8) * 4 + t % 4
+// i.e. the tile is [c / 4][token set (t / 4) % 2][c % 4][8 tokens of the set].  One matrix-core
+// k-step of a 32-token step (two blocks) then reads one 512-byte run from each block: every
+// cache line is fully used by a single load instruction.
+__host__ __device__ __forceinline__ int k_chunk_pos(int t, int c) {
+  return ((c >> 2) * 2 + ((t >> 2) & 1)) * 32 + (c & 3) * 8 + (t >> 3) * 4 + (t & 3);
+}
+
 }  // namespace pkv

@@ -111,9 +111,10 @@ __global__ void __launch_bounds__(G * 64) prefill_mfma_kernel(PrefillArgs a) {
       qf[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + ks * 32 + q4 * 8) : u32x4{0, 0, 0, 0};
   }
 
-  const int tok1 = 8 * (n16 >> 2) + (n16 & 3);
-  const int khalf = tok1 >> 4;
-  const int krow = tok1 & 15;
+  // Q.K product #s row m holds token 8*(m/4) + m%4 + 4s of the step's block m/8; in the K tile
+  // order those rows of one k-step are one 512-byte run per block (see k_chunk_pos).
+  const bool k_from_b = n16 >= 8;
+  const int k_in_tile = (q4 * 8 + (n16 & 7)) * 8;
   const int vhalf = q4 >> 1;
   const int vcol = (q4 & 1) * 8;
 
@@ -136,13 +137,12 @@ __global__ void __launch_bounds__(G * 64) prefill_mfma_kernel(PrefillArgs a) {
     const int64_t tileA = (static_cast<int64_t>(blkA) * a.Hkv + g) * TILE;
     const int64_t tileB = (static_cast<int64_t>(blkB) * a.Hkv + g) * TILE;
 
-    const uint16_t* krow1 = kc + (khalf ? tileB : tileA) + krow * D + q4 * 8;
-    const uint16_t* krow2 = krow1 + 4 * D;
+    const uint16_t* kp = kc + (k_from_b ? tileB : tileA) + k_in_tile;
     u32x4 k1[KS], k2[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      k1[ks] = *reinterpret_cast<const u32x4*>(krow1 + ks * 32);
-      k2[ks] = *reinterpret_cast<const u32x4*>(krow2 + ks * 32);
+      k1[ks] = *reinterpret_cast<const u32x4*>(kp + (2 * ks) * 256);
+      k2[ks] = *reinterpret_cast<const u32x4*>(kp + (2 * ks + 1) * 256);
     }
     const uint16_t* vbase = vc + (vhalf ? tileB : tileA) + n16 * kBlock + vcol;
     u32x4 vf[NB];

@@ -90,7 +90,8 @@ class Mirror:
         step = max(1, (1 << 26) // (self.Hkv * 16 * self.D))  # compare ~64M elements at a time
         for b0 in range(0, self.N, step):
             b1 = min(self.N, b0 + step)
-            assert np.array_equal(to_bits(self.k[b0:b1], self.dtype), self.cache.k[b0:b1]), f"K blocks {b0}:{b1}"
+            kb = to_bits(self.k[b0:b1], self.dtype).reshape(b1 - b0, self.Hkv, 16 * self.D)
+            assert np.array_equal(kb, self.cache.k_physical(slice(b0, b1))), f"K blocks {b0}:{b1}"
             assert np.array_equal(to_bits(self.v[b0:b1], self.dtype), self.cache.v[b0:b1]), f"V blocks {b0}:{b1}"
 
 

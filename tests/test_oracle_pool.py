@@ -271,3 +271,37 @@ def test_copy_blocks_whole_block():
     c.copy_blocks([(1, 3)])
     assert (c.k[3] == k1).all() and (c.v[3] == v1).all()
     assert (c.k[1] == k1).all() and (c.k[2] == k2).all()
+
+
+def test_k_tile_order_fixture():
+    """Single elements land where the hand-worked fixture puts them."""
+    for case in _golden("k_tile_order.json")["cases"]:
+        dt, D = case["dtype"], case["head_dim"]
+        c = CacheModel(2, 2, D, dt, fill_nan=False)
+        c.k[1, 1, case["token"], case["dim"]] = 7
+        phys = c.k_physical()
+        assert phys[1, 1, case["element_offset"]] == 7, case
+        assert np.count_nonzero(phys) == 1
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("bf16", 64), ("f16", 128), ("f32", 64), ("f32", 128)])
+def test_k_tile_order_is_a_permutation_with_contiguous_k_steps(dt, D):
+    """Every element appears once; and, the point of the order, the 8 tokens of one token set
+    times the 4 chunks of one 32-byte-per-chunk-group k-step occupy one contiguous run of 32
+    chunks (512 bytes for 16-bit types)."""
+    c = CacheModel(1, 1, D, dt, fill_nan=False)
+    E = 16 // c.k.dtype.itemsize
+    ids = np.arange(16 * D).reshape(16, D)  # logical id = t * D + d (fits the storage type)
+    c.k[0, 0] = ids
+    phys = c.k_physical()[0, 0].astype(np.int64)
+    assert sorted(phys.tolist()) == list(range(16 * D))
+    chunks = phys.reshape(-1, E)
+    assert (chunks == chunks[:, :1] + np.arange(E)).all()  # a chunk keeps its elements in order
+    tok = chunks[:, 0] // D
+    cidx = (chunks[:, 0] % D) // E
+    for run in range(len(chunks) // 32):
+        t, ch = tok[run * 32:(run + 1) * 32], cidx[run * 32:(run + 1) * 32]
+        assert len(set((t // 4) % 2)) == 1 and len(set(ch // 4)) == 1  # one token set, one chunk group
+        assert sorted(zip(t.tolist(), ch.tolist())) == sorted(
+            (tt, cq * 4 + cr) for tt in range(16) if (tt // 4) % 2 == (t[0] // 4) % 2
+            for cq in [ch[0] // 4] for cr in range(4))
