@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB of caches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic record from two rocprofv3 --pmc counter_collection.csv files "
+                         "(FETCH_SIZE run, WRITE_SIZE run) of this script, then exit")
     return ap.parse_args()
 
 
@@ -62,6 +65,48 @@ def measured_traffic(workload: str):
     if not entry or entry.get("decode_hip_sha256") != source_digest():
         return None
     return entry.get("hbm_bytes_per_launch")
+
+
+def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes per decode partition launch from two counter runs of this script.
+
+    FETCH_SIZE and WRITE_SIZE are KiB per dispatch.  Each is scaled by what the same counter
+    reads for the 1 GiB device-to-device copy this script runs (known bytes: 1 GiB read and
+    1 GiB written), so the figure is in true bytes whatever the counter's granularity."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
+        dec = [float(r["Counter_Value"]) for r in rows if "decode_mfma_kernel" in r["Kernel_Name"]]
+        if not dec:
+            raise SystemExit(f"no decode_mfma_kernel dispatch in {path}")
+        return copy, sum(dec) / len(dec), len(dec)
+
+    f_copy, f_dec, n_f = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_copy, w_dec, n_w = per_kernel(write_csv, "WRITE_SIZE")
+    known = float(1 << 30)
+    f_scale, w_scale = known / (f_copy * 1024), known / (w_copy * 1024)
+    hbm = f_dec * 1024 * f_scale + w_dec * 1024 * w_scale
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        rec = {}
+    rec[workload] = {
+        "decode_hip_sha256": source_digest(),
+        "hbm_bytes_per_launch": round(hbm),
+        "fetch_kib_per_dispatch": round(f_dec, 1),
+        "write_kib_per_dispatch": round(w_dec, 1),
+        "dispatches": [n_f, n_w],
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "calibration": "1 GiB device-to-device copy (__amd_rocclr_copyBuffer) in the same run: "
+                       f"FETCH_SIZE {f_copy:.1f} KiB, WRITE_SIZE {w_copy:.1f} KiB",
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    return rec[workload]
 
 
 def cpu_baseline(w, seconds: float):
@@ -115,6 +160,9 @@ def cpu_baseline(w, seconds: float):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        print(json.dumps(write_traffic(args.workload, *args.traffic_from)))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}); this library "
@@ -265,6 +313,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
+            "traffic_over_algorithmic": round(traffic / step_bytes, 4) if traffic else None,
         },
     }
     if not args.no_cpu_baseline:
