@@ -1,0 +1,210 @@
+"""Continuous-batching trace driver for the parity tests (test infrastructure).
+
+Replays a seeded request trace through the library's host block pool, mirrored operation by
+operation on the oracle's pool, and (with ``gpu=True``) through the library's device calls:
+each step appends one token per running sequence (``paged_cache_append``) and runs split-K
+decode attention over the live batch (``paged_attention_decode``).
+
+What each step compares:
+  * every step: slots, block tables and context lengths of the library pool against the
+    oracle pool, bit for bit, and the out-of-blocks decisions of both;
+  * every ``free_list_every`` steps: the two free lists, element by element;
+  * every ``check_every`` steps (GPU): the decode output against the oracle's fp64 attention
+    over the oracle's own byte-exact cache, max-abs.
+
+Scheduling policy (a harness around the method, as the pages describe serving, not the method):
+  * [Serving] The Build, Step 2 and [Chapter] "How the scheduler works": finished requests leave
+    first, then waiting requests are admitted first-come-first-served while fewer than
+    ``max_active`` run and the pool holds enough free blocks for the request's tokens plus one
+    ([Serving] The Concept: admit only what the memory can hold);
+  * [Chapter] "PagedAttention: KV cache memory": when the pool runs out mid-step, the most
+    recently admitted running request is preempted (its blocks freed) and later recomputed: on
+    re-admission its prompt and the tokens it had generated are appended again, with the same
+    bytes (prompt K/V come from a per-request stream; generated tokens' K/V are kept);
+  * a prompt's K/V are appended in one call at admission (no prefill attention in this trace).
+"""
+from __future__ import annotations
+
+import collections
+from dataclasses import dataclass, field
+
+import numpy as np
+
+import workloads as wl
+from oracle import OutOfBlocks, PoolModel
+from paged_kv_cache_404_amd import PKV_ENOMEM, BlockPool
+
+
+@dataclass
+class TraceStats:
+    steps: int = 0
+    seq_steps: int = 0
+    admissions: int = 0
+    preemptions: int = 0
+    finished: int = 0
+    max_active: int = 0
+    min_utilisation: float = 1.0
+    utilisation_sum: float = 0.0
+    attention_checks: int = 0
+    max_abs_err: float = 0.0
+    max_context: int = 0
+    kv_bytes: int = 0
+    errors: list = field(default_factory=list)
+
+    @property
+    def mean_utilisation(self) -> float:
+        return self.utilisation_sum / max(self.steps, 1)
+
+
+def run_trace(seed: int = 3, num_blocks: int = 12288, n_requests: int = 512, max_active: int = 128,
+              gpu: bool = False, check_every: int = 50, free_list_every: int = 25, partition_size: int = 512,
+              Hq: int = 32, Hkv: int = 8, D: int = 128, dtype: str = "bf16", max_steps: int | None = None,
+              atol: float = 2e-3) -> TraceStats:
+    reqs = wl.trace_requests(seed, n=n_requests)
+    fo = wl.shuffled_free_order(seed, num_blocks)
+    pool, opool = BlockPool(num_blocks, 16, fo), PoolModel(num_blocks, 16, fo)
+    st = TraceStats()
+    scale = 1.0 / np.sqrt(D)
+
+    if gpu:
+        import torch
+
+        from oracle import CacheModel
+        from oracle import attention as oatt
+        from paged_kv_cache_404_amd import ops
+
+        from .gpu_util import INT_VIEW, TORCH_DT, to_dev
+
+        _, ti = INT_VIEW[dtype]
+        sentinel = int(np.array(wl.NAN_BITS[dtype], dtype=wl.storage_np_dtype(dtype)).view(INT_VIEW[dtype][0]))
+        kc = torch.full((num_blocks, Hkv, 16, D), sentinel, dtype=ti, device="cuda").view(TORCH_DT[dtype])
+        vc = torch.full((num_blocks, Hkv, D, 16), sentinel, dtype=ti, device="cuda").view(TORCH_DT[dtype])
+        cache = CacheModel(num_blocks, Hkv, D, dtype)
+        max_ctx_cap = 16 * num_blocks
+        ws = ops.decode_workspace(max_active, Hq, D, max_ctx_cap, partition_size, device="cuda")
+        out = torch.empty((max_active, Hq, D), dtype=torch.float32, device="cuda")
+
+    def device_append(k_bits, v_bits, slots):
+        if not gpu or len(slots) == 0:
+            return
+        ops.paged_cache_append(kc, vc, to_dev(k_bits, dtype), to_dev(v_bits, dtype),
+                               torch.from_numpy(np.ascontiguousarray(slots, dtype=np.int32)).cuda())
+        cache.append(k_bits, v_bits, [int(x) for x in slots])
+
+    waiting = collections.deque(range(n_requests))  # arrival order
+    running: list[int] = []  # admission order
+    seq_of = {}
+    generated = [0] * n_requests
+    gen_k = [[] for _ in range(n_requests)]  # K/V bits of generated tokens, kept for recompute
+    gen_v = [[] for _ in range(n_requests)]
+
+    def free_both(seq):
+        pool.free(seq)
+        opool.free_seq(seq)
+
+    step = 0
+    while waiting or running:
+        if max_steps is not None and step >= max_steps:
+            break
+        # 1. retire finished requests
+        for r in [r for r in running if generated[r] >= reqs[r].output_len]:
+            free_both(seq_of.pop(r))
+            running.remove(r)
+            st.finished += 1
+        # 2. admit first-come-first-served
+        while waiting and len(running) < max_active and reqs[waiting[0]].arrival_step <= step:
+            r = waiting[0]
+            ntok = reqs[r].prompt_len + generated[r]
+            if pool.num_free() < wl.blocks_for(ntok + 1):
+                assert opool.num_free() < wl.blocks_for(ntok + 1)
+                break
+            waiting.popleft()
+            s = pool.new_seq()
+            assert opool.new_seq() == s
+            slots, cow = pool.append(s, ntok)
+            oslots, ocow = opool.append(s, ntok)
+            assert slots.tolist() == oslots and not cow and not ocow
+            if gpu:
+                pk, pv = wl.token_kv_bulk(seed, r, reqs[r].prompt_len, Hkv, D, dtype)
+                if generated[r]:
+                    pk = np.concatenate([pk] + gen_k[r])
+                    pv = np.concatenate([pv] + gen_v[r])
+                device_append(pk, pv, slots)
+            seq_of[r] = s
+            running.append(r)
+            st.admissions += 1
+        if not running:
+            step += 1
+            continue
+        # 3. one token per running request; preempt the newest on out-of-blocks
+        pending = list(running)
+        step_slots = {}
+        while pending:
+            seqs = [seq_of[r] for r in pending]
+            status, done, slots, cow = pool.append_many(seqs, [1] * len(seqs))
+            n_ok = len(seqs) if status == 0 else done
+            assert len(cow) == 0
+            for j in range(n_ok):
+                os_, ocow = opool.append(seqs[j], 1)
+                assert os_[0] == int(slots[j]) and not ocow
+                step_slots[pending[j]] = int(slots[j])
+            if status == 0:
+                break
+            assert status == PKV_ENOMEM
+            try:
+                opool.append(seqs[done], 1)
+                raise AssertionError("oracle pool admitted an append the library refused")
+            except OutOfBlocks:
+                pass
+            victim = running[-1]
+            assert victim in pending[done:]
+            free_both(seq_of.pop(victim))
+            running.pop()
+            waiting.appendleft(victim)
+            st.preemptions += 1
+            pending = [r for r in pending[done:] if r != victim]
+        B = len(running)
+        seqs = [seq_of[r] for r in running]
+        maxb = max(pool.seq_num_blocks(s) for s in seqs)
+        tables, lens = pool.block_tables(seqs, maxb)
+        otables, olens = opool.block_tables(seqs, maxb)
+        assert tables.tolist() == otables and lens.tolist() == olens, f"step {step}: tables differ"
+        if step % free_list_every == 0:
+            assert np.array_equal(pool.free_list(), np.asarray(opool.free, dtype=np.int32)), f"step {step}"
+        used = sum(int(x) for x in lens)
+        util = used / (16.0 * sum(pool.seq_num_blocks(s) for s in seqs))
+        st.min_utilisation = min(st.min_utilisation, util)
+        st.utilisation_sum += util
+        st.max_active = max(st.max_active, B)
+        st.max_context = max(st.max_context, int(lens.max()))
+        st.seq_steps += B
+        st.kv_bytes += used * Hkv * D * 2 * wl.elem_bytes(dtype)
+        # 4. device: append the step's tokens, decode over the live batch
+        if gpu:
+            sk, sv = wl.step_kv(seed, step, B, Hkv, D, dtype)
+            for i, r in enumerate(running):
+                gen_k[r].append(sk[i:i + 1])
+                gen_v[r].append(sv[i:i + 1])
+            device_append(sk, sv, [step_slots[r] for r in running])
+            q = wl.step_queries(seed, step, B, Hq, D, dtype)
+            maxL = int(lens.max())
+            o = out[:B]
+            ops.paged_attention_decode(o, to_dev(q, dtype), kc, vc, torch.from_numpy(tables).cuda(),
+                                       torch.from_numpy(lens).cuda(), maxL, scale, partition_size, ws)
+            if step % check_every == 0:
+                torch.cuda.synchronize()
+                ref = oatt.paged_decode(q, cache, otables, olens, scale)
+                err = float(np.abs(o.cpu().numpy() - ref).max())
+                st.max_abs_err = max(st.max_abs_err, err)
+                st.attention_checks += 1
+                if not err <= atol:
+                    st.errors.append((step, err))
+        for r in running:
+            generated[r] += 1
+        st.steps += 1
+        step += 1
+    # every request ran to completion and returned its blocks
+    assert max_steps is not None or st.finished == n_requests
+    if max_steps is None:
+        assert pool.num_free() == num_blocks and opool.num_free() == num_blocks
+    return st

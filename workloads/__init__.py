@@ -234,6 +234,17 @@ def token_kv_bulk(seed: int, rid: int, count: int, Hkv: int, D: int, dtype: str)
     return normal_bits(r, (count, Hkv, D), dtype), normal_bits(r, (count, Hkv, D), dtype)
 
 
+def step_kv(seed: int, step: int, B: int, Hkv: int, D: int, dtype: str):
+    """K/V bits of the B tokens a decode step appends (one stream per step)."""
+    r = np.random.default_rng([seed, 1 << 42, step])
+    return normal_bits(r, (B, Hkv, D), dtype), normal_bits(r, (B, Hkv, D), dtype)
+
+
+def shuffled_free_order(seed: int, num_blocks: int) -> np.ndarray:
+    """A seeded permutation of the pool's block ids (allocation pops from the end)."""
+    return np.random.default_rng([seed, 1 << 43]).permutation(num_blocks).astype(np.int32)
+
+
 def step_queries(seed: int, step: int, B: int, Hq: int, D: int, dtype: str):
     r = np.random.default_rng([seed, 1 << 41, step])
     return normal_bits(r, (B, Hq, D), dtype)
