@@ -2,9 +2,10 @@
 """Benchmark of the paged decode-attention hot path on one MI355X.
 
 A step is one continuous-batching decode step of one attention layer over a batch that is
-already resident in HBM: the cache append of every sequence's new token (paged_cache_append)
-followed by paged decode attention over all cached tokens (partition kernel + log-sum-exp
-reduce).  Default workload: Llama-3-8B-shaped layer, 32 q / 8 kv heads of 128, bf16, batch 64,
+already resident in HBM: the cache append of every sequence's new token and paged decode
+attention over all cached tokens.  By default the step is paged_attention_decode_append (the
+append fused into the decode partition kernel, then the log-sum-exp reduce); --separate times
+paged_cache_append followed by paged_attention_decode instead.  Default workload: Llama-3-8B-shaped layer, 32 q / 8 kv heads of 128, bf16, batch 64,
 context lengths ~ U[128, 2048], 16-token blocks scattered through a shuffled pool, split-K over
 512-token partitions.
 
@@ -13,7 +14,7 @@ Metric: effective KV+Q bytes per step / step time (GB/s), with KV = sum_b L_b * 
 Inputs rotate over R replicas of the caches (>= 1 GiB in total) so that the 256 MB last-level
 cache cannot serve repeated reads.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload llama|long]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload llama|long] [--separate]
 """
 from __future__ import annotations
 
@@ -43,6 +44,9 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB of caches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true",
+                    help="time paged_cache_append + paged_attention_decode as two calls instead of the fused "
+                         "paged_attention_decode_append")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from two rocprofv3 --pmc counter_collection.csv files "
                          "(FETCH_SIZE run, WRITE_SIZE run) of this script, then exit")
@@ -213,12 +217,15 @@ def main():
         out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
         ws = ops.decode_workspace(w.B, w.Hq, w.D, maxL, w.partition_size, device=dev)
         reps.append((ops.PreparedAppend(k, v, sk, sv, slots_t),
-                     ops.PreparedDecode(out, q, k, v, tables_t, lens_t, maxL, w.scale, w.partition_size, ws)))
+                     ops.PreparedDecode(out, q, k, v, tables_t, lens_t, maxL, w.scale, w.partition_size, ws,
+                                        new_key=None if args.separate else sk,
+                                        new_value=None if args.separate else sv)))
     torch.cuda.synchronize()
 
     def step(i):
         app, dec = reps[i % R]
-        app()
+        if args.separate:
+            app()
         dec.partitions()
         dec.reduce()
 
@@ -246,7 +253,7 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / args.steps
 
-    t_app = avg_us(lambda i: reps[i % R][0]())
+    t_app = avg_us(lambda i: reps[i % R][0]()) if args.separate else 0.0
     t_part = avg_us(lambda i: reps[i % R][1].partitions())
     t_red = avg_us(lambda i: reps[i % R][1].reduce())
 
@@ -301,13 +308,15 @@ def main():
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "seqs_steps_per_s": round(w.B / (wall / args.steps), 1),
         "kv_plus_q_bytes_per_step": step_bytes,
+        "step": ("paged_cache_append + paged_attention_decode (partitions, reduce)" if args.separate else
+                 "paged_attention_decode_append (fused append + partitions, reduce)"),
         "kernel_us": {"append": round(float(t_app), 3), "decode_partitions": round(part_us, 3),
                       "decode_reduce": round(float(t_red), 3)},
         "host_pool_and_builders_us_per_step": round(host_us, 1),
         "device_copy_probe_gbs": round(copy_gbs, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_mfma_kernel (partition pass)",
+            "kernel": "decode_mfma_kernel (partition pass" + ("" if args.separate else ", fused append") + ")",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

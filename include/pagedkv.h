@@ -166,6 +166,37 @@ int paged_attention_decode_reduce(void* out, int32_t out_dtype, const int32_t* c
                                   pkv_stream_t stream);
 
 /*
+ * paged_attention_decode_append - one decode step with the step's cache append fused in.
+ * [Serving] Steps 4 and 6 in one launch: every sequence's newest token (position
+ * context_lens[b] - 1) is written into its slot, block block_tables[b][(L - 1) / block_size],
+ * offset (L - 1) % block_size (the slot pkv_seq_append / pkv_seqs_append reserved for it), and
+ * attention over all context_lens[b] tokens uses that token's K/V straight from new_key /
+ * new_value.  Same result, bit for bit, as paged_cache_append of those tokens followed by
+ * paged_attention_decode; one launch fewer.
+ *
+ *   new_key, new_value device [B][num_kv_heads][head_dim] of `dtype`, 16-byte aligned.
+ *   k_cache, v_cache   device, written at the B new slots only.
+ *   Other arguments as paged_attention_decode.  The slots must be private to their sequences
+ *   (copy-on-write copies done first) and distinct.  bf16 / fp16 only: PKV_EUNSUPPORTED for
+ *   PKV_F32.
+ */
+int paged_attention_decode_append(void* out, int32_t out_dtype, const void* query, const void* new_key,
+                                  const void* new_value, void* k_cache, void* v_cache, const int32_t* block_tables,
+                                  const int32_t* context_lens, int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
+                                  int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
+                                  int32_t num_blocks, int32_t max_context_len, float scale, int32_t partition_size,
+                                  void* workspace, size_t workspace_bytes, int32_t dtype, pkv_stream_t stream);
+/* Its partition launch alone (then paged_attention_decode_reduce), as for paged_attention_decode. */
+int paged_attention_decode_append_partitions(void* out, int32_t out_dtype, const void* query, const void* new_key,
+                                             const void* new_value, void* k_cache, void* v_cache,
+                                             const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                             int32_t max_context_len, float scale, int32_t partition_size,
+                                             void* workspace, size_t workspace_bytes, int32_t dtype,
+                                             pkv_stream_t stream);
+
+/*
  * paged_attention_prefill_chunk - causal attention of one prompt chunk against the paged cache.
  * [Chapter] "How the scheduler works" and [Notes] "Prefill gets in the way": a long prompt is
  * prefilled in chunks that fit a per-step token budget.  Row i of the chunk sits at absolute

@@ -51,6 +51,10 @@ struct DecodeArgs {
   int32_t max_parts;
   int32_t part_size;  // tokens per partition, multiple of 16
   float scale_log2;   // scale * log2(e)
+  const void* new_k;  // fused append: [B][Hkv][D] K/V of the token at position L - 1
+  const void* new_v;
+  void* k_out;        // fused append: the caches, written at that token's slot
+  void* v_out;
 };
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -140,7 +144,14 @@ __device__ __forceinline__ void emit(const DecodeArgs& a, int b, int hq, int p, 
 // successor's loads outstanding.  The partition's block ids are loaded one per lane together with
 // the context length (64 blocks per load), so a step's tile addresses come from a lane read.
 // ------------------------------------------------------------------------------------------
-template <int DT, int DT_OUT, int D, int G, int NW>
+//
+// NEWTOK (fused append): the token at position L - 1 is this step's new token and its K/V come
+// from the input rows new_k / new_v instead of the cache.  It lies in the sequence's last
+// partition, in the last 32-token step of that partition; the wave that owns that step loads
+// the new K/V straight into the operand layout, substitutes them for the cache slot's (stale)
+// contents in its registers, and stores them into the slot (block table[(L - 1) / 16], offset
+// (L - 1) % 16).  No other workgroup reads that slot in the same launch.
+template <int DT, int DT_OUT, int D, int G, int NW, bool NEWTOK>
 __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
@@ -167,6 +178,37 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
   const int q4 = lane >> 4;
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v);
+  const int nsteps = (pend - pstart + 31) >> 5;
+
+  // Fused append: where the new token sits in the operand registers of its step (see the
+  // token order below): K rows in lanes n16 == nk_lane (set nk_set), V elements nk_e of the
+  // fragments in lanes q4 == nv_q4.
+  const int last_st = nsteps - 1;
+  const bool owner = NEWTOK && p == nparts - 1 && w == last_st % NW;
+  const int nu = (L - 1) - (pstart + last_st * 32);  // index of the new token inside its step
+  const int ntt = (L - 1) & 15;                     // offset inside its block
+  const int nk_lane = (nu >> 4) * 8 + (ntt >> 3) * 4 + (ntt & 3);
+  const int nk_set = (ntt >> 2) & 1;
+  const int nv_q4 = (nu >> 4) * 2 + (ntt >> 3);
+  u32x4 nk[KS];
+  uint32_t nv[NB];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) nk[ks] = u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) nv[nb] = 0;
+  if (owner) {
+    const int64_t row = (static_cast<int64_t>(b) * a.Hkv + g) * D;
+    const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + row;
+    const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + row;
+    if (n16 == nk_lane) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) nk[ks] = *reinterpret_cast<const u32x4*>(krow + (4 * ks + q4) * 8);
+    }
+    if (q4 == nv_q4) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) nv[nb] = vrow[nb * 16 + n16];
+    }
+  }
 
   // Q^T fragments: lane (head n16, group q4) holds Q[head][ks*32 + 8*q4 .. +8]; padded heads are 0.
   u32x4 qf[KS];
@@ -195,7 +237,6 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
   float m_run = -INFINITY;  // reference maximum (log2 domain), meaningful in lanes n16 < G
   float l_run = 0.f;        // this lane's share of sum p
 
-  const int nsteps = (pend - pstart + 31) >> 5;
   for (int c0 = 0; c0 < nsteps; c0 += kTableSteps) {
     const int cend = min(nsteps, c0 + kTableSteps);
     int st = c0 + w;
@@ -235,6 +276,36 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
     // The empty asm statements keep those loads where they are written.
     auto step = [&](int s, const bool prefetch) {
       const int nvalid = min(32, pend - (pstart + s * 32));
+      if (!prefetch && owner && s == last_st) {
+        // The new token replaces what its cache slot held before this launch.  The last step of
+        // a wave is always the one issued without a successor.  The asm operands keep the
+        // compiler from consuming (and so waiting for) the new token's loads before this step.
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(nk[ks]));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(nv[nb]));
+        if (n16 == nk_lane) {
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            if (nk_set) {
+              kf[KS + ks] = nk[ks];
+            } else {
+              kf[ks] = nk[ks];
+            }
+          }
+        }
+        if (q4 == nv_q4) {
+          const int e = ntt & 7;
+          const uint32_t sh = (e & 1) * 16;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+              if (wd == (e >> 1)) vf[nb][wd] = (vf[nb][wd] & ~(0xFFFFu << sh)) | (nv[nb] << sh);
+            }
+          }
+        }
+      }
       f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -321,6 +392,21 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
     load_v(st);
     for (; st + NW < cend; st += NW) step(st, true);
     step(st, false);
+  }
+
+  if (owner) {
+    // Store the new token into its slot.
+    const int blk = clamp_blk(a, table[(L - 1) >> 4]);
+    uint16_t* kt = static_cast<uint16_t*>(a.k_out) + (static_cast<int64_t>(blk) * a.Hkv + g) * TILE;
+    uint16_t* vt = static_cast<uint16_t*>(a.v_out) + (static_cast<int64_t>(blk) * a.Hkv + g) * TILE;
+    if (n16 == nk_lane) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<u32x4*>(kt + k_chunk_pos(ntt, 4 * ks + q4) * 8) = nk[ks];
+    }
+    if (q4 == nv_q4) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) vt[(nb * 16 + n16) * kBlock + ntt] = static_cast<uint16_t>(nv[nb]);
+    }
   }
 
   // Per-head sums over the four lane groups.
@@ -445,13 +531,54 @@ __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Log-sum-exp merge of partitions.  grid = (Hq, B), D threads.
+// Log-sum-exp merge of partitions.  grid = (Hq, B), D threads.  MAXP >= max_parts: every partial
+// of the row is loaded at once, together with the context length (one memory latency); the
+// sequence's own partition count then selects which take part.  Rows of single-partition
+// sequences were written by the partition pass and are left alone.
 // ------------------------------------------------------------------------------------------
-template <int DT_OUT>
+template <int DT_OUT, int MAXP>
 __global__ void __launch_bounds__(128) decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ part_ml,
                                                             const float* __restrict__ part_o,
                                                             const int32_t* __restrict__ lens, int32_t Hq, int32_t D,
                                                             int32_t max_parts, int32_t part_size) {
+  const int h = blockIdx.x;
+  const int b = blockIdx.y;
+  const int d = threadIdx.x;
+  if (d >= D) return;
+  const int64_t row0 = (static_cast<int64_t>(b) * Hq + h) * max_parts;
+  float m[MAXP], l[MAXP], o[MAXP];
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    const bool in = p < max_parts;
+    m[p] = in ? part_ml[(row0 + p) * 2] : -INFINITY;
+    l[p] = in ? part_ml[(row0 + p) * 2 + 1] : 0.f;
+    o[p] = in ? part_o[(row0 + p) * D + d] : 0.f;
+  }
+  const int L = min(lens[b], max_parts * part_size);
+  const int nparts = (L + part_size - 1) / part_size;
+  if (nparts <= 1) return;
+  float M = -INFINITY;
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) M = p < nparts ? fmaxf(M, m[p]) : M;
+  float acc = 0.f, lsum = 0.f;
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) {
+    if (p < nparts) {
+      const float f = fast_exp2(m[p] - M);
+      acc += f * o[p];
+      lsum += f * l[p];
+    }
+  }
+  store_from_float<DT_OUT>(out, (static_cast<int64_t>(b) * Hq + h) * D + d, acc / lsum);
+}
+
+// Any number of partitions: the same merge, loads in a loop.
+template <int DT_OUT>
+__global__ void __launch_bounds__(128) decode_reduce_loop_kernel(void* __restrict__ out,
+                                                                 const float* __restrict__ part_ml,
+                                                                 const float* __restrict__ part_o,
+                                                                 const int32_t* __restrict__ lens, int32_t Hq,
+                                                                 int32_t D, int32_t max_parts, int32_t part_size) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int d = threadIdx.x;
@@ -543,10 +670,18 @@ int launch_valu(const DecodeArgs& a, int B, hipStream_t s) {
 template <int DT, int DT_OUT, int D, int G>
 int launch_mfma(const DecodeArgs& a, int B, hipStream_t s) {
   const dim3 grid(a.Hkv, B, a.max_parts);
-  if (a.part_size <= 512)
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, DT_OUT, D, G, 4>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<DT, DT_OUT, D, G, 8>), grid, dim3(512), 0, s, a);
+  const bool fused = a.new_k != nullptr;
+  if (a.part_size <= 512) {
+    if (fused)
+      hipLaunchKernelGGL((decode_mfma_kernel<DT, DT_OUT, D, G, 4, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<DT, DT_OUT, D, G, 4, false>), grid, dim3(256), 0, s, a);
+  } else {
+    if (fused)
+      hipLaunchKernelGGL((decode_mfma_kernel<DT, DT_OUT, D, G, 8, true>), grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_mfma_kernel<DT, DT_OUT, D, G, 8, false>), grid, dim3(512), 0, s, a);
+  }
   return PKV_OK;
 }
 
@@ -581,22 +716,30 @@ int launch_partitions(const DecodeArgs& a, int32_t dtype, int32_t out_dtype, int
   }
 }
 
+template <int DT_OUT>
+void launch_reduce_t(void* out, const float* ml, const float* po, const int32_t* lens, int B, int Hq, int D,
+                     int max_parts, int part_size, hipStream_t s) {
+  const dim3 grid(Hq, B), block(D);
+  if (max_parts <= 4)
+    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 4>), grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
+                       part_size);
+  else if (max_parts <= 8)
+    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 8>), grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
+                       part_size);
+  else if (max_parts <= 16)
+    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 16>), grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
+                       part_size);
+  else
+    hipLaunchKernelGGL((decode_reduce_loop_kernel<DT_OUT>), grid, block, 0, s, out, ml, po, lens, Hq, D,
+                       max_parts, part_size);
+}
+
 int launch_reduce(void* out, int32_t out_dtype, const float* ml, const float* po, const int32_t* lens, int B, int Hq,
                   int D, int max_parts, int part_size, hipStream_t s) {
-  const dim3 grid(Hq, B), block(D);
   switch (out_dtype) {
-    case PKV_BF16:
-      hipLaunchKernelGGL(decode_reduce_kernel<PKV_BF16>, grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
-                         part_size);
-      break;
-    case PKV_F16:
-      hipLaunchKernelGGL(decode_reduce_kernel<PKV_F16>, grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
-                         part_size);
-      break;
-    default:
-      hipLaunchKernelGGL(decode_reduce_kernel<PKV_F32>, grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
-                         part_size);
-      break;
+    case PKV_BF16: launch_reduce_t<PKV_BF16>(out, ml, po, lens, B, Hq, D, max_parts, part_size, s); break;
+    case PKV_F16: launch_reduce_t<PKV_F16>(out, ml, po, lens, B, Hq, D, max_parts, part_size, s); break;
+    default: launch_reduce_t<PKV_F32>(out, ml, po, lens, B, Hq, D, max_parts, part_size, s); break;
   }
   return PKV_OK;
 }
@@ -612,19 +755,26 @@ extern "C" size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32
   return make_plan(num_seqs, num_q_heads, head_dim, max_context_len, partition_size).need_bytes;
 }
 
-extern "C" int paged_attention_decode_partitions(void* out, int32_t out_dtype, const void* query, const void* k_cache,
-                                                 const void* v_cache, const int32_t* block_tables,
-                                                 const int32_t* context_lens, int32_t B, int32_t num_q_heads,
-                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
-                                                 int32_t max_blocks_per_seq, int32_t num_blocks,
-                                                 int32_t max_context_len, float scale, int32_t partition_size,
-                                                 void* workspace, size_t workspace_bytes, int32_t dtype,
-                                                 pkv_stream_t stream) {
-  int st = validate("paged_attention_decode_partitions", out, out_dtype, query, k_cache, v_cache, block_tables,
-                    context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
-                    max_context_len, partition_size, workspace, workspace_bytes, dtype);
-  if (st != PKV_OK || B == 0 || max_context_len == 0) return st;
-  const Plan pl = make_plan(B, num_q_heads, head_dim, max_context_len, partition_size);
+namespace pkv {
+namespace {
+
+// Partition pass shared by the plain and the fused-append entry points (new_k == nullptr: plain).
+int partitions_impl(const char* fn, void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                    const void* v_cache, const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                    int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t max_blocks, int32_t num_blocks,
+                    int32_t max_ctx, float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                    int32_t dtype, const void* new_k, const void* new_v, void* k_out, void* v_out,
+                    pkv_stream_t stream) {
+  int st = validate(fn, out, out_dtype, query, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D, bs,
+                    max_blocks, num_blocks, max_ctx, partition_size, workspace, workspace_bytes, dtype);
+  if (st != PKV_OK || B == 0 || max_ctx == 0) return st;
+  if (new_k != nullptr || new_v != nullptr) {
+    if (dtype == PKV_F32) return fail(PKV_EUNSUPPORTED, "%s: fused append needs bf16 or fp16 caches", fn);
+    if (!new_k || !new_v) return fail(PKV_EINVAL, "%s: NULL new_key or new_value", fn);
+    if ((reinterpret_cast<uintptr_t>(new_k) | reinterpret_cast<uintptr_t>(new_v)) % 16 != 0)
+      return fail(PKV_EINVAL, "%s: new_key and new_value must be 16-byte aligned", fn);
+  }
+  const Plan pl = make_plan(B, Hq, D, max_ctx, partition_size);
   DecodeArgs a{};
   a.out = out;
   a.q = query;
@@ -634,15 +784,48 @@ extern "C" int paged_attention_decode_partitions(void* out, int32_t out_dtype, c
   a.lens = context_lens;
   a.part_ml = pl.need_bytes ? static_cast<float*>(workspace) : nullptr;
   a.part_o = pl.need_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + pl.ml_bytes) : nullptr;
-  a.Hq = num_q_heads;
-  a.Hkv = num_kv_heads;
-  a.max_blocks = max_blocks_per_seq;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.max_blocks = max_blocks;
   a.num_blocks = num_blocks;
   a.max_parts = pl.max_parts;
   a.part_size = pl.part_size;
   a.scale_log2 = scale * kLog2e;
-  launch_partitions(a, dtype, out_dtype, head_dim, B, as_stream(stream));
-  return check_launch("paged_attention_decode_partitions");
+  a.new_k = new_k;
+  a.new_v = new_v;
+  a.k_out = k_out;
+  a.v_out = v_out;
+  launch_partitions(a, dtype, out_dtype, D, B, as_stream(stream));
+  return check_launch(fn);
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int paged_attention_decode_partitions(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                                 const void* v_cache, const int32_t* block_tables,
+                                                 const int32_t* context_lens, int32_t B, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                 int32_t max_blocks_per_seq, int32_t num_blocks,
+                                                 int32_t max_context_len, float scale, int32_t partition_size,
+                                                 void* workspace, size_t workspace_bytes, int32_t dtype,
+                                                 pkv_stream_t stream) {
+  return partitions_impl("paged_attention_decode_partitions", out, out_dtype, query, k_cache, v_cache, block_tables,
+                         context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
+                         num_blocks, max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
+                         nullptr, nullptr, nullptr, nullptr, stream);
+}
+
+extern "C" int paged_attention_decode_append_partitions(
+    void* out, int32_t out_dtype, const void* query, const void* new_key, const void* new_value, void* k_cache,
+    void* v_cache, const int32_t* block_tables, const int32_t* context_lens, int32_t B, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    int32_t dtype, pkv_stream_t stream) {
+  return partitions_impl("paged_attention_decode_append_partitions", out, out_dtype, query, k_cache, v_cache,
+                         block_tables, context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size,
+                         max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size, workspace,
+                         workspace_bytes, dtype, new_key, new_value, k_cache, v_cache, stream);
 }
 
 extern "C" int paged_attention_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, int32_t B,
@@ -677,6 +860,24 @@ extern "C" int paged_attention_decode(void* out, int32_t out_dtype, const void* 
                                              num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                                              num_blocks, max_context_len, scale, partition_size, workspace,
                                              workspace_bytes, dtype, stream);
+  if (st != PKV_OK) return st;
+  return paged_attention_decode_reduce(out, out_dtype, context_lens, B, num_q_heads, head_dim, max_context_len,
+                                       partition_size, workspace, workspace_bytes, stream);
+}
+
+extern "C" int paged_attention_decode_append(void* out, int32_t out_dtype, const void* query, const void* new_key,
+                                             const void* new_value, void* k_cache, void* v_cache,
+                                             const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                             int32_t max_context_len, float scale, int32_t partition_size,
+                                             void* workspace, size_t workspace_bytes, int32_t dtype,
+                                             pkv_stream_t stream) {
+  int st = paged_attention_decode_append_partitions(out, out_dtype, query, new_key, new_value, k_cache, v_cache,
+                                                    block_tables, context_lens, B, num_q_heads, num_kv_heads,
+                                                    head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                                    max_context_len, scale, partition_size, workspace,
+                                                    workspace_bytes, dtype, stream);
   if (st != PKV_OK) return st;
   return paged_attention_decode_reduce(out, out_dtype, context_lens, B, num_q_heads, head_dim, max_context_len,
                                        partition_size, workspace, workspace_bytes, stream);

@@ -95,6 +95,25 @@ def paged_attention_decode(out, query, k_cache, v_cache, block_tables, context_l
     check(lib.paged_attention_decode(*args, _stream(stream)))
 
 
+def _fused_args(args, new_key, new_value):
+    """Argument tuple of the fused-append entry points from a _decode_args tuple."""
+    _dev(new_key, new_value)
+    B, Hkv, D = args[7], args[9], args[10]
+    for t in (new_key, new_value):
+        if tuple(t.shape) != (B, Hkv, D) or dtype_code(t.dtype) != args[-1]:
+            raise ValueError("new_key/new_value must be [B][Hkv][D] of the cache dtype")
+    return args[:3] + (new_key.data_ptr(), new_value.data_ptr()) + args[3:]
+
+
+def paged_attention_decode_append(out, query, new_key, new_value, k_cache, v_cache, block_tables, context_lens,
+                                  max_context_len, scale, partition_size=0, workspace=None, stream=None) -> None:
+    """One decode step with the append fused in: token context_lens[b] - 1 of every sequence
+    (new_key/new_value [B][Hkv][D]) is written to its slot and attended over."""
+    args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                        partition_size, workspace)
+    check(lib.paged_attention_decode_append(*_fused_args(args, new_key, new_value), _stream(stream)))
+
+
 def paged_attention_decode_partitions(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                                       partition_size, workspace, stream=None) -> None:
     args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
@@ -132,20 +151,27 @@ class PreparedDecode:
     C-ABI call (the tensors must stay alive and unchanged in shape)."""
 
     def __init__(self, out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                 partition_size=0, workspace=None, stream=None):
-        self._keep = (out, query, k_cache, v_cache, block_tables, context_lens, workspace)
+                 partition_size=0, workspace=None, stream=None, new_key=None, new_value=None):
+        self._keep = (out, query, k_cache, v_cache, block_tables, context_lens, workspace, new_key, new_value)
         self.args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                                  partition_size, workspace)
+        self.fused_args = None if new_key is None else _fused_args(self.args, new_key, new_value)
         self.stream = _stream(stream)
         B, Hq, D = query.shape
         self.reduce_args = (out.data_ptr(), dtype_code(out.dtype), context_lens.data_ptr(), B, Hq, D,
                             int(max_context_len), int(partition_size), self.args[17], self.args[18])
 
     def __call__(self) -> None:
-        check(lib.paged_attention_decode(*self.args, self.stream))
+        if self.fused_args is not None:
+            check(lib.paged_attention_decode_append(*self.fused_args, self.stream))
+        else:
+            check(lib.paged_attention_decode(*self.args, self.stream))
 
     def partitions(self) -> None:
-        check(lib.paged_attention_decode_partitions(*self.args, self.stream))
+        if self.fused_args is not None:
+            check(lib.paged_attention_decode_append_partitions(*self.fused_args, self.stream))
+        else:
+            check(lib.paged_attention_decode_partitions(*self.args, self.stream))
 
     def reduce(self) -> None:
         check(lib.paged_attention_decode_reduce(*self.reduce_args, self.stream))
