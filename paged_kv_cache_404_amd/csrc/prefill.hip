@@ -9,12 +9,13 @@
 // softmax, weighted sum of values; [Serving] "Production Serving: Continuous Batching and
 // PagedAttention", The Build, Step 6).
 //
-// MI355X mapping: a wavefront owns 16 consecutive chunk rows of one query head; a workgroup holds
-// the G query heads of one GQA group (same rows, same K/V tiles, which therefore hit in cache
-// after the first wave).  Per 32-token key step, S^T = K.Q^T (2 x D/32 MFMA 16x16x32) and
-// O += P.V (D/16 MFMA, twice: P split into hi + lo 16-bit rows so the weights keep ~16 mantissa
-// bits).  The causal limit only masks the last steps of each row tile.  Workgroups are ordered
-// so that consecutive ids on one XCD work on the same KV head (its K/V then stay in that XCD's L2).
+// MI355X mapping: a workgroup owns 16 consecutive chunk rows of the G query heads of one KV
+// head; its waves split the key range and the heads, and each wave serves two heads from every
+// K/V fragment it loads.  Per
+// 32-key step, S^T = K.Q^T (2 x D/32 MFMA 16x16x32) and O += P.V (D/16 MFMA, twice: P split
+// into hi + lo 16-bit rows so the weights keep ~16 mantissa bits).  The causal limit only masks
+// the last steps of each row tile.  Workgroups are ordered so that consecutive ids on one XCD
+// work on the same KV head (its K/V then stay in that XCD's L2).
 #include <cmath>
 
 #include "device.h"
@@ -67,11 +68,32 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   }
 }
 
+// One workgroup = 16 chunk rows x the G query heads of one KV head.  A wave owns HPW = min(G, 2)
+// heads of the group (HSETS = G / HPW head sets) over one key split (KSPLIT splits of the row
+// tile's keys; HSETS x KSPLIT <= 8 waves, two per SIMD): every K/V fragment it loads feeds the
+// Q.K and P.V products of both its heads, halving the vector-memory bytes per matrix
+// instruction (more heads per wave overflow the 256 architectural registers).  Each wave walks its consecutive 32-key steps with one step of
+// K/V in flight (next K once this step's Q.K products have consumed the K registers, next V
+// after the last P.V); block ids of 64 blocks at a time sit one per lane.  The splits are
+// merged exactly through LDS (log-sum-exp) at the end.
+template <int G>
+struct PrefillShape {
+  static constexpr int HPW = G < 2 ? G : 2;
+  static constexpr int HSETS = G / HPW;
+  static constexpr int KSPLIT = HSETS >= 4 ? 2 : 4;
+  static constexpr int NWAVES = HSETS * KSPLIT;
+};
+
 template <int DT, int DT_OUT, int D, int G>
-__global__ void __launch_bounds__(G * 64) prefill_mfma_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(PrefillShape<G>::NWAVES * 64) prefill_mfma_kernel(PrefillArgs a) {
   constexpr int KS = D / 32;
   constexpr int NB = D / 16;
   constexpr int TILE = kBlock * D;
+  constexpr int HPW = PrefillShape<G>::HPW;
+  constexpr int HSETS = PrefillShape<G>::HSETS;
+  constexpr int KSPLIT = PrefillShape<G>::KSPLIT;
+  constexpr int NT = PrefillShape<G>::NWAVES * 64;
+  constexpr int kTableSteps = 32;
 
   // XCD-aware order: hardware places workgroup id on XCD (id % 8); give every XCD whole KV heads.
   const int nwg = a.row_tiles * a.Hkv;
@@ -90,163 +112,254 @@ __global__ void __launch_bounds__(G * 64) prefill_mfma_kernel(PrefillArgs a) {
   tile = a.row_tiles - 1 - tile;
 
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;  // query head within the group
-  const int hq = g * G + w;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int hs = w % HSETS;  // head set
+  const int sp = w / HSETS;  // key split
+  const int hq0 = g * G + hs * HPW;
   const int n16 = lane & 15;
   const int q4 = lane >> 4;
-  const int i0 = tile * 16;            // first chunk row of this tile
-  const int my_row = i0 + n16;         // chunk row held in this lane's S^T column
+  const int i0 = tile * 16;       // first chunk row of this tile
+  const int my_row = i0 + n16;    // chunk row held in this lane's S^T column
   const bool row_ok = my_row < a.C;
   const int row_lim = a.ctx_start + min(my_row, a.C - 1);  // last visible key position of that row
 
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v);
 
-  u32x4 qf[KS];
-  {
+  u32x4 qf[HPW][KS];
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) {
     const uint16_t* qrow =
-        static_cast<const uint16_t*>(a.q) + (static_cast<int64_t>(min(my_row, a.C - 1)) * a.Hq + hq) * D;
+        static_cast<const uint16_t*>(a.q) + (static_cast<int64_t>(min(my_row, a.C - 1)) * a.Hq + hq0 + h) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
-      qf[ks] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + ks * 32 + q4 * 8) : u32x4{0, 0, 0, 0};
+      qf[h][ks] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + ks * 32 + q4 * 8) : u32x4{0, 0, 0, 0};
   }
 
   // Q.K product #s row m holds token 8*(m/4) + m%4 + 4s of the step's block m/8; in the K tile
-  // order those rows of one k-step are one 512-byte run per block (see k_chunk_pos).
+  // order those rows of one k-step are one 512-byte run per block (see k_chunk_pos).  Lane
+  // (row, q4) then holds the scores of step keys 8*q4 .. 8*q4+7, the k-range of its P row.
   const bool k_from_b = n16 >= 8;
   const int k_in_tile = (q4 * 8 + (n16 & 7)) * 8;
-  const int vhalf = q4 >> 1;
-  const int vcol = (q4 & 1) * 8;
+  const bool v_from_b = q4 >= 2;
+  const int v_in_tile = n16 * kBlock + (q4 & 1) * 8;
 
-  f32x4 o[NB];
+  f32x4 o[HPW][NB];
+  float m_run[HPW], l_run[HPW];  // per head: reference maximum (log2 domain) and this lane's sum
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  for (int h = 0; h < HPW; ++h) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) o[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[h] = -INFINITY;
+    l_run[h] = 0.f;
+  }
 
   const int last_row = min(i0 + 15, a.C - 1);
   const int nkeys = a.ctx_start + last_row + 1;  // keys any row of the tile can see
   const int full_keys = a.ctx_start + i0 + 1;    // keys every row of the tile sees
   const int nsteps = (nkeys + 31) >> 5;
-  for (int st = 0; st < nsteps; ++st) {
-    const int t0 = st * 32;
-    const int nvalid = min(32, nkeys - t0);
-    const int lb = t0 >> 4;
+  const int per_split = (nsteps + KSPLIT - 1) / KSPLIT;
+  const int s_lo = min(nsteps, sp * per_split);
+  const int s_hi = min(nsteps, s_lo + per_split);
+  const int kblocks = (nkeys + 15) >> 4;  // blocks the tile reads; the table holds at least these
+  const float c = a.scale_log2;
+
+  for (int c0 = s_lo; c0 < s_hi; c0 += kTableSteps) {
+    const int cend = min(s_hi, c0 + kTableSteps);
+    const int cb0 = 2 * c0;
+    const int cnb = min(2 * kTableSteps, kblocks - cb0);
     // block ids are a precondition; clamping turns a bad id into a wrong value instead of a fault
-    const int blkA = min(max(a.table[lb], 0), a.num_blocks - 1);
-    const int blkB = nvalid > 16 ? min(max(a.table[lb + 1], 0), a.num_blocks - 1) : blkA;
-    const int64_t tileA = (static_cast<int64_t>(blkA) * a.Hkv + g) * TILE;
-    const int64_t tileB = (static_cast<int64_t>(blkB) * a.Hkv + g) * TILE;
+    const int tab = min(max(a.table[min(cb0 + lane, kblocks - 1)], 0), a.num_blocks - 1);
 
-    const uint16_t* kp = kc + (k_from_b ? tileB : tileA) + k_in_tile;
-    u32x4 k1[KS], k2[KS];
+    u32x4 kf[2 * KS], vf[NB];
+    auto tiles = [&](int st, int64_t& tA, int64_t& tB) {
+      const int j = 2 * (st - c0);
+      const int bA = __builtin_amdgcn_readlane(tab, j);
+      const int bB = __builtin_amdgcn_readlane(tab, min(j + 1, cnb - 1));  // a lone last block pairs with itself
+      tA = (static_cast<int64_t>(bA) * a.Hkv + g) * TILE;
+      tB = (static_cast<int64_t>(bB) * a.Hkv + g) * TILE;
+    };
+    auto load_k = [&](int st) {
+      int64_t tA, tB;
+      tiles(st, tA, tB);
+      const uint16_t* kp = kc + (k_from_b ? tB : tA) + k_in_tile;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      k1[ks] = *reinterpret_cast<const u32x4*>(kp + (2 * ks) * 256);
-      k2[ks] = *reinterpret_cast<const u32x4*>(kp + (2 * ks + 1) * 256);
-    }
-    const uint16_t* vbase = vc + (vhalf ? tileB : tileA) + n16 * kBlock + vcol;
-    u32x4 vf[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) vf[nb] = *reinterpret_cast<const u32x4*>(vbase + nb * 16 * kBlock);
-
-    f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      s1 = mfma16x16x32<DT>(k1[ks], qf[ks], s1);
-      s2 = mfma16x16x32<DT>(k2[ks], qf[ks], s2);
-    }
-    // Lane (row n16, q4) holds the scores of step tokens 8*q4 + i, i = 0..7.
-    const int tb = t0 + 8 * q4;
-    const bool masked_step = t0 + 32 > full_keys;
-    float sc[8];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      sc[j] = s1[j] * a.scale_log2;
-      sc[4 + j] = s2[j] * a.scale_log2;
-    }
-    if (masked_step) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sc[i] = (row_ok && tb + i <= row_lim) ? sc[i] : -INFINITY;
-    }
-    float bmax = sc[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sc[i]);
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-
-    const bool need = row_ok && (bmax > m_run + kLazyRescaleLog2);
-    if (__any(need)) {
-      const float m_new = need ? bmax : m_run;
-      const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;
-      l_run *= alpha;
-      m_run = m_new;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float f = __shfl(alpha, 4 * q4 + j);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) o[nb][j] *= f;
+      for (int ks = 0; ks < KS; ++ks) {
+        kf[ks] = *reinterpret_cast<const u32x4*>(kp + (2 * ks) * 256);
+        kf[KS + ks] = *reinterpret_cast<const u32x4*>(kp + (2 * ks + 1) * 256);
       }
-    }
-    float pv[8];
-    float psum = 0.f;
+    };
+    auto load_v = [&](int st) {
+      int64_t tA, tB;
+      tiles(st, tA, tB);
+      const uint16_t* vp = vc + (v_from_b ? tB : tA) + v_in_tile;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      pv[i] = row_ok ? fast_exp2(sc[i] - m_run) : 0.f;
-      psum += pv[i];
-    }
-    l_run += psum;
-    u32x4 hi, lo;
+      for (int nb = 0; nb < NB; ++nb) vf[nb] = *reinterpret_cast<const u32x4*>(vp + nb * 16 * kBlock);
+    };
+
+    // One 32-key step for all HPW heads; with `prefetch` the next step's loads are issued as
+    // registers free up (the empty asm statements keep them where they are written).
+    auto step = [&](int st, const bool prefetch) {
+      const int t0 = st * 32;
+      const int nvalid = min(32, nkeys - t0);
+      const bool masked = t0 + 32 > full_keys;  // causal limit (and the chunk's end) inside this step
+      f32x4 s1[HPW], s2[HPW];
 #pragma unroll
-    for (int wd = 0; wd < 4; ++wd) {
-      const uint32_t h0 = to16<DT>(pv[2 * wd]);
-      const uint32_t h1 = to16<DT>(pv[2 * wd + 1]);
-      hi[wd] = h0 | (h1 << 16);
-      lo[wd] = to16<DT>(pv[2 * wd] - from16<DT>(h0)) | (to16<DT>(pv[2 * wd + 1] - from16<DT>(h1)) << 16);
-    }
-    if (nvalid < 32) {
-      // Keys past the last visible one may be stale (or NaN): zero them in V.
-      const int keep = min(8, max(0, nvalid - 8 * q4));
+      for (int h = 0; h < HPW; ++h) {
+        s1[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        s2[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-        for (int wd = 0; wd < 4; ++wd) {
-          const uint32_t m = (2 * wd + 1 < keep) ? 0xFFFFFFFFu : ((2 * wd < keep) ? 0x0000FFFFu : 0u);
-          vf[nb][wd] &= m;
+        for (int ks = 0; ks < KS; ++ks) {
+          s1[h] = mfma16x16x32<DT>(kf[ks], qf[h][ks], s1[h]);
+          s2[h] = mfma16x16x32<DT>(kf[KS + ks], qf[h][ks], s2[h]);
         }
       }
-    }
+      if (prefetch) {
+        asm volatile("" ::: "memory");
+        load_k(st + 1);
+        asm volatile("" ::: "memory");
+      }
+      if (nvalid < 32) {
+        // Keys past the last visible one may be stale (or NaN): zero them in V.
+        const int keep = min(8, max(0, nvalid - 8 * q4));
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      o[nb] = mfma16x16x32<DT>(hi, vf[nb], o[nb]);
-      o[nb] = mfma16x16x32<DT>(lo, vf[nb], o[nb]);
-    }
+        for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+          for (int wd = 0; wd < 4; ++wd) {
+            const uint32_t m = (2 * wd + 1 < keep) ? 0xFFFFFFFFu : ((2 * wd < keep) ? 0x0000FFFFu : 0u);
+            vf[nb][wd] &= m;
+          }
+        }
+      }
+      const int tb = t0 + 8 * q4;
+#pragma unroll
+      for (int h = 0; h < HPW; ++h) {
+        // Raw scores; scale * log2(e) > 0 is applied inside the exponent, so maxima of raw
+        // scores give the maxima of scaled ones.
+        float sc[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sc[j] = s1[h][j];
+          sc[4 + j] = s2[h][j];
+        }
+        if (masked) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sc[i] = (row_ok && tb + i <= row_lim) ? sc[i] : -INFINITY;
+        }
+        float bmax = sc[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sc[i]);
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
+        bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+        bmax *= c;
+
+        const bool need = row_ok && (bmax > m_run[h] + kLazyRescaleLog2);
+        if (__any(need)) {
+          const float m_new = need ? bmax : m_run[h];
+          const float alpha = need ? fast_exp2(m_run[h] - m_new) : 1.0f;
+          l_run[h] *= alpha;
+          m_run[h] = m_new;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float f = __shfl(alpha, 4 * q4 + j);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) o[h][nb][j] *= f;
+          }
+        }
+        // A split can lie wholly past a row's causal limit: then the row has seen no key yet
+        // (m = -inf, every score -inf) and its weights must be 0, not exp2(-inf - -inf) = NaN.
+        const float m_ref = m_run[h] == -INFINITY ? 0.f : m_run[h];
+        float pv[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pv[i] = fast_exp2(fmaf(sc[i], c, -m_ref));
+          psum += pv[i];
+        }
+        l_run[h] += psum;
+        u32x4 hi, lo;
+#pragma unroll
+        for (int wd = 0; wd < 4; ++wd) {
+          const uint32_t h0 = to16<DT>(pv[2 * wd]);
+          const uint32_t h1 = to16<DT>(pv[2 * wd + 1]);
+          hi[wd] = h0 | (h1 << 16);
+          lo[wd] = to16<DT>(pv[2 * wd] - from16<DT>(h0)) | (to16<DT>(pv[2 * wd + 1] - from16<DT>(h1)) << 16);
+        }
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          o[h][nb] = mfma16x16x32<DT>(hi, vf[nb], o[h][nb]);
+          o[h][nb] = mfma16x16x32<DT>(lo, vf[nb], o[h][nb]);
+        }
+      }
+      if (prefetch) {
+        asm volatile("" ::: "memory");
+        load_v(st + 1);
+        asm volatile("" ::: "memory");
+      }
+    };
+
+    int st = c0;
+    load_k(st);
+    load_v(st);
+    for (; st + 1 < cend; ++st) step(st, true);
+    step(st, false);
   }
 
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  // O row r = 4*q4 + j is chunk row i0 + r; column nb*16 + n16.
+  // Merge the key splits: O row r = 4*q4 + j is chunk row i0 + r, column nb*16 + n16.  Rows of
+  // rows past the chunk (row_ok false) hold garbage and are never stored.
+  __shared__ float sO[KSPLIT][G][16][D];
+  __shared__ float sM[KSPLIT][G][16];
+  __shared__ float sL[KSPLIT][G][16];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 4 * q4 + j;
-    const float lr = __shfl(l_run, r);
-    const int row = i0 + r;
-    if (row < a.C) {
-      const float inv = 1.0f / lr;
+  for (int h = 0; h < HPW; ++h) {
+    float l = l_run[h];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int hg = hs * HPW + h;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb)
-        store_from_float<DT_OUT>(a.out, (static_cast<int64_t>(row) * a.Hq + hq) * D + nb * 16 + n16, o[nb][j] * inv);
+    for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sO[sp][hg][4 * q4 + j][nb * 16 + n16] = o[h][nb][j];
+    }
+    if (q4 == 0) {
+      sM[sp][hg][n16] = m_run[h];
+      sL[sp][hg][n16] = l;
     }
   }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * 16 * D; idx += NT) {
+    const int h = idx / (16 * D);
+    const int r = (idx / D) % 16;
+    const int d = idx % D;
+    const int row = i0 + r;
+    if (row >= a.C) continue;
+    float M = sM[0][h][r];
+#pragma unroll
+    for (int k = 1; k < KSPLIT; ++k) M = fmaxf(M, sM[k][h][r]);
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int k = 0; k < KSPLIT; ++k) {
+      const float f = fast_exp2(sM[k][h][r] - M);  // splits without a step hold m = -inf -> 0
+      acc += f * sO[k][h][r][d];
+      lsum += f * sL[k][h][r];
+    }
+    store_from_float<DT_OUT>(a.out, (static_cast<int64_t>(row) * a.Hq + g * G + h) * D + d, acc / lsum);
+  }
+}
+
+template <int DT, int DT_OUT, int D, int G>
+void launch_one(const PrefillArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((prefill_mfma_kernel<DT, DT_OUT, D, G>), dim3(a.row_tiles * a.Hkv),
+                     dim3(PrefillShape<G>::NWAVES * 64), 0, s, a);
 }
 
 template <int DT, int DT_OUT, int D>
 void launch_g(const PrefillArgs& a, hipStream_t s) {
-  const dim3 grid(a.row_tiles * a.Hkv);
   switch (a.Hq / a.Hkv) {
-    case 1: hipLaunchKernelGGL((prefill_mfma_kernel<DT, DT_OUT, D, 1>), grid, dim3(64), 0, s, a); break;
-    case 2: hipLaunchKernelGGL((prefill_mfma_kernel<DT, DT_OUT, D, 2>), grid, dim3(128), 0, s, a); break;
-    case 4: hipLaunchKernelGGL((prefill_mfma_kernel<DT, DT_OUT, D, 4>), grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL((prefill_mfma_kernel<DT, DT_OUT, D, 8>), grid, dim3(512), 0, s, a); break;
+    case 1: launch_one<DT, DT_OUT, D, 1>(a, s); break;
+    case 2: launch_one<DT, DT_OUT, D, 2>(a, s); break;
+    case 4: launch_one<DT, DT_OUT, D, 4>(a, s); break;
+    default: launch_one<DT, DT_OUT, D, 8>(a, s); break;
   }
 }
 
