@@ -329,8 +329,7 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
       float bmax = sc[0];
 #pragma unroll
       for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sc[i]);
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-      bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+      bmax = group4_max(bmax);
 
       const bool need = (n16 < G) && (bmax > m_run + kLazyRescaleLog2);
       if (__any(need)) {
@@ -366,10 +365,13 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
         hi[wd] = h0 | (h1 << 16);
         lo[wd] = l0 | (l1 << 16);
       }
+      // Lo rows G..2G-1 take the lo parts of heads 0..G-1: a row shift by G inside each 16-lane
+      // row (DPP row_shr), valid for the lanes that use it (n16 >= G).
       u32x4 pa;
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
-        const uint32_t lo_src = static_cast<uint32_t>(__shfl(static_cast<int>(lo[wd]), lane - G));
+        const uint32_t lo_src = static_cast<uint32_t>(
+            __builtin_amdgcn_mov_dpp(static_cast<int>(lo[wd]), 0x110 + G, 0xF, 0xF, false));
         pa[wd] = (n16 < G) ? hi[wd] : ((n16 < 2 * G) ? lo_src : 0u);
       }
 
@@ -410,8 +412,7 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
   }
 
   // Per-head sums over the four lane groups.
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  l_run = group4_sum(l_run);
   // Fold each head's lo row (G + h) into its hi row (h): afterwards O row h = 4*q4 + j, h < G.
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {

@@ -63,6 +63,30 @@ __device__ __forceinline__ void store_from_float(void* base, int64_t i, float x)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Reductions over the four 16-lane groups of a wave (lanes n, n + 16, n + 32, n + 48), every
+// lane receiving the result.  gfx950's v_permlane16_swap / v_permlane32_swap exchange 16-lane
+// rows (lane i <-> i ^ 16) and 32-lane halves (i <-> i ^ 32) inside the VALU, instead of a
+// round trip through the LDS crossbar (ds_bpermute).  Each step combines the same two values
+// in the same order as x op shfl_xor(x, 16 or 32), so results are bit-identical to that form.
+__device__ __forceinline__ float swap16_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float swap16_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float swap32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float group4_max(float x) { return swap32_max(swap16_max(x)); }
+__device__ __forceinline__ float group4_sum(float x) { return swap32_sum(swap16_sum(x)); }
+
 // K tile order.  A (block, head) K tile holds 16 tokens x head_dim elements as 16-byte chunks;
 // chunk c of token t (elements [c*E, c*E + E) of that token's head vector, E = 16 / elem_size)
 // sits at chunk index

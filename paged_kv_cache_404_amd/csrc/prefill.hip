@@ -249,8 +249,7 @@ __global__ void __launch_bounds__(PrefillShape<G>::NWAVES * 64) prefill_mfma_ker
         float bmax = sc[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sc[i]);
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-        bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
+        bmax = group4_max(bmax);
         bmax *= c;
 
         const bool need = row_ok && (bmax > m_run[h] + kLazyRescaleLog2);
@@ -312,9 +311,7 @@ __global__ void __launch_bounds__(PrefillShape<G>::NWAVES * 64) prefill_mfma_ker
   __shared__ float sL[KSPLIT][G][16];
 #pragma unroll
   for (int h = 0; h < HPW; ++h) {
-    float l = l_run[h];
-    l += __shfl_xor(l, 16);
-    l += __shfl_xor(l, 32);
+    const float l = group4_sum(l_run[h]);
     const int hg = hs * HPW + h;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
