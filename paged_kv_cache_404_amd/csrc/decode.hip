@@ -68,24 +68,6 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// Float -> 16-bit pattern of the MFMA input type (round to nearest even) and back.
-template <int DT>
-__device__ __forceinline__ uint32_t to16(float x) {
-  if constexpr (DT == PKV_BF16) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-  } else {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-  }
-}
-template <int DT>
-__device__ __forceinline__ float from16(uint32_t b) {
-  if constexpr (DT == PKV_BF16) {
-    return bf16_bits_to_float(b);
-  } else {
-    return f16_bits_to_float(b);
-  }
-}
-
 template <int DT>
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   if constexpr (DT == PKV_BF16) {
@@ -355,15 +337,12 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
       }
       l_run += psum;
 
+      // hi = the weights rounded to 16 bits, lo = the rounding residuals rounded to 16 bits.
       u32x4 hi, lo;
 #pragma unroll
       for (int wd = 0; wd < 4; ++wd) {
-        const uint32_t h0 = to16<DT>(pv[2 * wd]);
-        const uint32_t h1 = to16<DT>(pv[2 * wd + 1]);
-        const uint32_t l0 = to16<DT>(pv[2 * wd] - from16<DT>(h0));
-        const uint32_t l1 = to16<DT>(pv[2 * wd + 1] - from16<DT>(h1));
-        hi[wd] = h0 | (h1 << 16);
-        lo[wd] = l0 | (l1 << 16);
+        hi[wd] = pack2<DT>(pv[2 * wd], pv[2 * wd + 1]);
+        lo[wd] = pack2<DT>(pv[2 * wd] - low_half<DT>(hi[wd]), pv[2 * wd + 1] - high_half<DT>(hi[wd]));
       }
       // Lo rows G..2G-1 take the lo parts of heads 0..G-1: a row shift by G inside each 16-lane
       // row (DPP row_shr), valid for the lanes that use it (n16 >= G).

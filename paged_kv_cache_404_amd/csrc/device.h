@@ -14,6 +14,9 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 constexpr int kBlock = 16;  // tokens per physical block (the kernels' only block size)
@@ -62,6 +65,35 @@ __device__ __forceinline__ void store_from_float(void* base, int64_t i, float x)
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Two floats -> two 16-bit elements of the matrix-core input type in one 32-bit word (low half =
+// a), round to nearest even: one v_cvt_pk_{bf16,f16}_f32.
+template <int DT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  const f32x2 x = {a, b};
+  if constexpr (DT == PKV_BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, f16x2));
+  }
+}
+// The low / high 16-bit element of a packed word, widened exactly to float.
+template <int DT>
+__device__ __forceinline__ float low_half(uint32_t w) {
+  if constexpr (DT == PKV_BF16) {
+    return __builtin_bit_cast(float, w << 16);
+  } else {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
+  }
+}
+template <int DT>
+__device__ __forceinline__ float high_half(uint32_t w) {
+  if constexpr (DT == PKV_BF16) {
+    return __builtin_bit_cast(float, w & 0xFFFF0000u);
+  } else {
+    return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+  }
+}
 
 // Reductions over the four 16-lane groups of a wave (lanes n, n + 16, n + 32, n + 48), every
 // lane receiving the result.  gfx950's v_permlane16_swap / v_permlane32_swap exchange 16-lane

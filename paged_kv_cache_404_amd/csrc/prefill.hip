@@ -42,22 +42,6 @@ struct PrefillArgs {
 };
 
 template <int DT>
-__device__ __forceinline__ uint32_t to16(float x) {
-  if constexpr (DT == PKV_BF16) {
-    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
-  } else {
-    return __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
-  }
-}
-template <int DT>
-__device__ __forceinline__ float from16(uint32_t b) {
-  if constexpr (DT == PKV_BF16) {
-    return bf16_bits_to_float(b);
-  } else {
-    return f16_bits_to_float(b);
-  }
-}
-template <int DT>
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   if constexpr (DT == PKV_BF16) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -276,13 +260,12 @@ __global__ void __launch_bounds__(PrefillShape<G>::NWAVES * 64) prefill_mfma_ker
           psum += pv[i];
         }
         l_run[h] += psum;
+        // hi = the weights rounded to 16 bits, lo = the rounding residuals rounded to 16 bits.
         u32x4 hi, lo;
 #pragma unroll
         for (int wd = 0; wd < 4; ++wd) {
-          const uint32_t h0 = to16<DT>(pv[2 * wd]);
-          const uint32_t h1 = to16<DT>(pv[2 * wd + 1]);
-          hi[wd] = h0 | (h1 << 16);
-          lo[wd] = to16<DT>(pv[2 * wd] - from16<DT>(h0)) | (to16<DT>(pv[2 * wd + 1] - from16<DT>(h1)) << 16);
+          hi[wd] = pack2<DT>(pv[2 * wd], pv[2 * wd + 1]);
+          lo[wd] = pack2<DT>(pv[2 * wd] - low_half<DT>(hi[wd]), pv[2 * wd + 1] - high_half<DT>(hi[wd]));
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
