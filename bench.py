@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attn: effective KV HBM GB/s (% of peak); seqs*steps/s"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partitions_traffic.json")
 
 
@@ -44,6 +45,8 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB of caches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the chunked-prefill and long-context measurements reported beside the main line")
     ap.add_argument("--separate", action="store_true",
                     help="time paged_cache_append + paged_attention_decode as two calls instead of the fused "
                          "paged_attention_decode_append")
@@ -111,6 +114,142 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
         json.dump(rec, f, indent=1)
         f.write("\n")
     return rec[workload]
+
+
+def _events_avg_us(torch, stream, fn, n):
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def measure_prefill(args, dev):
+    """paged_attention_prefill_chunk on the mixed step's chunk: 512 rows at positions 4096..4607
+    of one sequence (32 q / 8 kv heads of 128, bf16), causal against the paged cache.  Work:
+    4 * head_dim flops per visible (row, key) pair and query head."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_404_amd import BlockPool, ops
+
+    w = wl.mixed_step(5)
+    ctx, C, Hq, Hkv, D = w.ctx_start, w.chunk, w.Hq, w.Hkv, w.D
+    pool = BlockPool(w.num_blocks, 16, w.free_order)
+    s = pool.new_seq()
+    pool.append(s, ctx + C)
+    table, _ = pool.block_tables([s], wl.blocks_for(ctx + C))
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    k = torch.randn((w.num_blocks, Hkv, 16, D), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((w.num_blocks, Hkv, D, 16), generator=g, device=dev).to(torch.bfloat16)
+    q = torch.randn((C, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((C, Hq, D), dtype=torch.float32, device=dev)
+    tb = torch.from_numpy(table[0]).to(dev)
+    fn = lambda i: ops.paged_attention_prefill_chunk(out, q, k, v, tb, ctx, w.scale)  # noqa: E731
+    for i in range(5):
+        fn(i)
+    us = _events_avg_us(torch, torch.cuda.current_stream(), fn, max(20, args.steps // 4))
+    pairs = sum(ctx + i + 1 for i in range(C))
+    flops = pairs * Hq * 4 * D
+    tflops = flops / (us * 1e-6) / 1e12
+    res = {
+        "workload": f"prefill_chunk_{C}_after_{ctx}_gqa{Hq}x{Hkv}_d{D}_bf16",
+        "us_per_call": round(us, 3),
+        "flops_per_call": flops,
+        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": round(tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_prefill(ctx, Hq, Hkv, D, w.scale, args.cpu_seconds / 2)
+    return res
+
+
+def cpu_baseline_prefill(ctx, Hq, Hkv, D, scale, seconds):
+    """The oracle's prefill (numpy fp64) on the first R rows of the same chunk shape, R grown
+    until the sample takes about `seconds`."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import workloads as wl
+    from oracle import CacheModel, PoolModel
+    from oracle import attention as oatt
+
+    rng = np.random.default_rng(1005)
+    R = 4
+    while True:
+        N = wl.blocks_for(ctx + R) + 1
+        pool = PoolModel(N, 16, rng.permutation(N))
+        sq = pool.new_seq()
+        slots, _ = pool.append(sq, ctx + R)
+        cache = CacheModel(N, Hkv, D, "bf16", fill_nan=True)
+        cache.append(wl.normal_bits(rng, (ctx + R, Hkv, D), "bf16"), wl.normal_bits(rng, (ctx + R, Hkv, D), "bf16"),
+                     slots)
+        q = wl.normal_bits(rng, (R, Hq, D), "bf16")
+        table, _ = pool.block_tables([sq], len(pool.tables[sq]))
+        t0 = time.perf_counter()
+        oatt.prefill_chunk(q, cache, table[0], ctx, scale)
+        el = time.perf_counter() - t0
+        if el >= seconds or R >= 512:
+            break
+        R = min(512, max(R * 2, int(R * seconds / max(el, 1e-3))))
+    flops = sum(ctx + i + 1 for i in range(R)) * Hq * 4 * D
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {R} of 512 chunk rows after {ctx} cached tokens, numpy fp64, {el:.1f} s"}
+
+
+def measure_long(args, dev):
+    """The long-context decode: batch 8 at 32,768 tokens (2,048 scattered blocks each), split-K
+    over 512-token partitions, fused append; KV + Q bytes per step as in the main line."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_404_amd import BlockPool, ops
+
+    w = wl.long_context_decode(4)
+    pool = BlockPool(w.num_blocks, 16, w.free_order)
+    seqs = [pool.new_seq() for _ in range(w.B)]
+    st, _, _, _ = pool.append_many(seqs, [int(L) for L in w.lens])
+    assert st == 0
+    tables, lens = pool.block_tables(seqs, w.max_blocks_per_seq)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    k = torch.randn((w.num_blocks, w.Hkv, 16, w.D), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((w.num_blocks, w.Hkv, w.D, 16), generator=g, device=dev).to(torch.bfloat16)
+    q = torch.randn((w.B, w.Hq, w.D), generator=g, device=dev).to(torch.bfloat16)
+    sk = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev).to(torch.bfloat16)
+    sv = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
+    maxL = int(lens.max())
+    ws = ops.decode_workspace(w.B, w.Hq, w.D, maxL, w.partition_size, device=dev)
+    dec = ops.PreparedDecode(out, q, k, v, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), maxL,
+                             w.scale, w.partition_size, ws, new_key=sk, new_value=sv)
+    for _ in range(3):
+        dec()
+    n = max(10, args.steps // 10)
+    stream = torch.cuda.current_stream()
+    step_us = _events_avg_us(torch, stream, lambda i: dec(), n)
+    part_us = _events_avg_us(torch, stream, lambda i: dec.partitions(), n)
+    nbytes = w.kv_bytes() + w.q_bytes()
+    gbs = nbytes / (part_us * 1e-6) / 1e9
+    return {
+        "workload": w.name,
+        "kv_plus_q_bytes_per_step": nbytes,
+        "us_per_step": round(step_us, 3),
+        "gbs_per_step": round(nbytes / (step_us * 1e-6) / 1e9, 1),
+        "seqs_steps_per_s": round(w.B / (step_us * 1e-6), 1),
+        "kernel_us": {"decode_partitions": round(part_us, 3), "decode_reduce": round(step_us - part_us, 3)},
+        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel (partition pass, fused append)",
+                     "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+    }
 
 
 def cpu_baseline(w, seconds: float):
@@ -327,6 +466,11 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    if not args.no_extra and args.workload == "llama":
+        del reps
+        torch.cuda.empty_cache()
+        res["prefill"] = measure_prefill(args, dev)
+        res["long_context"] = measure_long(args, dev)
     print(json.dumps(res), flush=True)
 
 

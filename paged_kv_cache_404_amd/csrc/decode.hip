@@ -511,10 +511,11 @@ __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Log-sum-exp merge of partitions.  grid = (Hq, B), D threads.  MAXP >= max_parts: every partial
-// of the row is loaded at once, together with the context length (one memory latency); the
-// sequence's own partition count then selects which take part.  Rows of single-partition
-// sequences were written by the partition pass and are left alone.
+// Log-sum-exp merge of partitions.  grid = (Hq, B), 128 threads.  MAXP >= max_parts (up to 64):
+// every partial of the row is loaded at once, together with the context length (one memory
+// latency), (m, l) through LDS; the sequence's own partition count then selects which take
+// part.  Rows of single-partition sequences were written by the partition pass and are left
+// alone.
 // ------------------------------------------------------------------------------------------
 template <int DT_OUT, int MAXP>
 __global__ void __launch_bounds__(128) decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ part_ml,
@@ -524,29 +525,31 @@ __global__ void __launch_bounds__(128) decode_reduce_kernel(void* __restrict__ o
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int d = threadIdx.x;
-  if (d >= D) return;
   const int64_t row0 = (static_cast<int64_t>(b) * Hq + h) * max_parts;
-  float m[MAXP], l[MAXP], o[MAXP];
-#pragma unroll
-  for (int p = 0; p < MAXP; ++p) {
-    const bool in = p < max_parts;
-    m[p] = in ? part_ml[(row0 + p) * 2] : -INFINITY;
-    l[p] = in ? part_ml[(row0 + p) * 2 + 1] : 0.f;
-    o[p] = in ? part_o[(row0 + p) * D + d] : 0.f;
+  __shared__ float sm[MAXP], sl[MAXP];
+  // Thread p fetches partition p's (m, l); every thread fetches its dimension of every partial.
+  if (d < MAXP) {
+    const bool in = d < max_parts;
+    sm[d] = in ? part_ml[(row0 + d) * 2] : -INFINITY;
+    sl[d] = in ? part_ml[(row0 + d) * 2 + 1] : 0.f;
   }
+  float o[MAXP];
+#pragma unroll
+  for (int p = 0; p < MAXP; ++p) o[p] = (p < max_parts && d < D) ? part_o[(row0 + p) * D + d] : 0.f;
   const int L = min(lens[b], max_parts * part_size);
   const int nparts = (L + part_size - 1) / part_size;
-  if (nparts <= 1) return;
+  __syncthreads();
+  if (nparts <= 1 || d >= D) return;
   float M = -INFINITY;
 #pragma unroll
-  for (int p = 0; p < MAXP; ++p) M = p < nparts ? fmaxf(M, m[p]) : M;
+  for (int p = 0; p < MAXP; ++p) M = p < nparts ? fmaxf(M, sm[p]) : M;
   float acc = 0.f, lsum = 0.f;
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) {
     if (p < nparts) {
-      const float f = fast_exp2(m[p] - M);
+      const float f = fast_exp2(sm[p] - M);
       acc += f * o[p];
-      lsum += f * l[p];
+      lsum += f * sl[p];
     }
   }
   store_from_float<DT_OUT>(out, (static_cast<int64_t>(b) * Hq + h) * D + d, acc / lsum);
@@ -699,7 +702,7 @@ int launch_partitions(const DecodeArgs& a, int32_t dtype, int32_t out_dtype, int
 template <int DT_OUT>
 void launch_reduce_t(void* out, const float* ml, const float* po, const int32_t* lens, int B, int Hq, int D,
                      int max_parts, int part_size, hipStream_t s) {
-  const dim3 grid(Hq, B), block(D);
+  const dim3 grid(Hq, B), block(128);
   if (max_parts <= 4)
     hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 4>), grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
                        part_size);
@@ -709,8 +712,14 @@ void launch_reduce_t(void* out, const float* ml, const float* po, const int32_t*
   else if (max_parts <= 16)
     hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 16>), grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
                        part_size);
+  else if (max_parts <= 32)
+    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 32>), grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
+                       part_size);
+  else if (max_parts <= 64)
+    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 64>), grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
+                       part_size);
   else
-    hipLaunchKernelGGL((decode_reduce_loop_kernel<DT_OUT>), grid, block, 0, s, out, ml, po, lens, Hq, D,
+    hipLaunchKernelGGL((decode_reduce_loop_kernel<DT_OUT>), grid, dim3(D), 0, s, out, ml, po, lens, Hq, D,
                        max_parts, part_size);
 }
 
