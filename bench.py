@@ -4,10 +4,13 @@
 A step is one continuous-batching decode step of one attention layer over a batch that is
 already resident in HBM: the cache append of every sequence's new token and paged decode
 attention over all cached tokens.  By default the step is paged_attention_decode_append (the
-append fused into the decode partition kernel, then the log-sum-exp reduce); --separate times
-paged_cache_append followed by paged_attention_decode instead.  Default workload: Llama-3-8B-shaped layer, 32 q / 8 kv heads of 128, bf16, batch 64,
-context lengths ~ U[128, 2048], 16-token blocks scattered through a shuffled pool, split-K over
-512-token partitions.
+append fused into the decode kernel), single pass per (sequence, KV head) with the work handed
+out longest sequence first; --partition-size P > 0 splits the context into P-token partitions
+merged by the log-sum-exp reduce; --separate times paged_cache_append followed by
+paged_attention_decode instead.  Default workload: Llama-3-8B-shaped layer, 32 q / 8 kv heads of 128, bf16, batch 64,
+context lengths ~ U[128, 2048], 16-token blocks scattered through a shuffled pool.  Also reported
+in the same line: the chunked-prefill kernel (512 rows after 4,096 cached tokens) and the
+long-context decode (batch 8 x 32,768 tokens, 512-token partitions).
 
 Metric: effective KV+Q bytes per step / step time (GB/s), with KV = sum_b L_b * Hkv * D * 2 * 2 B
 (each cached token's K and V once per KV head) and Q = B * Hq * D * 2 B; also seqs*steps/s.
@@ -41,10 +44,13 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", choices=["llama", "long"], default="llama")
-    ap.add_argument("--partition-size", type=int, default=512)
+    ap.add_argument("--partition-size", type=int, default=None,
+                    help="0 = single pass; default 0 for the Llama-shaped batch, 512 for the long-context one")
     ap.add_argument("--replicas", type=int, default=0, help="0 = enough for >= 1 GiB of caches")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-order", action="store_true",
+                    help="do not pass the host copy of the context lengths (longest-first work order)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the chunked-prefill and long-context measurements reported beside the main line")
     ap.add_argument("--separate", action="store_true",
@@ -85,9 +91,11 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
-        dec = [float(r["Counter_Value"]) for r in rows if "decode_mfma_kernel" in r["Kernel_Name"]]
-        if not dec:
-            raise SystemExit(f"no decode_mfma_kernel dispatch in {path}")
+        dec_rows = [r for r in rows if "decode_mfma_kernel" in r["Kernel_Name"]]
+        if not dec_rows or len({r["Kernel_Name"] for r in dec_rows}) != 1:
+            raise SystemExit(f"{path}: need dispatches of exactly one decode_mfma_kernel instantiation "
+                             "(run the counter passes with --no-extra)")
+        dec = [float(r["Counter_Value"]) for r in dec_rows]
         return copy, sum(dec) / len(dec), len(dec)
 
     f_copy, f_dec, n_f = per_kernel(fetch_csv, "FETCH_SIZE")
@@ -230,7 +238,8 @@ def measure_long(args, dev):
     maxL = int(lens.max())
     ws = ops.decode_workspace(w.B, w.Hq, w.D, maxL, w.partition_size, device=dev)
     dec = ops.PreparedDecode(out, q, k, v, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev), maxL,
-                             w.scale, w.partition_size, ws, new_key=sk, new_value=sv)
+                             w.scale, w.partition_size, ws, new_key=sk, new_value=sv,
+                             host_context_lens=None if args.no_order else lens)
     for _ in range(3):
         dec()
     n = max(10, args.steps // 10)
@@ -321,9 +330,9 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.workload == "llama":
-        w = wl.llama_decode(2, partition_size=args.partition_size)
+        w = wl.llama_decode(2, partition_size=0 if args.partition_size is None else args.partition_size)
     else:
-        w = wl.long_context_decode(4, partition_size=args.partition_size)
+        w = wl.long_context_decode(4, partition_size=512 if args.partition_size is None else args.partition_size)
 
     # Host pool + builders: the cached prefix, then this step's append (timed on the host).
     pool = BlockPool(w.num_blocks, 16, w.free_order)
@@ -358,7 +367,8 @@ def main():
         reps.append((ops.PreparedAppend(k, v, sk, sv, slots_t),
                      ops.PreparedDecode(out, q, k, v, tables_t, lens_t, maxL, w.scale, w.partition_size, ws,
                                         new_key=None if args.separate else sk,
-                                        new_value=None if args.separate else sv)))
+                                        new_value=None if args.separate else sv,
+                                        host_context_lens=None if args.no_order else lens)))
     torch.cuda.synchronize()
 
     def step(i):
@@ -441,21 +451,24 @@ def main():
             if args.workload == "llama" else f"{int(w.lens[0])} each",
             "num_blocks": w.num_blocks,
             "partition_size": w.partition_size,
+            "work_order": "natural" if args.no_order else "longest first (host copy of the lengths)",
             "replicas": R,
             "parallelism": "none (one GPU)",
         },
         "pct_of_peak_hbm": round(100 * value / PEAK_HBM_GBS, 2),
         "seqs_steps_per_s": round(w.B / (wall / args.steps), 1),
         "kv_plus_q_bytes_per_step": step_bytes,
-        "step": ("paged_cache_append + paged_attention_decode (partitions, reduce)" if args.separate else
-                 "paged_attention_decode_append (fused append + partitions, reduce)"),
+        "step": (("paged_cache_append + paged_attention_decode" if args.separate else
+                  "paged_attention_decode_append (append fused into the decode kernel)") +
+                 (", single pass" if w.partition_size == 0 else
+                  f", {w.partition_size}-token partitions + log-sum-exp reduce")),
         "kernel_us": {"append": round(float(t_app), 3), "decode_partitions": round(part_us, 3),
                       "decode_reduce": round(float(t_red), 3)},
         "host_pool_and_builders_us_per_step": round(host_us, 1),
         "device_copy_probe_gbs": round(copy_gbs, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_mfma_kernel (partition pass" + ("" if args.separate else ", fused append") + ")",
+            "kernel": "decode_mfma_kernel" + ("" if args.separate else " (fused append)"),
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

@@ -136,6 +136,10 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_he
  *                  65535 partitions per sequence (PKV_EUNSUPPORTED beyond).
  *   workspace      device scratch of at least paged_attention_decode_workspace_bytes(...) bytes
  *                  (may be NULL when that is 0); contents on entry do not matter.
+ *   host_context_lens  NULL, or a host copy of context_lens (B <= 512 entries): used only to
+ *                  hand out the work longest sequence first, which shortens the launch's tail.
+ *                  The output does not depend on it (every sequence's arithmetic is the same
+ *                  whatever its position in the order).
  * Accumulation is fp32 whatever the input type.
  */
 int paged_attention_decode(void* out, int32_t out_dtype, const void* query, const void* k_cache,
@@ -143,7 +147,8 @@ int paged_attention_decode(void* out, int32_t out_dtype, const void* query, cons
                            int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
                            int32_t max_context_len, float scale, int32_t partition_size,
-                           void* workspace, size_t workspace_bytes, int32_t dtype, pkv_stream_t stream);
+                           void* workspace, size_t workspace_bytes, int32_t dtype,
+                           const int32_t* host_context_lens, pkv_stream_t stream);
 
 /*
  * paged_attention_decode_partitions / paged_attention_decode_reduce - the two launches of
@@ -159,7 +164,8 @@ int paged_attention_decode_partitions(void* out, int32_t out_dtype, const void* 
                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                       int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
                                       float scale, int32_t partition_size, void* workspace,
-                                      size_t workspace_bytes, int32_t dtype, pkv_stream_t stream);
+                                      size_t workspace_bytes, int32_t dtype,
+                                      const int32_t* host_context_lens, pkv_stream_t stream);
 int paged_attention_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, int32_t B,
                                   int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
                                   int32_t partition_size, const void* workspace, size_t workspace_bytes,
@@ -185,7 +191,8 @@ int paged_attention_decode_append(void* out, int32_t out_dtype, const void* quer
                                   const int32_t* context_lens, int32_t B, int32_t num_q_heads, int32_t num_kv_heads,
                                   int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq,
                                   int32_t num_blocks, int32_t max_context_len, float scale, int32_t partition_size,
-                                  void* workspace, size_t workspace_bytes, int32_t dtype, pkv_stream_t stream);
+                                  void* workspace, size_t workspace_bytes, int32_t dtype,
+                                  const int32_t* host_context_lens, pkv_stream_t stream);
 /* Its partition launch alone (then paged_attention_decode_reduce), as for paged_attention_decode. */
 int paged_attention_decode_append_partitions(void* out, int32_t out_dtype, const void* query, const void* new_key,
                                              const void* new_value, void* k_cache, void* v_cache,
@@ -194,7 +201,7 @@ int paged_attention_decode_append_partitions(void* out, int32_t out_dtype, const
                                              int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
                                              int32_t max_context_len, float scale, int32_t partition_size,
                                              void* workspace, size_t workspace_bytes, int32_t dtype,
-                                             pkv_stream_t stream);
+                                             const int32_t* host_context_lens, pkv_stream_t stream);
 
 /*
  * paged_attention_prefill_chunk - causal attention of one prompt chunk against the paged cache.

@@ -53,15 +53,15 @@ _SIGS = {
     "paged_cache_copy_blocks": (C.c_int, [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _vp]),
     "paged_attention_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "paged_attention_decode": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
-                                         _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp]),
+                                         _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp]),
     "paged_attention_decode_partitions": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
-                                                    _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp]),
+                                                    _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp]),
     "paged_attention_decode_reduce": (C.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "paged_attention_decode_append": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
-                                                _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp]),
+                                                _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp]),
     "paged_attention_decode_append_partitions": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                            _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
-                                                           _i32, _vp]),
+                                                           _i32, _vp, _vp]),
     "paged_attention_prefill_chunk": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                                 _i32, _f32, _i32, _vp]),
     "pkv_pool_create": (C.c_int, [_i32, _i32, _pi32, C.POINTER(_pool_p)]),

@@ -24,6 +24,7 @@
 // MFMA, so P.V keeps ~16 mantissa bits at no extra matrix instruction.  Scores use exp2 with
 // log2(e) folded into the scale; the running maximum is only raised when a score exceeds it by
 // more than 2^8 (lazy rescaling: exact, and p stays <= 256), which makes rescaling rare.
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -34,6 +35,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRescaleLog2 = 8.0f;
+
+// Sequences a longest-first work order can name (it travels in the kernel arguments).
+constexpr int kMaxOrder = 512;
 
 struct DecodeArgs {
   void* out;
@@ -55,6 +59,8 @@ struct DecodeArgs {
   const void* new_v;
   void* k_out;        // fused append: the caches, written at that token's slot
   void* v_out;
+  int32_t num_order;  // 0, or B: workgroup row y works on sequence order[y]
+  int32_t order[kMaxOrder];
 };
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -130,9 +136,11 @@ __device__ __forceinline__ void emit(const DecodeArgs& a, int b, int hq, int p, 
 // NEWTOK (fused append): the token at position L - 1 is this step's new token and its K/V come
 // from the input rows new_k / new_v instead of the cache.  It lies in the sequence's last
 // partition, in the last 32-token step of that partition; the wave that owns that step loads
-// the new K/V straight into the operand layout, substitutes them for the cache slot's (stale)
-// contents in its registers, and stores them into the slot (block table[(L - 1) / 16], offset
-// (L - 1) % 16).  No other workgroup reads that slot in the same launch.
+// the new K/V straight into the operand layout and substitutes them for the cache slot's (stale)
+// contents in its registers; it then stores the whole K and V tiles of that block (block
+// table[(L - 1) / 16]) back, the new token at offset (L - 1) % 16 and every other slot with the
+// bytes it was loaded with, so each cache line is written whole.  No other workgroup reads or
+// writes that block (the last block of a sequence is private to it) in the same launch.
 template <int DT, int DT_OUT, int D, int G, int NW, bool NEWTOK>
 __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
   static_assert(D == 64 || D == 128, "head_dim");
@@ -143,7 +151,7 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
   constexpr int kTableSteps = 32;   // steps covered by one block-id load (64 blocks, one per lane)
 
   const int g = blockIdx.x;
-  const int b = blockIdx.y;
+  const int b = a.num_order ? a.order[blockIdx.y] : static_cast<int>(blockIdx.y);
   const int p = blockIdx.z;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -287,6 +295,26 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
             }
           }
         }
+        // The registers now hold the new token's whole block (K and V tiles, the other slots
+        // as loaded): store both tiles back with the load's own lane pattern, so every cache
+        // line is written whole.  Done before the tail of V is zeroed below.
+        int64_t tA, tB;
+        tiles(s, tA, tB);
+        const bool in_b = (nu >> 4) != 0;
+        const int64_t tile = in_b ? tB : tA;
+        if (k_from_b == in_b) {
+          uint16_t* kp = static_cast<uint16_t*>(a.k_out) + tile + k_in_tile;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            *reinterpret_cast<u32x4*>(kp + (2 * ks) * 256) = kf[ks];
+            *reinterpret_cast<u32x4*>(kp + (2 * ks + 1) * 256) = kf[KS + ks];
+          }
+        }
+        if (v_from_b == in_b) {
+          uint16_t* vp = static_cast<uint16_t*>(a.v_out) + tile + v_in_tile;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<u32x4*>(vp + nb * 16 * kBlock) = vf[nb];
+        }
       }
       f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -375,21 +403,6 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
     step(st, false);
   }
 
-  if (owner) {
-    // Store the new token into its slot.
-    const int blk = clamp_blk(a, table[(L - 1) >> 4]);
-    uint16_t* kt = static_cast<uint16_t*>(a.k_out) + (static_cast<int64_t>(blk) * a.Hkv + g) * TILE;
-    uint16_t* vt = static_cast<uint16_t*>(a.v_out) + (static_cast<int64_t>(blk) * a.Hkv + g) * TILE;
-    if (n16 == nk_lane) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) *reinterpret_cast<u32x4*>(kt + k_chunk_pos(ntt, 4 * ks + q4) * 8) = nk[ks];
-    }
-    if (q4 == nv_q4) {
-#pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vt[(nb * 16 + n16) * kBlock + ntt] = static_cast<uint16_t>(nv[nb]);
-    }
-  }
-
   // Per-head sums over the four lane groups.
   l_run = group4_sum(l_run);
   // Fold each head's lo row (G + h) into its hi row (h): afterwards O row h = 4*q4 + j, h < G.
@@ -447,7 +460,7 @@ template <int DT, int DT_OUT, int D>
 __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
   constexpr int E = DT == PKV_F32 ? 4 : 8;  // elements per 16-byte chunk of the K tile
   const int hq = blockIdx.x;
-  const int b = blockIdx.y;
+  const int b = a.num_order ? a.order[blockIdx.y] : static_cast<int>(blockIdx.y);
   const int p = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int g = hq / G;
@@ -753,7 +766,7 @@ int partitions_impl(const char* fn, void* out, int32_t out_dtype, const void* qu
                     int32_t Hq, int32_t Hkv, int32_t D, int32_t bs, int32_t max_blocks, int32_t num_blocks,
                     int32_t max_ctx, float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
                     int32_t dtype, const void* new_k, const void* new_v, void* k_out, void* v_out,
-                    pkv_stream_t stream) {
+                    const int32_t* host_lens, pkv_stream_t stream) {
   int st = validate(fn, out, out_dtype, query, k_cache, v_cache, block_tables, context_lens, B, Hq, Hkv, D, bs,
                     max_blocks, num_blocks, max_ctx, partition_size, workspace, workspace_bytes, dtype);
   if (st != PKV_OK || B == 0 || max_ctx == 0) return st;
@@ -784,6 +797,12 @@ int partitions_impl(const char* fn, void* out, int32_t out_dtype, const void* qu
   a.new_v = new_v;
   a.k_out = k_out;
   a.v_out = v_out;
+  if (host_lens != nullptr && B <= kMaxOrder) {
+    // Longest sequences first (ties by index): the scheduling order only, never the arithmetic.
+    for (int i = 0; i < B; ++i) a.order[i] = i;
+    std::stable_sort(a.order, a.order + B, [&](int32_t x, int32_t y) { return host_lens[x] > host_lens[y]; });
+    a.num_order = B;
+  }
   launch_partitions(a, dtype, out_dtype, D, B, as_stream(stream));
   return check_launch(fn);
 }
@@ -798,11 +817,11 @@ extern "C" int paged_attention_decode_partitions(void* out, int32_t out_dtype, c
                                                  int32_t max_blocks_per_seq, int32_t num_blocks,
                                                  int32_t max_context_len, float scale, int32_t partition_size,
                                                  void* workspace, size_t workspace_bytes, int32_t dtype,
-                                                 pkv_stream_t stream) {
+                                                 const int32_t* host_context_lens, pkv_stream_t stream) {
   return partitions_impl("paged_attention_decode_partitions", out, out_dtype, query, k_cache, v_cache, block_tables,
                          context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                          num_blocks, max_context_len, scale, partition_size, workspace, workspace_bytes, dtype,
-                         nullptr, nullptr, nullptr, nullptr, stream);
+                         nullptr, nullptr, nullptr, nullptr, host_context_lens, stream);
 }
 
 extern "C" int paged_attention_decode_append_partitions(
@@ -810,11 +829,11 @@ extern "C" int paged_attention_decode_append_partitions(
     void* v_cache, const int32_t* block_tables, const int32_t* context_lens, int32_t B, int32_t num_q_heads,
     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
     int32_t max_context_len, float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
-    int32_t dtype, pkv_stream_t stream) {
+    int32_t dtype, const int32_t* host_context_lens, pkv_stream_t stream) {
   return partitions_impl("paged_attention_decode_append_partitions", out, out_dtype, query, k_cache, v_cache,
                          block_tables, context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size,
                          max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size, workspace,
-                         workspace_bytes, dtype, new_key, new_value, k_cache, v_cache, stream);
+                         workspace_bytes, dtype, new_key, new_value, k_cache, v_cache, host_context_lens, stream);
 }
 
 extern "C" int paged_attention_decode_reduce(void* out, int32_t out_dtype, const int32_t* context_lens, int32_t B,
@@ -844,11 +863,12 @@ extern "C" int paged_attention_decode(void* out, int32_t out_dtype, const void* 
                                       int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                       int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
                                       int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
-                                      size_t workspace_bytes, int32_t dtype, pkv_stream_t stream) {
+                                      size_t workspace_bytes, int32_t dtype, const int32_t* host_context_lens,
+                                      pkv_stream_t stream) {
   int st = paged_attention_decode_partitions(out, out_dtype, query, k_cache, v_cache, block_tables, context_lens, B,
                                              num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq,
                                              num_blocks, max_context_len, scale, partition_size, workspace,
-                                             workspace_bytes, dtype, stream);
+                                             workspace_bytes, dtype, host_context_lens, stream);
   if (st != PKV_OK) return st;
   return paged_attention_decode_reduce(out, out_dtype, context_lens, B, num_q_heads, head_dim, max_context_len,
                                        partition_size, workspace, workspace_bytes, stream);
@@ -861,12 +881,12 @@ extern "C" int paged_attention_decode_append(void* out, int32_t out_dtype, const
                                              int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
                                              int32_t max_context_len, float scale, int32_t partition_size,
                                              void* workspace, size_t workspace_bytes, int32_t dtype,
-                                             pkv_stream_t stream) {
+                                             const int32_t* host_context_lens, pkv_stream_t stream) {
   int st = paged_attention_decode_append_partitions(out, out_dtype, query, new_key, new_value, k_cache, v_cache,
                                                     block_tables, context_lens, B, num_q_heads, num_kv_heads,
                                                     head_dim, block_size, max_blocks_per_seq, num_blocks,
                                                     max_context_len, scale, partition_size, workspace,
-                                                    workspace_bytes, dtype, stream);
+                                                    workspace_bytes, dtype, host_context_lens, stream);
   if (st != PKV_OK) return st;
   return paged_attention_decode_reduce(out, out_dtype, context_lens, B, num_q_heads, head_dim, max_context_len,
                                        partition_size, workspace, workspace_bytes, stream);

@@ -5,6 +5,7 @@ contiguity, then pass raw pointers and the current HIP stream to the C ABI.
 """
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 from ._lib import PKV_BF16, PKV_F16, PKV_F32, check, lib
@@ -67,8 +68,15 @@ def decode_workspace(B: int, Hq: int, D: int, max_context_len: int, partition_si
     return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
 
 
+def _host_lens_ptr(host_context_lens):
+    if host_context_lens is None:
+        return None, None
+    hl = np.ascontiguousarray(np.asarray(host_context_lens, dtype=np.int32))
+    return hl, hl.ctypes.data
+
+
 def _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale, partition_size,
-                 workspace):
+                 workspace, host_ptr=None):
     _dev(out, query, k_cache, v_cache, block_tables, context_lens)
     B, Hq, D = query.shape
     N, Hkv, bs, Dk = k_cache.shape
@@ -85,13 +93,16 @@ def _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_c
     ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
     return (out.data_ptr(), dtype_code(out.dtype), query.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
             block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D, bs, block_tables.shape[1], N,
-            int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes, dtype_code(k_cache.dtype))
+            int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes, dtype_code(k_cache.dtype),
+            host_ptr)
 
 
 def paged_attention_decode(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                           partition_size=0, workspace=None, stream=None) -> None:
+                           partition_size=0, workspace=None, stream=None, host_context_lens=None) -> None:
+    """host_context_lens: optional host copy of context_lens, used only to order the work."""
+    hl, hp = _host_lens_ptr(host_context_lens)
     args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                        partition_size, workspace)
+                        partition_size, workspace, hp)
     check(lib.paged_attention_decode(*args, _stream(stream)))
 
 
@@ -100,17 +111,19 @@ def _fused_args(args, new_key, new_value):
     _dev(new_key, new_value)
     B, Hkv, D = args[7], args[9], args[10]
     for t in (new_key, new_value):
-        if tuple(t.shape) != (B, Hkv, D) or dtype_code(t.dtype) != args[-1]:
+        if tuple(t.shape) != (B, Hkv, D) or dtype_code(t.dtype) != args[19]:
             raise ValueError("new_key/new_value must be [B][Hkv][D] of the cache dtype")
     return args[:3] + (new_key.data_ptr(), new_value.data_ptr()) + args[3:]
 
 
 def paged_attention_decode_append(out, query, new_key, new_value, k_cache, v_cache, block_tables, context_lens,
-                                  max_context_len, scale, partition_size=0, workspace=None, stream=None) -> None:
+                                  max_context_len, scale, partition_size=0, workspace=None, stream=None,
+                                  host_context_lens=None) -> None:
     """One decode step with the append fused in: token context_lens[b] - 1 of every sequence
     (new_key/new_value [B][Hkv][D]) is written to its slot and attended over."""
+    hl, hp = _host_lens_ptr(host_context_lens)
     args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                        partition_size, workspace)
+                        partition_size, workspace, hp)
     check(lib.paged_attention_decode_append(*_fused_args(args, new_key, new_value), _stream(stream)))
 
 
@@ -151,10 +164,12 @@ class PreparedDecode:
     C-ABI call (the tensors must stay alive and unchanged in shape)."""
 
     def __init__(self, out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                 partition_size=0, workspace=None, stream=None, new_key=None, new_value=None):
-        self._keep = (out, query, k_cache, v_cache, block_tables, context_lens, workspace, new_key, new_value)
+                 partition_size=0, workspace=None, stream=None, new_key=None, new_value=None,
+                 host_context_lens=None):
+        hl, hp = _host_lens_ptr(host_context_lens)
+        self._keep = (out, query, k_cache, v_cache, block_tables, context_lens, workspace, new_key, new_value, hl)
         self.args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
-                                 partition_size, workspace)
+                                 partition_size, workspace, hp)
         self.fused_args = None if new_key is None else _fused_args(self.args, new_key, new_value)
         self.stream = _stream(stream)
         B, Hq, D = query.shape

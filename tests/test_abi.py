@@ -61,7 +61,7 @@ def _decode(**kw):
     return pkv.lib.paged_attention_decode(args["out"], args["out_dtype"], args["query"], args["k"], args["v"],
                                           args["tables"], args["lens"], args["B"], args["Hq"], args["Hkv"], args["D"],
                                           args["bs"], args["max_blocks"], args["N"], args["max_ctx"], args["scale"],
-                                          args["ps"], args["ws"], args["ws_bytes"], args["dtype"], NULL)
+                                          args["ps"], args["ws"], args["ws_bytes"], args["dtype"], NULL, NULL)
 
 
 @pytest.mark.parametrize("kw,status", [

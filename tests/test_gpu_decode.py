@@ -184,3 +184,24 @@ def test_copy_on_write_shared_prefix_decode():
     ref = oatt.paged_decode(q, m.cache, tables, lens, mw.scale)
     out, _, _ = run_decode(m, samples, q, mw.Hq, mw.scale, 512)
     _check(out, ref)
+
+
+@pytest.mark.parametrize("ps", [0, 512])
+def test_longest_first_order_is_bitwise_invariant(ps):
+    """host_context_lens only orders the work: the output bits are the same with or without it."""
+    w = wl.custom_decode(91, [300, 17, 2048, 1, 900, 513, 64, 1500], 32, 8, 128, "bf16", partition_size=ps)
+    t = wl.decode_tensors(w)
+    m, seqs = build_decode(w, t)
+    tables, lens = m.tables(seqs)
+    q = to_dev(t.q, "bf16")
+    mcl = int(lens.max())
+    outs = []
+    for hl in (None, lens):
+        out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
+        ops.paged_attention_decode(out, q, m.k, m.v, i32(tables), i32(lens), mcl, w.scale, ps,
+                                   ops.decode_workspace(w.B, w.Hq, w.D, mcl, ps), host_context_lens=hl)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    ref = oatt.paged_decode(t.q, m.cache, tables, lens, w.scale)
+    _check(outs[1], ref)
