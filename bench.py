@@ -7,7 +7,8 @@ attention over all cached tokens.  By default the step is paged_attention_decode
 append fused into the decode kernel), single pass per (sequence, KV head) with the work handed
 out longest sequence first; --partition-size P > 0 splits the context into P-token partitions
 merged by the log-sum-exp reduce; --separate times paged_cache_append followed by
-paged_attention_decode instead.  Default workload: Llama-3-8B-shaped layer, 32 q / 8 kv heads of 128, bf16, batch 64,
+paged_attention_decode instead, and --overlap paged_attention_decode_newest with the append on a
+second stream.  Default workload: Llama-3-8B-shaped layer, 32 q / 8 kv heads of 128, bf16, batch 64,
 context lengths ~ U[128, 2048], 16-token blocks scattered through a shuffled pool.  Also reported
 in the same line: the chunked-prefill kernel (512 rows after 4,096 cached tokens) and the
 long-context decode (batch 8 x 32,768 tokens, 512-token partitions).
@@ -17,7 +18,8 @@ Metric: effective KV+Q bytes per step / step time (GB/s), with KV = sum_b L_b * 
 Inputs rotate over R replicas of the caches (>= 1 GiB in total) so that the 256 MB last-level
 cache cannot serve repeated reads.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload llama|long] [--separate]
+    python bench.py [--gpus 1] [--steps 200] [--warmup 20] [--workload llama|long]
+                    [--separate | --overlap]
 """
 from __future__ import annotations
 
@@ -53,7 +55,11 @@ def parse():
                     help="do not pass the host copy of the context lengths (longest-first work order)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the chunked-prefill and long-context measurements reported beside the main line")
-    ap.add_argument("--separate", action="store_true",
+    mode = ap.add_mutually_exclusive_group()
+    mode.add_argument("--overlap", action="store_true",
+                    help="time paged_attention_decode_newest with paged_cache_append on a second stream, each "
+                         "step's decode waiting for the previous step's append")
+    mode.add_argument("--separate", action="store_true",
                     help="time paged_cache_append + paged_attention_decode as two calls instead of the fused "
                          "paged_attention_decode_append")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -355,6 +361,7 @@ def main():
     lens_t = torch.from_numpy(lens).to(dev)
     slots_t = torch.from_numpy(step_slots).to(dev)
     maxL = int(lens.max())
+    side = torch.cuda.Stream(device=dev) if args.overlap else None
     reps = []
     for r in range(R):
         k = torch.randn((w.num_blocks, w.Hkv, 16, w.D), generator=g, device=dev, dtype=torch.float32).to(tdt)
@@ -364,17 +371,28 @@ def main():
         sv = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev, dtype=torch.float32).to(tdt)
         out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
         ws = ops.decode_workspace(w.B, w.Hq, w.D, maxL, w.partition_size, device=dev)
-        reps.append((ops.PreparedAppend(k, v, sk, sv, slots_t),
+        reps.append((ops.PreparedAppend(k, v, sk, sv, slots_t, stream=side),
                      ops.PreparedDecode(out, q, k, v, tables_t, lens_t, maxL, w.scale, w.partition_size, ws,
                                         new_key=None if args.separate else sk,
                                         new_value=None if args.separate else sv,
-                                        host_context_lens=None if args.no_order else lens)))
+                                        host_context_lens=None if args.no_order else lens,
+                                        write_cache=not args.overlap)))
     torch.cuda.synchronize()
+    main_stream = torch.cuda.current_stream()
 
     def step(i):
         app, dec = reps[i % R]
         if args.separate:
             app()
+        elif args.overlap:
+            # The append may run beside this step's decode (which takes the new tokens from the
+            # input rows); the next step's decode reads them from the cache, so it waits for it.
+            side.wait_stream(main_stream)
+            app()
+            dec.partitions()
+            dec.reduce()
+            main_stream.wait_stream(side)
+            return
         dec.partitions()
         dec.reduce()
 
@@ -402,7 +420,10 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) * 1e3 / args.steps
 
-    t_app = avg_us(lambda i: reps[i % R][0]()) if args.separate else 0.0
+    if args.overlap:
+        # Kernel durations alone, both on the main stream.
+        reps = [(ops.PreparedAppend(*a._keep), d) for a, d in reps]
+    t_app = avg_us(lambda i: reps[i % R][0]()) if args.separate or args.overlap else 0.0
     t_part = avg_us(lambda i: reps[i % R][1].partitions())
     t_red = avg_us(lambda i: reps[i % R][1].reduce())
 
@@ -459,6 +480,7 @@ def main():
         "seqs_steps_per_s": round(w.B / (wall / args.steps), 1),
         "kv_plus_q_bytes_per_step": step_bytes,
         "step": (("paged_cache_append + paged_attention_decode" if args.separate else
+                  "paged_attention_decode_newest with paged_cache_append on a second stream" if args.overlap else
                   "paged_attention_decode_append (append fused into the decode kernel)") +
                  (", single pass" if w.partition_size == 0 else
                   f", {w.partition_size}-token partitions + log-sum-exp reduce")),
@@ -468,7 +490,8 @@ def main():
         "device_copy_probe_gbs": round(copy_gbs, 1),
         "roofline": {
             "bound": "hbm",
-            "kernel": "decode_mfma_kernel" + ("" if args.separate else " (fused append)"),
+            "kernel": "decode_mfma_kernel" + ("" if args.separate else " (new tokens from the input rows)"
+                                              if args.overlap else " (fused append)"),
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",

@@ -204,6 +204,31 @@ int paged_attention_decode_append_partitions(void* out, int32_t out_dtype, const
                                              const int32_t* host_context_lens, pkv_stream_t stream);
 
 /*
+ * paged_attention_decode_newest - decode attention in which every sequence's newest token
+ * (position context_lens[b] - 1) is taken from new_key / new_value instead of the cache, and the
+ * cache is not written.  The caller stores those tokens with paged_cache_append, before, after,
+ * or concurrently on another stream: this call never depends on the bytes of those slots, so the
+ * append can overlap the attention.  Output bit for bit that of paged_attention_decode_append.
+ * Arguments as paged_attention_decode_append (k_cache, v_cache read only).  bf16 / fp16 only.
+ */
+int paged_attention_decode_newest(void* out, int32_t out_dtype, const void* query, const void* new_key,
+                                  const void* new_value, const void* k_cache, const void* v_cache,
+                                  const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                  int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len,
+                                  float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+                                  int32_t dtype, const int32_t* host_context_lens, pkv_stream_t stream);
+/* Its partition launch alone (then paged_attention_decode_reduce). */
+int paged_attention_decode_newest_partitions(void* out, int32_t out_dtype, const void* query, const void* new_key,
+                                             const void* new_value, const void* k_cache, const void* v_cache,
+                                             const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                             int32_t max_context_len, float scale, int32_t partition_size,
+                                             void* workspace, size_t workspace_bytes, int32_t dtype,
+                                             const int32_t* host_context_lens, pkv_stream_t stream);
+
+/*
  * paged_attention_prefill_chunk - causal attention of one prompt chunk against the paged cache.
  * [Chapter] "How the scheduler works" and [Notes] "Prefill gets in the way": a long prompt is
  * prefilled in chunks that fit a per-step token budget.  Row i of the chunk sits at absolute

@@ -62,6 +62,11 @@ _SIGS = {
     "paged_attention_decode_append_partitions": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                            _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                                            _i32, _vp, _vp]),
+    "paged_attention_decode_newest": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp]),
+    "paged_attention_decode_newest_partitions": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                                           _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
+                                                           _i32, _vp, _vp]),
     "paged_attention_prefill_chunk": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                                 _i32, _f32, _i32, _vp]),
     "pkv_pool_create": (C.c_int, [_i32, _i32, _pi32, C.POINTER(_pool_p)]),

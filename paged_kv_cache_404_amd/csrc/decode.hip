@@ -266,14 +266,17 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
     // The empty asm statements keep those loads where they are written.
     auto step = [&](int s, const bool prefetch) {
       const int nvalid = min(32, pend - (pstart + s * 32));
-      if (!prefetch && owner && s == last_st) {
+      const bool new_step = !prefetch && owner && s == last_st;
+      // The new token's block (step block A or B) and its tile offset, for the store-back.
+      const bool in_b = (nu >> 4) != 0;
+      if (new_step) {
         // The new token replaces what its cache slot held before this launch.  The last step of
         // a wave is always the one issued without a successor.  The asm operands keep the
         // compiler from consuming (and so waiting for) the new token's loads before this step.
+        // K is substituted here, V just before the P.V product, so this step still waits for
+        // its V tile no earlier than any other step.
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) asm volatile("" : "+v"(nk[ks]));
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(nv[nb]));
         if (n16 == nk_lane) {
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
@@ -284,36 +287,18 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
             }
           }
         }
-        if (q4 == nv_q4) {
-          const int e = ntt & 7;
-          const uint32_t sh = (e & 1) * 16;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) {
-#pragma unroll
-            for (int wd = 0; wd < 4; ++wd) {
-              if (wd == (e >> 1)) vf[nb][wd] = (vf[nb][wd] & ~(0xFFFFu << sh)) | (nv[nb] << sh);
-            }
-          }
-        }
-        // The registers now hold the new token's whole block (K and V tiles, the other slots
-        // as loaded): store both tiles back with the load's own lane pattern, so every cache
-        // line is written whole.  Done before the tail of V is zeroed below.
-        int64_t tA, tB;
-        tiles(s, tA, tB);
-        const bool in_b = (nu >> 4) != 0;
-        const int64_t tile = in_b ? tB : tA;
-        if (k_from_b == in_b) {
-          uint16_t* kp = static_cast<uint16_t*>(a.k_out) + tile + k_in_tile;
+        // The registers now hold the new token's whole K tile (the other slots as loaded):
+        // store it back with the load's own lane pattern, so every cache line is written whole.
+        // Without k_out the caller writes the cache itself (paged_attention_decode_newest).
+        if (a.k_out != nullptr && k_from_b == in_b) {
+          int64_t tA, tB;
+          tiles(s, tA, tB);
+          uint16_t* kp = static_cast<uint16_t*>(a.k_out) + (in_b ? tB : tA) + k_in_tile;
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             *reinterpret_cast<u32x4*>(kp + (2 * ks) * 256) = kf[ks];
             *reinterpret_cast<u32x4*>(kp + (2 * ks + 1) * 256) = kf[KS + ks];
           }
-        }
-        if (v_from_b == in_b) {
-          uint16_t* vp = static_cast<uint16_t*>(a.v_out) + tile + v_in_tile;
-#pragma unroll
-          for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<u32x4*>(vp + nb * 16 * kBlock) = vf[nb];
         }
       }
       f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
@@ -382,6 +367,29 @@ __global__ void __launch_bounds__(NW * 64) decode_mfma_kernel(DecodeArgs a) {
         pa[wd] = (n16 < G) ? hi[wd] : ((n16 < 2 * G) ? lo_src : 0u);
       }
 
+      if (new_step) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(nv[nb]));
+        if (q4 == nv_q4) {
+          const int e = ntt & 7;
+          const uint32_t sh = (e & 1) * 16;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+              if (wd == (e >> 1)) vf[nb][wd] = (vf[nb][wd] & ~(0xFFFFu << sh)) | (nv[nb] << sh);
+            }
+          }
+        }
+        // Likewise the whole V tile, before the tail past the context is zeroed below.
+        if (a.v_out != nullptr && v_from_b == in_b) {
+          int64_t tA, tB;
+          tiles(s, tA, tB);
+          uint16_t* vp = static_cast<uint16_t*>(a.v_out) + (in_b ? tB : tA) + v_in_tile;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<u32x4*>(vp + nb * 16 * kBlock) = vf[nb];
+        }
+      }
       if (nvalid < 32) {
         // Tokens past the context are stale (possibly NaN): zero them in V, never multiply them.
         const int keep = min(8, max(0, nvalid - tb));
@@ -883,6 +891,36 @@ extern "C" int paged_attention_decode_append(void* out, int32_t out_dtype, const
                                              void* workspace, size_t workspace_bytes, int32_t dtype,
                                              const int32_t* host_context_lens, pkv_stream_t stream) {
   int st = paged_attention_decode_append_partitions(out, out_dtype, query, new_key, new_value, k_cache, v_cache,
+                                                    block_tables, context_lens, B, num_q_heads, num_kv_heads,
+                                                    head_dim, block_size, max_blocks_per_seq, num_blocks,
+                                                    max_context_len, scale, partition_size, workspace,
+                                                    workspace_bytes, dtype, host_context_lens, stream);
+  if (st != PKV_OK) return st;
+  return paged_attention_decode_reduce(out, out_dtype, context_lens, B, num_q_heads, head_dim, max_context_len,
+                                       partition_size, workspace, workspace_bytes, stream);
+}
+
+extern "C" int paged_attention_decode_newest_partitions(
+    void* out, int32_t out_dtype, const void* query, const void* new_key, const void* new_value, const void* k_cache,
+    const void* v_cache, const int32_t* block_tables, const int32_t* context_lens, int32_t B, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    int32_t dtype, const int32_t* host_context_lens, pkv_stream_t stream) {
+  return partitions_impl("paged_attention_decode_newest_partitions", out, out_dtype, query, k_cache, v_cache,
+                         block_tables, context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size,
+                         max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size, workspace,
+                         workspace_bytes, dtype, new_key, new_value, nullptr, nullptr, host_context_lens, stream);
+}
+
+extern "C" int paged_attention_decode_newest(void* out, int32_t out_dtype, const void* query, const void* new_key,
+                                             const void* new_value, const void* k_cache, const void* v_cache,
+                                             const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                                             int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                             int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                             int32_t max_context_len, float scale, int32_t partition_size,
+                                             void* workspace, size_t workspace_bytes, int32_t dtype,
+                                             const int32_t* host_context_lens, pkv_stream_t stream) {
+  int st = paged_attention_decode_newest_partitions(out, out_dtype, query, new_key, new_value, k_cache, v_cache,
                                                     block_tables, context_lens, B, num_q_heads, num_kv_heads,
                                                     head_dim, block_size, max_blocks_per_seq, num_blocks,
                                                     max_context_len, scale, partition_size, workspace,

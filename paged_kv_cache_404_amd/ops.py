@@ -127,6 +127,18 @@ def paged_attention_decode_append(out, query, new_key, new_value, k_cache, v_cac
     check(lib.paged_attention_decode_append(*_fused_args(args, new_key, new_value), _stream(stream)))
 
 
+def paged_attention_decode_newest(out, query, new_key, new_value, k_cache, v_cache, block_tables, context_lens,
+                                  max_context_len, scale, partition_size=0, workspace=None, stream=None,
+                                  host_context_lens=None) -> None:
+    """Decode with every sequence's newest token (position context_lens[b] - 1) taken from
+    new_key/new_value; the cache is not written (append those tokens with paged_cache_append,
+    possibly concurrently on another stream)."""
+    hl, hp = _host_lens_ptr(host_context_lens)
+    args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                        partition_size, workspace, hp)
+    check(lib.paged_attention_decode_newest(*_fused_args(args, new_key, new_value), _stream(stream)))
+
+
 def paged_attention_decode_partitions(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                                       partition_size, workspace, stream=None) -> None:
     args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
@@ -165,12 +177,15 @@ class PreparedDecode:
 
     def __init__(self, out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                  partition_size=0, workspace=None, stream=None, new_key=None, new_value=None,
-                 host_context_lens=None):
+                 host_context_lens=None, write_cache=True):
+        """With new_key/new_value: the fused append (write_cache) or the newest-token variant that
+        leaves the cache to the caller (write_cache=False)."""
         hl, hp = _host_lens_ptr(host_context_lens)
         self._keep = (out, query, k_cache, v_cache, block_tables, context_lens, workspace, new_key, new_value, hl)
         self.args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                                  partition_size, workspace, hp)
         self.fused_args = None if new_key is None else _fused_args(self.args, new_key, new_value)
+        self.write_cache = write_cache
         self.stream = _stream(stream)
         B, Hq, D = query.shape
         self.reduce_args = (out.data_ptr(), dtype_code(out.dtype), context_lens.data_ptr(), B, Hq, D,
@@ -178,13 +193,16 @@ class PreparedDecode:
 
     def __call__(self) -> None:
         if self.fused_args is not None:
-            check(lib.paged_attention_decode_append(*self.fused_args, self.stream))
+            fn = lib.paged_attention_decode_append if self.write_cache else lib.paged_attention_decode_newest
+            check(fn(*self.fused_args, self.stream))
         else:
             check(lib.paged_attention_decode(*self.args, self.stream))
 
     def partitions(self) -> None:
         if self.fused_args is not None:
-            check(lib.paged_attention_decode_append_partitions(*self.fused_args, self.stream))
+            fn = (lib.paged_attention_decode_append_partitions if self.write_cache else
+                  lib.paged_attention_decode_newest_partitions)
+            check(fn(*self.fused_args, self.stream))
         else:
             check(lib.paged_attention_decode_partitions(*self.args, self.stream))
 

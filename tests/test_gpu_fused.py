@@ -1,4 +1,6 @@
-"""GPU parity of the fused append + decode entry point (paged_attention_decode_append).
+"""GPU parity of the fused append + decode entry point (paged_attention_decode_append) and of
+its newest-token variant (paged_attention_decode_newest), which leaves the cache write to
+paged_cache_append.
 
 Each case caches every sequence's prefix, reserves the step's slot on both pools, then runs the
 fused call.  Checked: the cache bytes (the new token included, every other byte still the NaN
@@ -129,6 +131,52 @@ def test_fused_after_copy_on_write():
     t = wl.DecodeTensors([], [], wl.normal_bits(rng, (n, Hkv, D), "bf16"), wl.normal_bits(rng, (n, Hkv, D), "bf16"),
                          wl.normal_bits(rng, (n, Hq, D), "bf16"))
     _fused_vs_all(m, seqs, w, t, slots, 16)
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,lens,ps", [CASES[0], CASES[3], CASES[4], CASES[6], CASES[9]])
+@pytest.mark.parametrize("concurrent", [False, True])
+def test_newest_token_variant(dtype, Hq, Hkv, D, lens, ps, concurrent):
+    """paged_attention_decode_newest leaves the cache alone and gives the fused call's output bit
+    for bit; with paged_cache_append launched beside it on a second stream, the output and the
+    appended cache still match the fused call's."""
+    w = wl.custom_decode(150 + len(lens) + ps, lens, Hq, Hkv, D, dtype, partition_size=ps)
+    t = wl.decode_tensors(w)
+    m, seqs = _prefix(w, t)
+    slots, _ = _reserve(m, seqs)
+    tables, lens_a = m.tables(seqs)
+    B, mcl = len(seqs), int(lens_a.max())
+    q = to_dev(t.q, w.dtype)
+    sk, sv = to_dev(t.step_k, w.dtype), to_dev(t.step_v, w.dtype)
+    k1, v1 = m.k.clone(), m.v.clone()
+    out = torch.full((B, w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
+    ops.paged_attention_decode_append(out, q, sk, sv, m.k, m.v, i32(tables), i32(lens_a), mcl, w.scale, ps,
+                                      ops.decode_workspace(B, w.Hq, w.D, mcl, ps))
+    out2 = torch.full_like(out, float("nan"))
+    ws2 = ops.decode_workspace(B, w.Hq, w.D, mcl, ps)
+    tab_d, len_d, slot_d = i32(tables), i32(lens_a), i32(slots)
+    torch.cuda.synchronize()
+    if concurrent:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        ops.paged_cache_append(k1, v1, sk, sv, slot_d, stream=side)
+        ops.paged_attention_decode_newest(out2, q, sk, sv, k1, v1, tab_d, len_d, mcl, w.scale, ps, ws2)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+    else:
+        k0, v0 = k1.clone(), v1.clone()
+        ops.paged_attention_decode_newest(out2, q, sk, sv, k1, v1, tab_d, len_d, mcl, w.scale, ps, ws2)
+        torch.cuda.synchronize()
+        assert torch.equal(k0.view(torch.int16), k1.view(torch.int16))
+        assert torch.equal(v0.view(torch.int16), v1.view(torch.int16))
+        ops.paged_cache_append(k1, v1, sk, sv, slot_d)
+        torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+    assert torch.equal(k1.view(torch.int16), m.k.view(torch.int16))
+    assert torch.equal(v1.view(torch.int16), m.v.view(torch.int16))
+    m.cache.append(t.step_k, t.step_v, slots)
+    m.assert_cache_bit_exact()
+    ref = oatt.paged_decode(t.q, m.cache, tables, lens_a, w.scale)
+    assert float(np.abs(out2.cpu().numpy().astype(np.float64) - ref).max()) <= ATOL
 
 
 def test_fused_rejects_fp32():
