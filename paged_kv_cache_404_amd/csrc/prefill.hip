@@ -25,6 +25,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLazyRescaleLog2 = 8.0f;
+// Running maximum before any visible key: finite, so exp2(x - m) needs no -inf guard, and far
+// below any score (a split that sees no key of a row keeps it; the merge weighs it exp2(-1e30) = 0).
+constexpr float kNoMax = -1e30f;
 
 struct PrefillArgs {
   void* out;
@@ -134,7 +137,7 @@ __global__ void __launch_bounds__(PrefillShape<G>::NWAVES * 64) prefill_mfma_ker
   for (int h = 0; h < HPW; ++h) {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) o[h][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    m_run[h] = -INFINITY;
+    m_run[h] = kNoMax;
     l_run[h] = 0.f;
   }
 
@@ -215,29 +218,47 @@ __global__ void __launch_bounds__(PrefillShape<G>::NWAVES * 64) prefill_mfma_ker
           }
         }
       }
-      const int tb = t0 + 8 * q4;
+      // Raw scores; scale * log2(e) > 0 is applied inside the exponent, so maxima of raw scores
+      // give the maxima of scaled ones.  Both heads go through each phase before the next one, so
+      // that the common path (no mask, no rescale) is one basic block in which the compiler can
+      // issue one head's softmax arithmetic between the other head's matrix instructions.
+      float sc[HPW][8];
 #pragma unroll
       for (int h = 0; h < HPW; ++h) {
-        // Raw scores; scale * log2(e) > 0 is applied inside the exponent, so maxima of raw
-        // scores give the maxima of scaled ones.
-        float sc[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          sc[j] = s1[h][j];
-          sc[4 + j] = s2[h][j];
+          sc[h][j] = s1[h][j];
+          sc[h][4 + j] = s2[h][j];
         }
-        if (masked) {
+      }
+      if (masked) {
+        // Keys visible to this lane's row in this step: t0 + 8*q4 + i <= row_lim.  The empty asm
+        // keeps the compares inside the (rarely taken) branch.
+        int lim = row_ok ? row_lim - (t0 + 8 * q4) : -1;
+        asm volatile("" : "+v"(lim));
 #pragma unroll
-          for (int i = 0; i < 8; ++i) sc[i] = (row_ok && tb + i <= row_lim) ? sc[i] : -INFINITY;
+        for (int h = 0; h < HPW; ++h) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sc[h][i] = (i <= lim) ? sc[h][i] : -INFINITY;
         }
-        float bmax = sc[0];
+      }
+      // Lazy rescale: a row's reference maximum moves only when one of its scores exceeds it by
+      // more than 2^8.  Each lane tests its own 8 scores per head; the row maximum over the
+      // row's four lanes is formed only when some lane of the wave passes that test.
+      float lmax[HPW];
+      bool big = false;
 #pragma unroll
-        for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sc[i]);
-        bmax = group4_max(bmax);
-        bmax *= c;
-
-        const bool need = row_ok && (bmax > m_run[h] + kLazyRescaleLog2);
-        if (__any(need)) {
+      for (int h = 0; h < HPW; ++h) {
+        lmax[h] = sc[h][0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) lmax[h] = fmaxf(lmax[h], sc[h][i]);
+        big = big || (lmax[h] * c > m_run[h] + kLazyRescaleLog2);
+      }
+      if (__any(big)) {
+#pragma unroll
+        for (int h = 0; h < HPW; ++h) {
+          const float bmax = group4_max(lmax[h]) * c;
+          const bool need = row_ok && (bmax > m_run[h] + kLazyRescaleLog2);
           const float m_new = need ? bmax : m_run[h];
           const float alpha = need ? fast_exp2(m_run[h] - m_new) : 1.0f;
           l_run[h] *= alpha;
@@ -249,16 +270,17 @@ __global__ void __launch_bounds__(PrefillShape<G>::NWAVES * 64) prefill_mfma_ker
             for (int nb = 0; nb < NB; ++nb) o[h][nb][j] *= f;
           }
         }
-        // A split can lie wholly past a row's causal limit: then the row has seen no key yet
-        // (m = -inf, every score -inf) and its weights must be 0, not exp2(-inf - -inf) = NaN.
-        const float m_ref = m_run[h] == -INFINITY ? 0.f : m_run[h];
-        float pv[8];
-        float psum = 0.f;
+      }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pv[i] = fast_exp2(fmaf(sc[i], c, -m_ref));
-          psum += pv[i];
-        }
+      for (int h = 0; h < HPW; ++h) {
+        // Before a row's first visible key m_run is the finite kNoMax: masked scores (-inf) get
+        // weight exp2(-inf) = 0, and the first real maximum rescales by exp2(kNoMax - m) = 0.
+        float pv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pv[i] = fast_exp2(fmaf(sc[h][i], c, -m_run[h]));
+        float psum = pv[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) psum += pv[i];
         l_run[h] += psum;
         // hi = the weights rounded to 16 bits, lo = the rounding residuals rounded to 16 bits.
         u32x4 hi, lo;
@@ -319,7 +341,7 @@ __global__ void __launch_bounds__(PrefillShape<G>::NWAVES * 64) prefill_mfma_ker
     float acc = 0.f, lsum = 0.f;
 #pragma unroll
     for (int k = 0; k < KSPLIT; ++k) {
-      const float f = fast_exp2(sM[k][h][r] - M);  // splits without a step hold m = -inf -> 0
+      const float f = fast_exp2(sM[k][h][r] - M);  // a split that saw no key of the row holds kNoMax -> 0
       acc += f * sO[k][h][r][d];
       lsum += f * sL[k][h][r];
     }
