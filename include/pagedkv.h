@@ -63,6 +63,9 @@ extern "C" {
 #define PKV_F16 1
 #define PKV_BF16 2
 
+/* partition_size value: a batch-adaptive single pass (not batch invariant; see paged_attention_decode). */
+#define PKV_SINGLE_PASS_ADAPTIVE (-1)
+
 typedef void* pkv_stream_t; /* hipStream_t */
 
 /* Thread-local message describing the last non-zero status returned to this thread. */
@@ -107,7 +110,7 @@ int paged_cache_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst
 
 /*
  * paged_attention_decode_workspace_bytes - device workspace paged_attention_decode needs.
- * 0 when partition_size is 0 (single pass).  Otherwise room for one (max, sum, unnormalised
+ * 0 when partition_size is 0 or -1 (single pass).  Otherwise room for one (max, sum, unnormalised
  * output) partial per (sequence, query head, partition).
  */
 size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads, int32_t head_dim,
@@ -131,9 +134,19 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_he
  *   partition_size 0: one pass per (sequence, KV head).  Otherwise a multiple of block_size:
  *                  the context is cut into fixed partitions of that many tokens, each processed
  *                  independently, and the partial softmaxes are merged exactly (log-sum-exp).
- *                  Partition boundaries depend only on the token position, never on the batch,
- *                  so a sequence's output bits do not depend on the rest of the batch.  At most
- *                  65535 partitions per sequence (PKV_EUNSUPPORTED beyond).
+ *                  At most 65535 partitions per sequence (PKV_EUNSUPPORTED beyond).
+ *                  PKV_SINGLE_PASS_ADAPTIVE (-1): one pass whose split of the work inside a
+ *                  workgroup follows the batch's max_context_len (fewer waves when it is at most
+ *                  512), faster on batches of short contexts but not batch invariant.
+ *                  Batch invariance (every value except -1): for a fixed partition_size, dtype,
+ *                  out_dtype and head shape, a sequence's output bits depend only on its own
+ *                  query, cached K/V and length - not on the other sequences, their number or
+ *                  order, max_context_len, max_blocks_per_seq, host_context_lens, or whether the
+ *                  step's token comes through the fused append.  Partition boundaries are token
+ *                  positions and the waves per workgroup depend on partition_size alone.
+ *                  [Notes] "Continuous batching and PagedAttention: serving many users from one
+ *                  GPU" names batch-dependent reduction order as the source of nondeterministic
+ *                  outputs at temperature 0.
  *   workspace      device scratch of at least paged_attention_decode_workspace_bytes(...) bytes
  *                  (may be NULL when that is 0); contents on entry do not matter.
  *   host_context_lens  NULL, or a host copy of context_lens (B <= 512 entries): used only to

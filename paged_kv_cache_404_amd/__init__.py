@@ -7,7 +7,7 @@ decode attention with split-K, chunked-prefill causal attention).  This package 
 memory and streams).  Importing it fails when the library is not built; there is no fallback.
 """
 from ._lib import (EXPORTED, PKV_BF16, PKV_EHIP, PKV_EINVAL, PKV_ENOMEM, PKV_EUNSUPPORTED, PKV_F16, PKV_F32,  # noqa: F401
-                   PKV_OK, LIB_PATH, OutOfBlocksError, PagedKVError, last_error, lib)
+                   PKV_OK, PKV_SINGLE_PASS_ADAPTIVE, LIB_PATH, OutOfBlocksError, PagedKVError, last_error, lib)
 from .pool import BlockPool  # noqa: F401
 
 

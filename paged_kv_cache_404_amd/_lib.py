@@ -19,6 +19,9 @@ PKV_F32 = 0
 PKV_F16 = 1
 PKV_BF16 = 2
 
+# partition_size value: a batch-adaptive single pass (faster on short contexts, not batch invariant).
+PKV_SINGLE_PASS_ADAPTIVE = -1
+
 
 class PagedKVError(RuntimeError):
     def __init__(self, status: int, message: str):

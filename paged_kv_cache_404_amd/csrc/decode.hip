@@ -646,8 +646,8 @@ int validate(const char* fn, void* out, int32_t out_dtype, const void* query, co
   const int G = Hq / Hkv;
   if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PKV_EUNSUPPORTED, "%s: group size %d", fn, G);
   if (B > 65535 || Hq > 65535) return fail(PKV_EUNSUPPORTED, "%s: batch or head count above 65535", fn);
-  if (partition_size < 0 || partition_size % bs != 0)
-    return fail(PKV_EINVAL, "%s: partition_size %d must be 0 or a multiple of block_size", fn, partition_size);
+  if (partition_size != PKV_SINGLE_PASS_ADAPTIVE && (partition_size < 0 || partition_size % bs != 0))
+    return fail(PKV_EINVAL, "%s: partition_size %d must be 0, -1 or a multiple of block_size", fn, partition_size);
   if (partition_size > 0 && (max_ctx + static_cast<int64_t>(partition_size) - 1) / partition_size > 65535)
     return fail(PKV_EUNSUPPORTED, "%s: more than 65535 partitions per sequence", fn);
   if (static_cast<int64_t>(max_ctx) > static_cast<int64_t>(max_blocks) * bs)
@@ -670,12 +670,17 @@ int launch_valu(const DecodeArgs& a, int B, hipStream_t s) {
   return PKV_OK;
 }
 
-// Waves per workgroup: 4 for partitions up to 512 tokens (<= 4 steps per wave), 8 above.
+// Waves per workgroup: 4 for partitions of up to 512 tokens (<= 4 steps per wave), 8 above and
+// for the single pass.  The choice depends only on the caller's partition_size, never on the
+// batch (a single pass spans the batch's longest context, so its wave count is fixed): a
+// sequence's reduction order, and so its output bits, do not depend on the rest of the batch.
+// The batch-adaptive single pass (partition_size -1) applies the 512-token rule to the batch's
+// longest context instead.
 template <int DT, int DT_OUT, int D, int G>
-int launch_mfma(const DecodeArgs& a, int B, hipStream_t s) {
+int launch_mfma(const DecodeArgs& a, int B, bool single_pass, hipStream_t s) {
   const dim3 grid(a.Hkv, B, a.max_parts);
   const bool fused = a.new_k != nullptr;
-  if (a.part_size <= 512) {
+  if (!single_pass && a.part_size <= 512) {
     if (fused)
       hipLaunchKernelGGL((decode_mfma_kernel<DT, DT_OUT, D, G, 4, true>), grid, dim3(256), 0, s, a);
     else
@@ -690,33 +695,37 @@ int launch_mfma(const DecodeArgs& a, int B, hipStream_t s) {
 }
 
 template <int DT, int DT_OUT, int D>
-int dispatch_group(const DecodeArgs& a, int B, hipStream_t s) {
+int dispatch_group(const DecodeArgs& a, int B, bool single_pass, hipStream_t s) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_mfma<DT, DT_OUT, D, 1>(a, B, s);
-    case 2: return launch_mfma<DT, DT_OUT, D, 2>(a, B, s);
-    case 4: return launch_mfma<DT, DT_OUT, D, 4>(a, B, s);
-    default: return launch_mfma<DT, DT_OUT, D, 8>(a, B, s);
+    case 1: return launch_mfma<DT, DT_OUT, D, 1>(a, B, single_pass, s);
+    case 2: return launch_mfma<DT, DT_OUT, D, 2>(a, B, single_pass, s);
+    case 4: return launch_mfma<DT, DT_OUT, D, 4>(a, B, single_pass, s);
+    default: return launch_mfma<DT, DT_OUT, D, 8>(a, B, single_pass, s);
   }
 }
 
 template <int DT, int DT_OUT>
-int dispatch_dim(const DecodeArgs& a, int D, int B, hipStream_t s) {
+int dispatch_dim(const DecodeArgs& a, int D, int B, bool single_pass, hipStream_t s) {
   if constexpr (DT == PKV_F32) {
     return D == 64 ? launch_valu<DT, DT_OUT, 64>(a, B, s) : launch_valu<DT, DT_OUT, 128>(a, B, s);
   } else {
-    return D == 64 ? dispatch_group<DT, DT_OUT, 64>(a, B, s) : dispatch_group<DT, DT_OUT, 128>(a, B, s);
+    return D == 64 ? dispatch_group<DT, DT_OUT, 64>(a, B, single_pass, s)
+                   : dispatch_group<DT, DT_OUT, 128>(a, B, single_pass, s);
   }
 }
 
-int launch_partitions(const DecodeArgs& a, int32_t dtype, int32_t out_dtype, int D, int B, hipStream_t s) {
+int launch_partitions(const DecodeArgs& a, int32_t dtype, int32_t out_dtype, int D, int B, bool single_pass,
+                      hipStream_t s) {
   const bool f32out = out_dtype == PKV_F32;
   switch (dtype) {
     case PKV_BF16:
-      return f32out ? dispatch_dim<PKV_BF16, PKV_F32>(a, D, B, s) : dispatch_dim<PKV_BF16, PKV_BF16>(a, D, B, s);
+      return f32out ? dispatch_dim<PKV_BF16, PKV_F32>(a, D, B, single_pass, s)
+                    : dispatch_dim<PKV_BF16, PKV_BF16>(a, D, B, single_pass, s);
     case PKV_F16:
-      return f32out ? dispatch_dim<PKV_F16, PKV_F32>(a, D, B, s) : dispatch_dim<PKV_F16, PKV_F16>(a, D, B, s);
+      return f32out ? dispatch_dim<PKV_F16, PKV_F32>(a, D, B, single_pass, s)
+                    : dispatch_dim<PKV_F16, PKV_F16>(a, D, B, single_pass, s);
     default:
-      return dispatch_dim<PKV_F32, PKV_F32>(a, D, B, s);
+      return dispatch_dim<PKV_F32, PKV_F32>(a, D, B, single_pass, s);
   }
 }
 
@@ -811,7 +820,7 @@ int partitions_impl(const char* fn, void* out, int32_t out_dtype, const void* qu
     std::stable_sort(a.order, a.order + B, [&](int32_t x, int32_t y) { return host_lens[x] > host_lens[y]; });
     a.num_order = B;
   }
-  launch_partitions(a, dtype, out_dtype, D, B, as_stream(stream));
+  launch_partitions(a, dtype, out_dtype, D, B, partition_size == 0, as_stream(stream));
   return check_launch(fn);
 }
 
@@ -848,13 +857,14 @@ extern "C" int paged_attention_decode_reduce(void* out, int32_t out_dtype, const
                                              int32_t num_q_heads, int32_t head_dim, int32_t max_context_len,
                                              int32_t partition_size, const void* workspace, size_t workspace_bytes,
                                              pkv_stream_t stream) {
-  if (B < 0 || num_q_heads <= 0 || (head_dim != 64 && head_dim != 128) || max_context_len < 0 || partition_size < 0)
+  if (B < 0 || num_q_heads <= 0 || (head_dim != 64 && head_dim != 128) || max_context_len < 0 ||
+      partition_size < PKV_SINGLE_PASS_ADAPTIVE)
     return fail(PKV_EINVAL, "paged_attention_decode_reduce: bad sizes");
   if (out_dtype != PKV_F32 && out_dtype != PKV_F16 && out_dtype != PKV_BF16)
     return fail(PKV_EINVAL, "paged_attention_decode_reduce: unknown out_dtype %d", out_dtype);
-  if (partition_size % kBlock != 0)
+  if (partition_size > 0 && partition_size % kBlock != 0)
     return fail(PKV_EINVAL, "paged_attention_decode_reduce: partition_size must be a multiple of 16");
-  if (B == 0 || max_context_len == 0 || partition_size == 0) return PKV_OK;
+  if (B == 0 || max_context_len == 0 || partition_size <= 0) return PKV_OK;
   const Plan pl = make_plan(B, num_q_heads, head_dim, max_context_len, partition_size);
   if (pl.max_parts <= 1) return PKV_OK;
   if (!out || !context_lens || !workspace || workspace_bytes < pl.need_bytes)

@@ -72,6 +72,7 @@ def _decode(**kw):
     (dict(dtype=7), pkv.PKV_EINVAL),
     (dict(out_dtype=pkv.PKV_F16), pkv.PKV_EINVAL),  # neither f32 nor the input type
     (dict(ps=24), pkv.PKV_EINVAL),                 # not a multiple of the block size
+    (dict(ps=-2), pkv.PKV_EINVAL),                 # negative other than the adaptive single pass
     (dict(max_ctx=129), pkv.PKV_EINVAL),           # beyond max_blocks * block_size
     (dict(query=NULL), pkv.PKV_EINVAL),
     (dict(ps=32), pkv.PKV_EINVAL),                 # workspace missing

@@ -1,0 +1,116 @@
+"""Batch invariance of decode attention as a product guarantee.
+
+For a fixed partition_size (and dtype, output dtype, head configuration), a sequence's output
+bits depend only on its own query, its own cached K/V and its own length: not on how many other
+sequences share the call, which ones, in what order, on max_context_len, on the width of the
+block-table rows, on the host copy of the lengths (work order), or on whether the step's token is
+appended by the fused call.  The pages name reduction orders that move with the batch as the
+source of temperature-0 nondeterminism ([Notes] "Continuous batching and PagedAttention: serving
+many users from one GPU"); here partition boundaries are fixed token positions and the waves per
+workgroup depend on partition_size alone (the single pass always uses 8)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from oracle import attention as oatt
+from paged_kv_cache_404_amd import PKV_SINGLE_PASS_ADAPTIVE, ops
+
+from .gpu_util import ATOL, build_decode, i32, to_dev
+
+pytestmark = pytest.mark.gpu
+
+# Short (<= 512) and long sequences: a single pass over a batch of short sequences alone and over
+# the same sequences next to long ones must agree bit for bit.
+LENS = [37, 300, 2048, 1, 512, 513, 1200, 64, 4000, 16]
+
+
+def _decode(m, seqs, q_bits, Hq, scale, ps, dtype, max_blocks=None, max_context_len=None, host_lens=False):
+    tables, lens = m.tables(seqs, max_blocks)
+    B = len(seqs)
+    out = torch.full((B, Hq, m.D), float("nan"), dtype=torch.float32, device="cuda")
+    mcl = int(lens.max()) if max_context_len is None else max_context_len
+    ops.paged_attention_decode(out, to_dev(q_bits, dtype), m.k, m.v, i32(tables), i32(lens), mcl, scale, ps,
+                               ops.decode_workspace(B, Hq, m.D, mcl, ps), host_context_lens=lens if host_lens else None)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("dtype,ps", [("bf16", 0), ("bf16", 256), ("bf16", 512), ("bf16", 2048), ("f16", 0),
+                                      ("f32", 0), ("f32", 512)])
+def test_sequence_output_independent_of_batch(dtype, ps):
+    Hq, Hkv, D = (32, 8, 128) if dtype != "f32" else (8, 8, 64)
+    w = wl.custom_decode(300 + ps, LENS, Hq, Hkv, D, dtype, partition_size=ps)
+    t = wl.decode_tensors(w)
+    m, seqs = build_decode(w, t)
+    full = _decode(m, seqs, t.q, Hq, w.scale, ps, dtype)
+    tables, lens = m.tables(seqs)
+    ref = oatt.paged_decode(t.q, m.cache, tables, lens, w.scale)
+    assert float(np.abs(full.cpu().numpy().astype(np.float64) - ref).max()) <= ATOL
+    rng = np.random.default_rng(ps + 7)
+    variants = []
+    # every sequence alone, with the tightest max_context_len and table width
+    for i in range(len(seqs)):
+        one = _decode(m, [seqs[i]], t.q[[i]], Hq, w.scale, ps, dtype)
+        variants.append(([i], one))
+    # reversed and shuffled orders; longest-first work order; padded max_context_len and tables
+    rev = list(range(len(seqs)))[::-1]
+    variants.append((rev, _decode(m, [seqs[i] for i in rev], t.q[rev], Hq, w.scale, ps, dtype, host_lens=True)))
+    shuf = [int(x) for x in rng.permutation(len(seqs))]
+    variants.append((shuf, _decode(m, [seqs[i] for i in shuf], t.q[shuf], Hq, w.scale, ps, dtype,
+                                   max_blocks=400, max_context_len=6000)))
+    # only the short sequences (a single pass would see a batch maximum <= 512 here)
+    short = [i for i, L in enumerate(LENS) if L <= 512]
+    variants.append((short, _decode(m, [seqs[i] for i in short], t.q[short], Hq, w.scale, ps, dtype)))
+    for idx, out in variants:
+        for j, i in enumerate(idx):
+            assert torch.equal(out[j].view(torch.int32), full[i].view(torch.int32)), (ps, idx, i)
+
+
+@pytest.mark.parametrize("ps", [0, 512])
+def test_fused_append_output_independent_of_batch(ps):
+    """The fused append + decode of one sequence gives the same bits alone and in a batch."""
+    lens = [700, 33, 1500, 16, 260]
+    w = wl.custom_decode(330 + ps, lens, 32, 8, 128, "bf16", partition_size=ps)
+    t = wl.decode_tensors(w)
+    m, seqs = build_decode(w, t)
+    tables, lens_a = m.tables(seqs)
+    k0, v0 = m.k.clone(), m.v.clone()
+    q, sk, sv = to_dev(t.q, "bf16"), to_dev(t.step_k, "bf16"), to_dev(t.step_v, "bf16")
+
+    def fused(idx, mcl):
+        k, v = k0.clone(), v0.clone()
+        out = torch.full((len(idx), w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
+        ops.paged_attention_decode_append(out, q[idx].contiguous(), sk[idx].contiguous(), sv[idx].contiguous(), k, v,
+                                          i32(tables[idx]), i32(lens_a[idx]), mcl, w.scale, ps,
+                                          ops.decode_workspace(len(idx), w.Hq, w.D, mcl, ps))
+        torch.cuda.synchronize()
+        return out, k, v
+
+    full, kf, vf = fused(list(range(len(seqs))), int(lens_a.max()))
+    for i in range(len(seqs)):
+        one, k1, v1 = fused([i], int(lens_a[i]))
+        assert torch.equal(one[0].view(torch.int32), full[i].view(torch.int32))
+    rev = list(range(len(seqs)))[::-1]
+    out_r, kr, vr = fused(rev, tables.shape[1] * 16)  # the widest max_context_len the tables allow
+    for j, i in enumerate(rev):
+        assert torch.equal(out_r[j].view(torch.int32), full[i].view(torch.int32))
+    assert torch.equal(kr.view(torch.int16), kf.view(torch.int16))
+    assert torch.equal(vr.view(torch.int16), vf.view(torch.int16))
+
+
+def test_adaptive_single_pass():
+    """PKV_SINGLE_PASS_ADAPTIVE picks 4 waves per workgroup when the batch's longest context is at
+    most 512 tokens (the same arithmetic as one 512-token partition) and 8 above (the same as the
+    invariant single pass); either way within the oracle tolerance."""
+    short = [37, 300, 1, 512, 64, 16]
+    for lens, twin in ((short, 512), (short + [2048, 700], 0)):
+        w = wl.custom_decode(350 + len(lens), lens, 32, 8, 128, "bf16")
+        t = wl.decode_tensors(w)
+        m, seqs = build_decode(w, t)
+        got = _decode(m, seqs, t.q, w.Hq, w.scale, PKV_SINGLE_PASS_ADAPTIVE, "bf16")
+        want = _decode(m, seqs, t.q, w.Hq, w.scale, twin, "bf16")
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32))
+        tables, lens_a = m.tables(seqs)
+        ref = oatt.paged_decode(t.q, m.cache, tables, lens_a, w.scale)
+        assert float(np.abs(got.cpu().numpy().astype(np.float64) - ref).max()) <= ATOL
