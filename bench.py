@@ -218,6 +218,37 @@ def cpu_baseline_prefill(ctx, Hq, Hkv, D, scale, seconds):
             "sample": f"first {R} of 512 chunk rows after {ctx} cached tokens, numpy fp64, {el:.1f} s"}
 
 
+def measure_prefix_cache():
+    """Host prefix cache on a long-context-sized pool (18,023 blocks): register a 2,048-token
+    prompt (128 blocks), then time lookups of that prompt plus 64 new tokens (128 trie probes, 128
+    new references) each followed by freeing the new sequence, and re-registration (128 probes)."""
+    import numpy as np
+
+    from paged_kv_cache_404_amd import BlockPool
+    rng = np.random.default_rng(9)
+    N = 18023
+    pool = BlockPool(N, 16, rng.permutation(N))
+    prompt = rng.integers(0, 128000, 2048).astype(np.int32)
+    s = pool.new_seq()
+    pool.append(s, 2048)
+    assert pool.prefix_insert(s, prompt) == 128
+    req = np.concatenate([prompt, rng.integers(0, 128000, 64).astype(np.int32)])
+    n_iter = 2000
+    t0 = time.perf_counter()
+    for _ in range(n_iter):
+        q, n = pool.prefix_lookup(req)
+        pool.free(q)
+    lookup_us = (time.perf_counter() - t0) / n_iter * 1e6
+    assert n == 2048
+    t0 = time.perf_counter()
+    for _ in range(n_iter):
+        pool.prefix_insert(s, prompt)
+    insert_us = (time.perf_counter() - t0) / n_iter * 1e6
+    return {"workload": "prefix_cache_lookup_2048_tokens_pool_18023", "lookup_and_free_us": round(lookup_us, 2),
+            "reinsert_us": round(insert_us, 2), "matched_tokens": int(n), "blocks_per_lookup": 128,
+            "note": "host time per call through the Python binding (ctypes call overhead included)"}
+
+
 def measure_long(args, dev):
     """The long-context decode: batch 8 at 32,768 tokens (2,048 scattered blocks each), split-K
     over 512-token partitions, fused append; KV + Q bytes per step as in the main line."""
@@ -507,6 +538,7 @@ def main():
         torch.cuda.empty_cache()
         res["prefill"] = measure_prefill(args, dev)
         res["long_context"] = measure_long(args, dev)
+        res["prefix_cache"] = measure_prefix_cache()
     print(json.dumps(res), flush=True)
 
 

@@ -270,8 +270,10 @@ int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const void* quer
  *   - an append whose first token lands in a partially filled last block with refcount > 1 takes
  *     a fresh block, reports (old, new) for paged_cache_copy_blocks, and drops one reference of old;
  *   - free drops one reference per block in table order and returns a block to the free list
- *     when its count reaches 0.
- * Appends are all-or-nothing: PKV_ENOMEM leaves the pool unchanged.  Sequence ids are the lowest
+ *     when its count reaches 0 (a block registered in the prefix cache goes to its LRU instead).
+ * Appends are all-or-nothing: PKV_ENOMEM leaves the pool unchanged.  With the prefix cache in
+ * use, an allocation with an empty free list evicts (see pkv_prefix_insert), and PKV_ENOMEM means
+ * the free list and the evictable blocks together are too few.  Sequence ids are the lowest
  * id not currently live.  The pool is host memory only, synchronous, and not thread-safe per
  * handle (different handles are independent).  It never touches the GPU.
  */
@@ -321,6 +323,38 @@ int pkv_build_block_tables(const pkv_pool* pool, const int32_t* seqs, int32_t n,
  */
 int pkv_build_slot_mapping(const pkv_pool* pool, const int32_t* seqs, const int32_t* starts,
                            const int32_t* counts, int32_t n, int32_t* slots_out);
+
+/* ============================== prefix cache ============================== */
+/*
+ * [Serving] Step 8 ("Prefix caching"): a request whose leading tokens are already held in blocks
+ * shares them - the longest block-aligned prefix first - and each shared block gains a reference.
+ * Blocks are registered by content: registered block k of a prefix is identified by the tokens of
+ * the whole prefix up to and including its own block_size tokens.  Tokens are opaque host int32.
+ *
+ * pkv_prefix_insert - register seq's full blocks (the first min(n_tokens, length) / block_size)
+ *   under the prefixes of `tokens` (the caller's token ids for the sequence's positions 0..).
+ *   A prefix already registered keeps its block (seq's copy stays unregistered) and the walk goes
+ *   on below it; the walk stops at a block already registered under a different prefix.  Only
+ *   full blocks are registered, so a registered block is never written again.
+ *   *n_registered (may be NULL) = seq's blocks newly registered.
+ * pkv_prefix_lookup - start a new sequence (lowest free id) holding the longest registered
+ *   block-aligned prefix of tokens[0 .. n_tokens) (possibly all of it, possibly none): its table
+ *   is those blocks, its length *n_matched; each block gains a reference.  The caller appends the
+ *   remaining tokens with pkv_seq_append as usual.
+ * Release and eviction: a registered block whose count reaches 0 is not freed but waits on an LRU
+ *   list (least recently released first); a lookup hit takes it off.  The registered blocks one
+ *   pkv_seq_free releases join the list deepest first (reverse table order), so eviction shortens
+ *   a registered prefix from its end.  An allocation that finds
+ *   the free list empty evicts the LRU head: it and every registered block below it (prefixes
+ *   extending through it) are unregistered; those below without references move from the LRU to
+ *   the free list, least recently released first; the evicted block is the one allocated.
+ * pkv_prefix_evictable - copy the LRU (front = next to evict) to out; *n = its length.
+ * pkv_prefix_num_registered - number of registered blocks.
+ */
+int pkv_prefix_insert(pkv_pool* pool, int32_t seq, const int32_t* tokens, int32_t n_tokens, int32_t* n_registered);
+int pkv_prefix_lookup(pkv_pool* pool, const int32_t* tokens, int32_t n_tokens, int32_t* seq_out, int32_t* n_matched);
+int pkv_prefix_evictable(const pkv_pool* pool, int32_t* out, int32_t capacity, int32_t* n);
+int pkv_prefix_num_registered(const pkv_pool* pool, int32_t* out);
 
 #ifdef __cplusplus
 }

@@ -25,6 +25,27 @@ for it; the reading used here (and by the library) is:
 * ``free`` drops one reference per block in table order; a block returns to the free list
   when its count reaches zero.
 * Sequence ids are the lowest id not currently live.
+
+Prefix caching follows [Serving] The Build, Step 8 ("Prefix caching"): a dictionary from a
+block-aligned token prefix to the list of blocks holding it; a lookup tries the longest
+block-aligned prefix of the request first and, on a hit, adds one reference to every block of
+the match.  The pages show no insertion or release; the reading used here (and by the library):
+
+* ``prefix_insert(seq, tokens)`` registers, for k = 1 .. (full blocks of seq), the prefix
+  ``tokens[:16k]`` with the blocks of the prefix ``tokens[:16(k-1)]`` as already registered plus
+  seq's block k; a prefix that is already registered keeps its blocks; registration stops at a
+  block that is already registered under another prefix.  Only full blocks are registered, so
+  a registered block is never written again.
+* ``prefix_lookup(tokens)`` starts a new sequence holding the longest registered block-aligned
+  prefix of ``tokens`` (the whole request may match).
+* A registered block whose count reaches zero is not freed: it waits on an LRU list (least
+  recently released first) and can still be matched, which takes it off the list.  The blocks a
+  finished sequence releases join the list deepest first (reverse table order), so eviction
+  shortens a registered prefix from its end rather than cutting it at the root.
+* An allocation with an empty free list evicts the LRU head: every prefix whose blocks include
+  it is unregistered, and the blocks left in no registered prefix leave the LRU for the free
+  list in LRU order; the evicted block is the one allocated.  An append fails only when the free
+  list and the LRU together are too short.
 """
 from __future__ import annotations
 
@@ -53,19 +74,39 @@ class PoolModel:
         self.refcnt = [0] * self.num_blocks
         self.tables: dict[int, list[int]] = {}
         self.lens: dict[int, int] = {}
+        self.entries: dict[tuple, list[int]] = {}  # registered prefix tokens -> its blocks
+        self.lru: list[int] = []  # registered blocks with no reference, least recently released first
 
     # ---- block level --------------------------------------------------------------
     def _alloc(self) -> int:
-        if not self.free:
+        if self.free:
+            b = self.free.pop()
+        elif self.lru:
+            b = self._evict()
+        else:
             raise OutOfBlocks()
-        b = self.free.pop()
         self.refcnt[b] = 1
         return b
 
-    def _release(self, b: int) -> None:
+    def _release(self, b: int, idle: list) -> None:
+        """Drop one reference; an unregistered block at zero goes back on the free list, a
+        registered one is collected in ``idle`` for the LRU."""
         self.refcnt[b] -= 1
         if self.refcnt[b] == 0:
-            self.free.append(b)
+            (idle if self._registered(b) else self.free).append(b)
+
+    def _registered(self, b: int) -> bool:
+        return any(b in blocks for blocks in self.entries.values())
+
+    def _evict(self) -> int:
+        b = self.lru.pop(0)
+        for key in [k for k, blocks in self.entries.items() if b in blocks]:
+            del self.entries[key]
+        for x in list(self.lru):
+            if not self._registered(x):
+                self.lru.remove(x)
+                self.free.append(x)
+        return b
 
     # ---- sequence level -----------------------------------------------------------
     def _check(self, seq: int) -> None:
@@ -109,7 +150,7 @@ class PoolModel:
     def append(self, seq: int, n: int):
         """Reserve slots for ``n`` tokens.  Returns (slots, cow_pairs)."""
         need = self.blocks_needed(seq, n)
-        if need > len(self.free):
+        if need > len(self.free) + len(self.lru):
             raise OutOfBlocks()
         table = self.tables[seq]
         bs = self.block_size
@@ -130,10 +171,58 @@ class PoolModel:
 
     def free_seq(self, seq: int) -> None:
         self._check(seq)
+        idle: list[int] = []
         for b in self.tables[seq]:
-            self._release(b)
+            self._release(b, idle)
+        self.lru.extend(reversed(idle))
         del self.tables[seq]
         del self.lens[seq]
+
+    # ---- prefix cache ([Serving] The Build, Step 8) ------------------------------------
+    def prefix_lookup(self, tokens):
+        """New sequence holding the longest registered block-aligned prefix of ``tokens``.
+        Returns (seq, matched token count)."""
+        s = self.new_seq()
+        bs = self.block_size
+        for n in range(len(tokens) // bs * bs, 0, -bs):
+            key = tuple(int(t) for t in tokens[:n])
+            if key in self.entries:
+                blocks = self.entries[key]
+                for b in blocks:
+                    if self.refcnt[b] == 0:
+                        self.lru.remove(b)
+                    self.refcnt[b] += 1
+                self.tables[s] = list(blocks)
+                self.lens[s] = n
+                return s, n
+        return s, 0
+
+    def prefix_insert(self, seq: int, tokens) -> int:
+        """Register seq's full blocks under their token prefixes.  Returns how many of seq's
+        blocks were newly registered."""
+        self._check(seq)
+        bs = self.block_size
+        nfull = min(len(tokens), self.lens[seq]) // bs
+        chain: list[int] = []
+        added = 0
+        for k in range(1, nfull + 1):
+            key = tuple(int(t) for t in tokens[: k * bs])
+            if key in self.entries:
+                chain = list(self.entries[key])
+                continue
+            b = self.tables[seq][k - 1]
+            if self._registered(b):
+                break
+            chain = chain + [b]
+            self.entries[key] = chain
+            added += 1
+        return added
+
+    def num_evictable(self) -> int:
+        return len(self.lru)
+
+    def num_registered(self) -> int:
+        return len({b for blocks in self.entries.values() for b in blocks})
 
     # ---- builders -----------------------------------------------------------------
     def slot(self, seq: int, pos: int) -> int:

@@ -87,6 +87,10 @@ _SIGS = {
     "pkv_seq_num_blocks": (C.c_int, [_pool_p, _i32, _pi32]),
     "pkv_build_block_tables": (C.c_int, [_pool_p, _pi32, _i32, _i32, _pi32, _pi32]),
     "pkv_build_slot_mapping": (C.c_int, [_pool_p, _pi32, _pi32, _pi32, _i32, _pi32]),
+    "pkv_prefix_insert": (C.c_int, [_pool_p, _i32, _pi32, _i32, _pi32]),
+    "pkv_prefix_lookup": (C.c_int, [_pool_p, _pi32, _i32, _pi32, _pi32]),
+    "pkv_prefix_evictable": (C.c_int, [_pool_p, _pi32, _i32, _pi32]),
+    "pkv_prefix_num_registered": (C.c_int, [_pool_p, _pi32]),
 }
 
 for _name, (_res, _args) in _SIGS.items():

@@ -109,3 +109,28 @@ class BlockPool:
         out = np.zeros(max(total, 1), dtype=np.int32)
         check(lib.pkv_build_slot_mapping(self._h, _ptr(s), _ptr(st), _ptr(c), len(s), _ptr(out)))
         return out[:total].copy()
+
+    # ---- prefix cache ----
+    def prefix_insert(self, seq: int, tokens) -> int:
+        """Register seq's full blocks under the prefixes of ``tokens``; returns how many."""
+        t = _i32(tokens)
+        n = C.c_int32()
+        check(lib.pkv_prefix_insert(self._h, int(seq), _ptr(t) if t.size else None, int(t.size), C.byref(n)))
+        return n.value
+
+    def prefix_lookup(self, tokens):
+        """New sequence holding the longest registered block-aligned prefix: (seq, n_matched)."""
+        t = _i32(tokens)
+        s, n = C.c_int32(), C.c_int32()
+        check(lib.pkv_prefix_lookup(self._h, _ptr(t) if t.size else None, int(t.size), C.byref(s), C.byref(n)))
+        return s.value, n.value
+
+    def evictable(self) -> np.ndarray:
+        """Registered blocks without references, next to evict first."""
+        got = C.c_int32()
+        buf = np.zeros(max(self.num_blocks, 1), dtype=np.int32)
+        check(lib.pkv_prefix_evictable(self._h, _ptr(buf), buf.size, C.byref(got)))
+        return buf[: got.value].copy()
+
+    def num_registered(self) -> int:
+        return self._out(lib.pkv_prefix_num_registered)

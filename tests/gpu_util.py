@@ -56,6 +56,17 @@ class Mirror:
         self.pool.free(seq)
         self.opool.free_seq(seq)
 
+    def prefix_insert(self, seq: int, tokens) -> int:
+        a, b = self.pool.prefix_insert(seq, tokens), self.opool.prefix_insert(seq, tokens)
+        assert a == b
+        return a
+
+    def prefix_lookup(self, tokens):
+        a, b = self.pool.prefix_lookup(tokens), self.opool.prefix_lookup(tokens)
+        assert a == b
+        assert self.pool.evictable().tolist() == self.opool.lru
+        return a
+
     def append(self, seqs, counts, key_bits: np.ndarray, value_bits: np.ndarray, check_pool: bool = True):
         """Reserve slots on both pools (must agree), copy-on-write copies, then scatter K/V."""
         st, done, slots, cow = self.pool.append_many(seqs, counts)

@@ -171,3 +171,109 @@ def test_full_free_returns_every_block():
         cp.free(s)
     assert sorted(cp.free_list().tolist()) == list(range(64))
     assert all(cp.refcount(b) == 0 for b in range(64))
+
+
+# ---- prefix cache: library against the oracle, every observable after every operation -------
+
+def _prefix_state_equal(cp: BlockPool, op: PoolModel):
+    _state_equal(cp, op)
+    assert cp.evictable().tolist() == op.lru
+    assert cp.num_registered() == op.num_registered()
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4, 5])
+def test_prefix_cache_random_operations_bit_exact(seed):
+    """Random lookups, inserts, appends (with evictions), forks and frees.  Requests follow one of
+    three seeded documents up to a random point and then diverge, so prefixes repeat, hit, miss
+    and get evicted."""
+    rng = np.random.default_rng(500 + seed)
+    N = int(rng.integers(6, 14) if seed < 3 else rng.integers(14, 40))
+    fo = rng.permutation(N)
+    cp, op = BlockPool(N, 16, fo), PoolModel(N, 16, fo)
+    docs = [[int(x) for x in rng.integers(0, 50, 200)] for _ in range(3)]
+
+    def tokens(d, start, n):  # follow document d, or diverge with probability 0.25
+        if rng.random() < 0.25:
+            return [int(x) for x in rng.integers(50, 99, n)]
+        return [docs[d][(start + i) % 200] for i in range(n)]
+
+    live, toks, doc = [], {}, {}
+    hits = evictions = 0
+    for _ in range(1500):
+        r = rng.random()
+        if r < 0.2 or not live:
+            d = int(rng.integers(3))
+            cut = int(rng.integers(0, 70))
+            t = tokens(d, 0, cut) + [int(x) for x in rng.integers(50, 99, int(rng.integers(0, 20)))]
+            a, b = cp.prefix_lookup(t), op.prefix_lookup(t)
+            assert a == b
+            hits += a[1] > 0
+            live.append(a[0])
+            toks[a[0]], doc[a[0]] = t[: a[1]], d
+        elif r < 0.25:
+            p = live[int(rng.integers(len(live)))]
+            a, b = cp.fork(p), op.fork(p)
+            assert a == b
+            live.append(a)
+            toks[a], doc[a] = list(toks[p]), doc[p]
+        elif r < 0.5:
+            s = live.pop(int(rng.integers(len(live))))
+            if rng.random() < 0.7:  # most finished sequences register their blocks first
+                assert cp.prefix_insert(s, toks[s]) == op.prefix_insert(s, toks[s])
+            cp.free(s)
+            op.free_seq(s)
+        elif r < 0.6:
+            s = live[int(rng.integers(len(live)))]
+            assert cp.prefix_insert(s, toks[s]) == op.prefix_insert(s, toks[s])
+        else:
+            s = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, 36))
+            need = op.blocks_needed(s, n)
+            evicts = len(op.free) < need <= len(op.free) + len(op.lru)
+            try:
+                want = op.append(s, n)
+            except OutOfBlocks:
+                with pytest.raises(OutOfBlocksError):
+                    cp.append(s, n)
+            else:
+                slots, cow = cp.append(s, n)
+                assert slots.tolist() == want[0] and cow == want[1]
+                evictions += evicts
+                toks[s] = toks[s] + tokens(doc[s], len(toks[s]), n)
+        _prefix_state_equal(cp, op)
+    assert hits > 20
+    assert evictions >= 5
+
+
+def test_prefix_cache_worked_scenario_library():
+    """The oracle's hand-worked scenario, run on the library."""
+    t40 = list(range(100, 140))
+    p = BlockPool(8, 16)
+    s0 = p.new_seq()
+    p.append(s0, 40)
+    assert p.prefix_insert(s0, t40) == 2
+    assert p.prefix_lookup(t40) == (1, 32)
+    assert p.prefix_lookup(t40[:20] + [999] * 20) == (2, 16)
+    assert p.prefix_lookup([5] + t40[1:]) == (3, 0)
+    for s in (0, 1, 2, 3):
+        p.free(s)
+    assert p.evictable().tolist() == [6, 7] and p.free_list().tolist() == [0, 1, 2, 3, 4, 5]
+    s, n = p.prefix_lookup(t40)
+    assert (s, n) == (0, 32) and p.evictable().tolist() == []
+    p.free(s)
+    assert p.evictable().tolist() == [6, 7]
+    s = p.new_seq()
+    p.append(s, 96)
+    p.append(s, 1)
+    t, _ = p.block_tables([s], 7)
+    assert t.tolist() == [[5, 4, 3, 2, 1, 0, 6]]
+    assert p.free_list().tolist() == [] and p.evictable().tolist() == [7] and p.num_registered() == 1
+    assert p.prefix_lookup(t40)[1] == 16
+
+
+def test_prefix_cache_bad_arguments():
+    p = BlockPool(4, 16)
+    with pytest.raises(PagedKVError):
+        p.prefix_insert(3, [1] * 16)  # unknown sequence
+    s, n = p.prefix_lookup([])
+    assert n == 0 and p.seq_len(s) == 0

@@ -305,3 +305,134 @@ def test_k_tile_order_is_a_permutation_with_contiguous_k_steps(dt, D):
         assert sorted(zip(t.tolist(), ch.tolist())) == sorted(
             (tt, cq * 4 + cr) for tt in range(16) if (tt // 4) % 2 == (t[0] // 4) % 2
             for cq in [ch[0] // 4] for cr in range(4))
+
+
+# ---- prefix cache ([Serving] The Build, Step 8), values worked by hand ----------------------
+
+T40 = list(range(100, 140))
+
+
+def test_prefix_cache_worked_scenario():
+    p = PoolModel(8, 16)  # free list 0..7: allocation takes 7, 6, 5, ...
+    s0 = p.new_seq()
+    p.append(s0, 40)
+    assert p.tables[s0] == [7, 6, 5]
+    assert p.prefix_insert(s0, T40) == 2  # two full blocks: prefixes of 16 and 32 tokens
+    assert p.entries == {tuple(T40[:16]): [7], tuple(T40[:32]): [7, 6]}
+    s1, n = p.prefix_lookup(T40)  # longest block-aligned match: 32 tokens (40 is not aligned)
+    assert (s1, n, p.tables[s1], p.lens[s1]) == (1, 32, [7, 6], 32)
+    assert p.refcnt[7] == 2 and p.refcnt[6] == 2
+    s2, n = p.prefix_lookup(T40[:20] + [999] * 20)  # diverges inside the second block
+    assert (s2, n, p.tables[s2]) == (2, 16, [7])
+    s3, n = p.prefix_lookup([5] + T40[1:])  # diverges in the first token
+    assert (s3, n, p.tables[s3]) == (3, 0, [])
+    assert p.refcnt[7] == 3
+    p.free_seq(s0)  # 7: 3 -> 2, 6: 2 -> 1, 5: 1 -> 0 and unregistered -> free list
+    assert p.free == [0, 1, 2, 3, 4, 5] and p.lru == []
+    p.free_seq(s1)  # 7: 2 -> 1, 6: 1 -> 0, registered -> LRU
+    p.free_seq(s2)  # 7: 1 -> 0 -> LRU behind 6
+    p.free_seq(s3)
+    assert p.lru == [6, 7] and p.free == [0, 1, 2, 3, 4, 5]
+    s, n = p.prefix_lookup(T40)  # a hit on unreferenced blocks takes them off the LRU
+    assert (s, n, p.tables[s], p.lru) == (0, 32, [7, 6], [])
+    p.free_seq(s)  # both reach zero together: they join the LRU deepest first
+    assert p.lru == [6, 7]
+    s = p.new_seq()
+    p.append(s, 96)  # the six free blocks, last first
+    assert p.tables[s] == [5, 4, 3, 2, 1, 0] and p.free == []
+    p.append(s, 1)  # free list empty: evict the LRU head (6), which only the 32-token prefix uses
+    assert p.tables[s] == [5, 4, 3, 2, 1, 0, 6]
+    assert p.entries == {tuple(T40[:16]): [7]} and p.lru == [7] and p.free == []
+    s4, n = p.prefix_lookup(T40)
+    assert n == 16 and p.tables[s4] == [7] and p.lru == []
+    p.append(s, 15)  # fills block 6 (positions 97..111): the next token needs a block, none is left
+    with pytest.raises(OutOfBlocks):
+        p.append(s, 1)
+    p.free_seq(s4)
+    p.append(s, 1)  # now 7 is evictable: the last registered prefix goes
+    assert p.tables[s][-1] == 7 and p.entries == {} and p.lru == []
+
+
+def test_prefix_cache_shares_the_common_first_block():
+    p = PoolModel(8, 16)
+    a = [1] * 16 + [2] * 16
+    b = [1] * 16 + [3] * 16
+    s0, s1 = p.new_seq(), p.new_seq()
+    p.append(s0, 32)
+    p.append(s1, 32)
+    assert p.tables[s0] == [7, 6] and p.tables[s1] == [5, 4]
+    assert p.prefix_insert(s0, a) == 2
+    assert p.prefix_insert(s1, b) == 1  # the 16-token prefix is already held by block 7
+    assert p.entries[tuple(b)] == [7, 4]
+    assert p.prefix_insert(s1, b) == 0  # registering again changes nothing
+    s, n = p.prefix_lookup(b + [9] * 5)
+    assert (n, p.tables[s]) == (32, [7, 4])
+    s2, n = p.prefix_lookup(a)  # the whole request may match
+    assert (n, p.tables[s2]) == (32, [7, 6])
+    p.free_seq(s1)  # 5 was never registered (a duplicate of 7's tokens): straight to the free list
+    assert p.free[-1] == 5 and p.refcnt[4] == 1 and p.lru == []
+    # a block registered under one prefix is not registered under another
+    assert p.prefix_insert(s0, [8] * 32) == 0
+
+
+def test_prefix_cache_capacity_counts_the_lru():
+    p = PoolModel(4, 16)
+    s = p.new_seq()
+    p.append(s, 64)
+    toks = list(range(64))
+    assert p.prefix_insert(s, toks) == 4
+    p.free_seq(s)
+    assert p.free == [] and p.lru == [0, 1, 2, 3]  # deepest block first
+    t = p.new_seq()
+    with pytest.raises(OutOfBlocks):
+        p.append(t, 65)  # five blocks > 0 free + 4 evictable
+    assert p.lru == [0, 1, 2, 3] and p.tables[t] == []  # all-or-nothing
+    p.append(t, 17)  # two blocks: the two deepest registered blocks are evicted
+    assert p.tables[t] == [0, 1] and p.free == [] and p.lru == [2, 3]
+    assert p.entries == {tuple(toks[:16]): [3], tuple(toks[:32]): [3, 2]}
+    p.free_seq(t)  # 0 and 1 are no longer registered: straight to the free list
+    assert p.free == [0, 1] and p.lru == [2, 3]
+    p.append(p.new_seq(), 64)  # free blocks first (1, 0), then the LRU: 2, then 3 (its child gone)
+    assert p.entries == {} and p.lru == [] and p.free == []
+
+
+def test_prefix_cache_random_invariants():
+    rng = np.random.default_rng(11)
+    p = PoolModel(24, 16, rng.permutation(24))
+    live, toks = [], {}
+    for _ in range(400):
+        r = rng.random()
+        if r < 0.2 or not live:
+            t = [int(x) for x in rng.integers(0, 2, int(rng.integers(0, 80)))]
+            s, n = p.prefix_lookup(t)
+            # the match is the longest registered aligned prefix: no longer one is registered
+            assert n % 16 == 0 and tuple(t[:n]) in p.entries or n == 0
+            assert all(tuple(t[:m]) not in p.entries for m in range(n + 16, len(t) // 16 * 16 + 1, 16))
+            live.append(s)
+            toks[s] = t[:n]
+        elif r < 0.35:
+            s = live.pop(int(rng.integers(len(live))))
+            p.free_seq(s)
+            del toks[s]
+        elif r < 0.5:
+            s = live[int(rng.integers(len(live)))]
+            p.prefix_insert(s, toks[s])
+        else:
+            s = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, 30))
+            try:
+                p.append(s, n)
+            except OutOfBlocks:
+                continue
+            toks[s] = toks[s] + [int(x) for x in rng.integers(0, 2, n)]
+        # every block is in exactly one of: referenced, free list, LRU
+        held = {b for b in range(24) if p.refcnt[b] > 0}
+        assert len(held) + len(p.free) + len(p.lru) == 24
+        assert not (held & set(p.free)) and not (held & set(p.lru)) and not (set(p.free) & set(p.lru))
+        reg = {b for blocks in p.entries.values() for b in blocks}
+        assert set(p.lru) <= reg and not (set(p.free) & reg)
+        # every registered prefix's shorter aligned prefixes are registered, with the same blocks
+        for key, blocks in p.entries.items():
+            assert len(key) == 16 * len(blocks)
+            if len(blocks) > 1:
+                assert p.entries[key[:-16]] == blocks[:-1]
