@@ -271,6 +271,24 @@ def test_prefix_cache_worked_scenario_library():
     assert p.prefix_lookup(t40)[1] == 16
 
 
+def test_prefix_cache_eviction_below_library():
+    """The oracle's eviction-below scenario, run on the library."""
+    p = BlockPool(6, 16)
+    x, y = p.new_seq(), p.new_seq()
+    p.append(x, 16)
+    p.append(y, 32)
+    a = [1] * 16
+    assert p.prefix_insert(x, a) == 1 and p.prefix_insert(y, a + [2] * 16) == 1
+    p.free(x)
+    z = p.new_seq()
+    p.append(z, 48)
+    p.append(z, 1)
+    assert p.num_registered() == 0 and p.evictable().tolist() == []
+    assert p.prefix_lookup(a + [2] * 16)[1] == 0
+    p.free(y)
+    assert p.free_list().tolist() == [4, 3]
+
+
 def test_prefix_cache_bad_arguments():
     p = BlockPool(4, 16)
     with pytest.raises(PagedKVError):

@@ -150,10 +150,87 @@ def test_missing_copy_on_write_caught(monkeypatch):
 
 def test_free_order_reversed_caught(monkeypatch):
     def free_reversed(self, seq):
+        idle = []
         for b in reversed(self.tables[seq]):
-            self._release(b)
+            self._release(b, idle)
+        self.lru.extend(reversed(idle))
         del self.tables[seq]
         del self.lens[seq]
 
     monkeypatch.setattr(opool.PoolModel, "free_seq", free_reversed)
     assert _fails(TP.test_free_returns_blocks_in_table_order) >= 1
+
+
+# ---- prefix cache ---------------------------------------------------------------------------
+PREFIX_PINS = (TP.test_prefix_cache_worked_scenario, TP.test_prefix_cache_shares_the_common_first_block,
+               TP.test_prefix_cache_capacity_counts_the_lru, TP.test_prefix_cache_random_invariants,
+               TP.test_prefix_cache_eviction_unregisters_the_blocks_below)
+
+
+def test_prefix_lookup_shortest_first_caught(monkeypatch):
+    def lookup_shortest(self, tokens):
+        s = self.new_seq()
+        bs = self.block_size
+        for n in range(bs, len(tokens) // bs * bs + 1, bs):
+            key = tuple(int(t) for t in tokens[:n])
+            if key in self.entries:
+                for b in self.entries[key]:
+                    if self.refcnt[b] == 0:
+                        self.lru.remove(b)
+                    self.refcnt[b] += 1
+                self.tables[s] = list(self.entries[key])
+                self.lens[s] = n
+                return s, n
+        return s, 0
+
+    monkeypatch.setattr(opool.PoolModel, "prefix_lookup", lookup_shortest)
+    assert _fails(*PREFIX_PINS) >= 1
+
+
+def test_prefix_release_in_table_order_caught(monkeypatch):
+    def free_table_order(self, seq):
+        idle = []
+        for b in self.tables[seq]:
+            self._release(b, idle)
+        self.lru.extend(idle)
+        del self.tables[seq]
+        del self.lens[seq]
+
+    monkeypatch.setattr(opool.PoolModel, "free_seq", free_table_order)
+    assert _fails(*PREFIX_PINS) >= 1
+
+
+def test_prefix_eviction_keeps_descendants_caught(monkeypatch):
+    def evict_only_exact(self):
+        b = self.lru.pop(0)
+        for key in [k for k, blocks in self.entries.items() if blocks[-1] == b]:
+            del self.entries[key]
+        return b
+
+    monkeypatch.setattr(opool.PoolModel, "_evict", evict_only_exact)
+    assert _fails(*PREFIX_PINS) >= 1
+
+
+def test_prefix_hit_without_reference_caught(monkeypatch):
+    orig = opool.PoolModel.prefix_lookup
+
+    def lookup_no_ref(self, tokens):
+        before = list(self.refcnt)
+        lru = list(self.lru)
+        s, n = orig(self, tokens)
+        self.refcnt = before
+        self.lru = lru
+        return s, n
+
+    monkeypatch.setattr(opool.PoolModel, "prefix_lookup", lookup_no_ref)
+    assert _fails(*PREFIX_PINS) >= 1
+
+
+def test_prefix_lru_freed_to_free_list_caught(monkeypatch):
+    def release_always_free(self, b, idle):
+        self.refcnt[b] -= 1
+        if self.refcnt[b] == 0:
+            self.free.append(b)
+
+    monkeypatch.setattr(opool.PoolModel, "_release", release_always_free)
+    assert _fails(*PREFIX_PINS) >= 1

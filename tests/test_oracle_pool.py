@@ -436,3 +436,28 @@ def test_prefix_cache_random_invariants():
             assert len(key) == 16 * len(blocks)
             if len(blocks) > 1:
                 assert p.entries[key[:-16]] == blocks[:-1]
+
+
+def test_prefix_cache_eviction_unregisters_the_blocks_below():
+    """A block registered below another sequence's block: evicting the parent must unregister it
+    even though its own holder still references it."""
+    p = PoolModel(6, 16)  # allocation takes 5, 4, 3, ...
+    x, y = p.new_seq(), p.new_seq()
+    p.append(x, 16)
+    p.append(y, 32)
+    assert p.tables[x] == [5] and p.tables[y] == [4, 3]
+    a = [1] * 16
+    b = a + [2] * 16
+    assert p.prefix_insert(x, a) == 1
+    assert p.prefix_insert(y, b) == 1  # the 16-token prefix is block 5; y's block 3 goes below it
+    assert p.entries == {tuple(a): [5], tuple(b): [5, 3]}
+    p.free_seq(x)  # 5 reaches zero while 3, below it, is still held by y
+    assert p.lru == [5] and p.free == [0, 1, 2]
+    z = p.new_seq()
+    p.append(z, 48)  # 2, 1, 0
+    p.append(z, 1)  # evicts 5: both prefixes go, and 3 is no longer registered
+    assert p.tables[z] == [2, 1, 0, 5] and p.entries == {} and p.lru == []
+    s, n = p.prefix_lookup(b)
+    assert n == 0
+    p.free_seq(y)  # 4 and 3 are unregistered: both to the free list
+    assert p.free == [4, 3] and p.lru == []
