@@ -17,13 +17,16 @@ Python + numpy, floating point in fp64.  Sources, cited by page title and sectio
   (16-token blocks, copy-on-write sharing, preemption).
 * [Notes] "Continuous batching and PagedAttention: serving many users from one GPU"
   (trefon notes): "Fragmentation: PagedAttention" (block table, sharing until
-  divergence), "Prefill gets in the way" (chunked prefill).
+  divergence), "Prefill gets in the way" (chunked prefill), "Memory, not compute, caps
+  the batch" (quantised caches hold more tokens).
+* The FP8 format itself is the OCP 8-bit Floating Point Specification's E4M3 (not on the pages).
 
 Modules:
   pool       host block pool model: LIFO free list, refcounts, fork, copy-on-write,
              all-or-nothing append, free, block tables and slot mapping
   cache      byte-exact model of the paged K/V cache layout, append and block copy
   attention  gather to contiguous K/V and fp64 softmax attention (decode, prefill chunk)
+  fp8        FP8 (OCP E4M3) K/V cache: codec, per-(token, head) quantisation, cache model
   brute      pure-Python per-page / per-token loops for tiny inputs (pins the numpy path)
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against values the pages
@@ -35,4 +38,5 @@ brute force and an independent library routine instead.
 
 from .pool import PoolModel, OutOfBlocks, InvalidOp  # noqa: F401
 from .cache import CacheModel  # noqa: F401
-from . import attention, brute  # noqa: F401
+from .fp8 import Fp8CacheModel  # noqa: F401
+from . import attention, brute, fp8  # noqa: F401

@@ -46,11 +46,14 @@ def gather(cache, table, L: int):
     blocks = np.asarray(table[:nb], dtype=np.int64)
     if nb and (blocks.min() < 0 or blocks.max() >= cache.N):
         raise IndexError("block table entry outside the pool")
-    k = cache.k[blocks]  # [nb][H][bs][D]
-    v = cache.v[blocks]  # [nb][H][D][bs]
+    if cache.dtype == "fp8":  # codes times their per-slot scales, exact in fp64
+        k, v = cache.dequant_kv(blocks)
+    else:
+        k = bits_to_f64(cache.k[blocks], cache.dtype)  # [nb][H][bs][D]
+        v = bits_to_f64(cache.v[blocks], cache.dtype)  # [nb][H][D][bs]
     K = k.transpose(1, 0, 2, 3).reshape(cache.H, nb * bs, cache.D)[:, :L]
     V = v.transpose(1, 0, 3, 2).reshape(cache.H, nb * bs, cache.D)[:, :L]
-    return bits_to_f64(K, cache.dtype), bits_to_f64(V, cache.dtype)
+    return K, V
 
 
 def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float):
@@ -62,10 +65,11 @@ def softmax_attention(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float)
     return w @ V, w
 
 
-def paged_decode(q_bits, cache, tables, lens, scale: float, return_weights: bool = False):
-    """Decode attention for a batch.  q_bits [B][Hq][D]; tables rows of physical block ids;
-    lens[b] >= 1 tokens.  Returns fp64 [B][Hq][D] (and per-(b, h) weights on request)."""
-    q = bits_to_f64(q_bits, cache.dtype)
+def paged_decode(q_bits, cache, tables, lens, scale: float, return_weights: bool = False, q_dtype=None):
+    """Decode attention for a batch.  q_bits [B][Hq][D] (of q_dtype, default the cache's type);
+    tables rows of physical block ids; lens[b] >= 1 tokens.  Returns fp64 [B][Hq][D] (and per-(b, h)
+    weights on request)."""
+    q = bits_to_f64(q_bits, q_dtype or cache.dtype)
     B, Hq, D = q.shape
     if Hq % cache.H:
         raise ValueError("num_q_heads must be a multiple of num_kv_heads")
