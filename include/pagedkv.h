@@ -259,6 +259,65 @@ int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const void* quer
                                   int32_t block_size, int32_t num_blocks, float scale, int32_t dtype,
                                   pkv_stream_t stream);
 
+/* ============================== FP8 K/V cache ============================== */
+/*
+ * An 8-bit cache halves the bytes a bandwidth-bound decode step reads and doubles the tokens that
+ * fit ([Notes] "Continuous batching and PagedAttention: serving many users from one GPU", "Memory,
+ * not compute, caps the batch").  Format: OCP 8-bit floating point E4M3 (bias 7, largest finite
+ * 448, subnormals, no infinities).  Quantisation of each (token, KV head) row x of head_dim values,
+ * K and V separately: amax = max |x_i|; scale s = amax / 448 (fp32, stored per slot);
+ * code_i = E4M3 round-to-nearest-even(x_i * (448 / amax)) (0 when amax = 0); the cached value is
+ * code_i * s.  A scale per slot means an append never rewrites the other tokens of its block.
+ *
+ * Layouts (device, caller-owned):
+ *   k_cache  uint8 [num_blocks][Hkv][16 * head_dim]; within a (block, head) tile, byte (t, d) is at
+ *            ((d / 64) * 2 + (t / 4) % 2) * 512 + ((t / 8) * 4 + t % 4) * 64 + d % 64.
+ *   v_cache  uint8 [num_blocks][Hkv][head_dim][16] (dimension-major).
+ *   k_scale, v_scale  fp32 [num_blocks][Hkv][16].
+ * head_dim 64 or 128, block_size 16.  All four arrays 16-byte aligned.
+ */
+
+/*
+ * paged_cache_append_fp8 - quantise the step's K/V rows and scatter them into their slots.
+ *   key/value  device [T][num_kv_heads][head_dim] of in_dtype (PKV_F32/F16/BF16), token stride
+ *              key_stride/value_stride elements (0 = contiguous).
+ *   slot_mapping  device int32 [T], slot = block * 16 + offset; -1 = skip.  Slots must be unique.
+ * Writes codes and both scales of every valid slot, nothing else.  Bit-exact with the definition.
+ */
+int paged_cache_append_fp8(void* k_cache, void* v_cache, void* k_scale, void* v_scale, const void* key,
+                           const void* value, int64_t key_stride, int64_t value_stride, const int32_t* slot_mapping,
+                           int32_t T, int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                           int32_t in_dtype, pkv_stream_t stream);
+
+/* Copy-on-write copy of whole blocks of an fp8 cache: codes and scales (pairs as in paged_cache_copy_blocks). */
+int paged_cache_copy_blocks_fp8(void* k_cache, void* v_cache, void* k_scale, void* v_scale, const int32_t* src_dst,
+                                int32_t n, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                int32_t num_blocks, pkv_stream_t stream);
+
+/*
+ * paged_attention_decode_fp8 - paged_attention_decode over an fp8 cache: the same arguments and
+ * guarantees (split-K, batch invariance, longest-first order, workspace from
+ * paged_attention_decode_workspace_bytes), plus k_scale/v_scale; `q_dtype` is the query's type
+ * (PKV_BF16 or PKV_F16), out_dtype PKV_F32 or q_dtype.  The result is attention over the values the
+ * cache stands for (code * scale), accumulated in fp32.  _partitions is its first launch alone
+ * (then paged_attention_decode_reduce).
+ */
+int paged_attention_decode_fp8(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                               const void* v_cache, const void* k_scale, const void* v_scale,
+                               const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int32_t max_blocks_per_seq, int32_t num_blocks, int32_t max_context_len, float scale,
+                               int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t q_dtype,
+                               const int32_t* host_context_lens, pkv_stream_t stream);
+int paged_attention_decode_fp8_partitions(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                          const void* v_cache, const void* k_scale, const void* v_scale,
+                                          const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                          int32_t max_context_len, float scale, int32_t partition_size,
+                                          void* workspace, size_t workspace_bytes, int32_t q_dtype,
+                                          const int32_t* host_context_lens, pkv_stream_t stream);
+
 /* ============================== host block pool ============================== */
 /*
  * [Serving] Step 4: a pool of physical block ids with a free list; allocation takes the id at the

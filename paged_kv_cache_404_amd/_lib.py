@@ -72,6 +72,14 @@ _SIGS = {
                                                            _i32, _vp, _vp]),
     "paged_attention_prefill_chunk": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                                 _i32, _f32, _i32, _vp]),
+    "paged_cache_append_fp8": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i32, _i32, _i32,
+                                         _i32, _i32, _vp]),
+    "paged_cache_copy_blocks_fp8": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "paged_attention_decode_fp8": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                             _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp]),
+    "paged_attention_decode_fp8_partitions": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                                        _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
+                                                        _i32, _vp, _vp]),
     "pkv_pool_create": (C.c_int, [_i32, _i32, _pi32, C.POINTER(_pool_p)]),
     "pkv_pool_destroy": (None, [_pool_p]),
     "pkv_pool_num_free": (C.c_int, [_pool_p, _pi32]),

@@ -128,3 +128,25 @@ extern "C" int paged_cache_copy_blocks(void* k_cache, void* v_cache, const int32
                      static_cast<uint8_t*>(v_cache), src_dst, block_bytes, num_blocks);
   return check_launch("paged_cache_copy_blocks");
 }
+
+extern "C" int paged_cache_copy_blocks_fp8(void* k_cache, void* v_cache, void* k_scale, void* v_scale,
+                                           const int32_t* src_dst, int32_t n, int32_t num_kv_heads, int32_t head_dim,
+                                           int32_t block_size, int32_t num_blocks, pkv_stream_t stream) {
+  if (n < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PKV_EINVAL, "paged_cache_copy_blocks_fp8: bad sizes");
+  if (n == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_scale || !v_scale || !src_dst)
+    return fail(PKV_EINVAL, "paged_cache_copy_blocks_fp8: NULL pointer");
+  const int64_t code_bytes = static_cast<int64_t>(num_kv_heads) * block_size * head_dim;
+  const int64_t scale_bytes = static_cast<int64_t>(num_kv_heads) * block_size * 4;
+  if (code_bytes % 16 != 0 || scale_bytes % 16 != 0 ||
+      (reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache) |
+       reinterpret_cast<uintptr_t>(k_scale) | reinterpret_cast<uintptr_t>(v_scale)) % 16 != 0)
+    return fail(PKV_EUNSUPPORTED, "paged_cache_copy_blocks_fp8: blocks must be multiples of 16 bytes, arrays aligned");
+  hipStream_t s = as_stream(stream);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n, 2), dim3(256), 0, s, static_cast<uint8_t*>(k_cache),
+                     static_cast<uint8_t*>(v_cache), src_dst, code_bytes, num_blocks);
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n, 2), dim3(64), 0, s, static_cast<uint8_t*>(k_scale),
+                     static_cast<uint8_t*>(v_scale), src_dst, scale_bytes, num_blocks);
+  return check_launch("paged_cache_copy_blocks_fp8");
+}

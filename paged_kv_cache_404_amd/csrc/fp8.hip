@@ -1,0 +1,658 @@
+// FP8 K/V cache: append with quantisation, and paged decode attention over the quantised cache.
+//
+// [Notes] "Continuous batching and PagedAttention: serving many users from one GPU", "Memory, not
+// compute, caps the batch": the cache bounds how many sequences run at once and a quantised cache
+// multiplies the tokens that fit; on a bandwidth-bound decode it also divides the bytes per step.
+// Format: OCP 8-bit floating point E4M3 (bias 7, largest finite 448, subnormals, no infinities),
+// which gfx950 converts in hardware (v_cvt_pk_fp8_f32, v_cvt_scalef32_pk_{bf16,f16}_fp8).
+//
+// Quantisation, per (token, KV head) row x of head_dim values (x widened exactly to fp32):
+//   amax = max |x_i|,  s = amax / 448 (stored),  inv = 448 / amax (0 when amax = 0),
+//   code_i = E4M3 round-to-nearest-even(x_i * inv),  value_i = code_i * s.
+// K and V rows are quantised separately; every (block, head, slot) has its own K and V scale, so an
+// append never touches the other tokens of its block.
+//
+// Layout: K tile of one (block, head) = 16 tokens x D bytes, byte (t, d) at
+//   ((d / 64) * 2 + (t / 4) % 2) * 512 + ((t / 8) * 4 + t % 4) * 64 + d % 64,
+// so that a matrix-core operand load of one token set and 64 dimensions is one 512-byte run per
+// block; V tile = [D][16] bytes (dimension-major); scales fp32 [block][head][slot].
+//
+// Decode (MI355X): the structure of the bf16 kernel (one wave per 32-token step, GQA heads in the
+// MFMA columns, hi/lo weights in the padding rows, lazy rescale, one step of loads in flight).
+// Codes are widened exactly to bf16/fp16 in registers for v_mfma_f32_16x16x32; a lane's 16-byte K
+// load holds dimensions [64p + 16 q4, +16) of one token, split into k-steps 2p and 2p + 1, and the
+// query fragments follow the same dimension order.  Per-token scales enter outside the products:
+// each score is multiplied by its key's scale, and each weight by its value's scale before P.V
+// (the softmax sum uses the unscaled weight).
+#include <algorithm>
+#include <cmath>
+
+#include "device.h"
+
+namespace pkv {
+namespace {
+
+constexpr float kE4M3Max = 448.0f;
+constexpr float kLog2eF8 = 1.4426950408889634f;
+constexpr float kLazyRescaleLog2F8 = 8.0f;
+constexpr int kMaxOrderF8 = 512;
+
+__host__ __device__ __forceinline__ int fp8_k_pos(int t, int d) {
+  return ((d >> 6) * 2 + ((t >> 2) & 1)) * 512 + ((t >> 3) * 4 + (t & 3)) * 64 + (d & 63);
+}
+
+template <int DT>
+__device__ __forceinline__ float in_elem(const uint8_t* row, int i) {
+  if constexpr (DT == PKV_F32) {
+    return reinterpret_cast<const float*>(row)[i];
+  } else if constexpr (DT == PKV_BF16) {
+    return bf16_bits_to_float(reinterpret_cast<const uint16_t*>(row)[i]);
+  } else {
+    return f16_bits_to_float(reinterpret_cast<const uint16_t*>(row)[i]);
+  }
+}
+
+// Four fp32 values -> four E4M3 codes in one dword (byte i = value i), round to nearest even.
+__device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return static_cast<uint32_t>(w);
+}
+
+// R = D / 8 lanes per (token, head) row; lane j quantises dimensions [8j, 8j + 8).
+template <int DT_IN, int D>
+__global__ void __launch_bounds__(256) append_fp8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
+                                                         float* __restrict__ ksc, float* __restrict__ vsc,
+                                                         const uint8_t* __restrict__ key,
+                                                         const uint8_t* __restrict__ value, int64_t key_stride_b,
+                                                         int64_t value_stride_b, const int32_t* __restrict__ slots,
+                                                         int32_t T, int32_t H, int32_t num_blocks) {
+  constexpr int R = D / 8;
+  constexpr int ES = DT_IN == PKV_F32 ? 4 : 2;
+  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t row = gid / R;
+  const int j = static_cast<int>(gid % R);
+  const bool active = row < static_cast<int64_t>(T) * H;
+  const int t = active ? static_cast<int>(row / H) : 0;
+  const int h = active ? static_cast<int>(row % H) : 0;
+  const int slot = active ? slots[t] : -1;
+  const bool ok = slot >= 0 && slot / kBlock < num_blocks;  // -1 = skip; out-of-pool slots are never written
+  float kx[8], vx[8];
+  float ka = 0.f, va = 0.f;
+  const uint8_t* krow = key + t * key_stride_b + (static_cast<int64_t>(h) * D + 8 * j) * ES;
+  const uint8_t* vrow = value + t * value_stride_b + (static_cast<int64_t>(h) * D + 8 * j) * ES;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    kx[i] = ok ? in_elem<DT_IN>(krow, i) : 0.f;
+    vx[i] = ok ? in_elem<DT_IN>(vrow, i) : 0.f;
+    ka = fmaxf(ka, fabsf(kx[i]));
+    va = fmaxf(va, fabsf(vx[i]));
+  }
+  // Row maximum over the row's R lanes (aligned groups inside the wave; every lane takes part).
+#pragma unroll
+  for (int o = R / 2; o > 0; o >>= 1) {
+    ka = fmaxf(ka, __shfl_xor(ka, o));
+    va = fmaxf(va, __shfl_xor(va, o));
+  }
+  if (!ok) return;
+  const float ks = __fdiv_rn(ka, kE4M3Max);
+  const float vs = __fdiv_rn(va, kE4M3Max);
+  const float kinv = ka > 0.f ? __fdiv_rn(kE4M3Max, ka) : 0.f;
+  const float vinv = va > 0.f ? __fdiv_rn(kE4M3Max, va) : 0.f;
+  const int64_t blk = slot / kBlock;
+  const int off = slot % kBlock;
+  const int64_t head = blk * H + h;
+  u32x2 kw;
+  kw[0] = pack4_fp8(kx[0] * kinv, kx[1] * kinv, kx[2] * kinv, kx[3] * kinv);
+  kw[1] = pack4_fp8(kx[4] * kinv, kx[5] * kinv, kx[6] * kinv, kx[7] * kinv);
+  *reinterpret_cast<u32x2*>(kc + head * kBlock * D + fp8_k_pos(off, 8 * j)) = kw;
+  const uint32_t v0 = pack4_fp8(vx[0] * vinv, vx[1] * vinv, vx[2] * vinv, vx[3] * vinv);
+  const uint32_t v1 = pack4_fp8(vx[4] * vinv, vx[5] * vinv, vx[6] * vinv, vx[7] * vinv);
+  uint8_t* vcol = vc + (head * D + 8 * j) * kBlock + off;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    vcol[i * kBlock] = static_cast<uint8_t>(v0 >> (8 * i));
+    vcol[(i + 4) * kBlock] = static_cast<uint8_t>(v1 >> (8 * i));
+  }
+  if (j == 0) {
+    ksc[head * kBlock + off] = ks;
+    vsc[head * kBlock + off] = vs;
+  }
+}
+
+struct Fp8Args {
+  void* out;
+  const void* q;
+  const uint8_t* k;
+  const uint8_t* v;
+  const float* ksc;
+  const float* vsc;
+  const int32_t* tables;
+  const int32_t* lens;
+  float* part_ml;
+  float* part_o;
+  int32_t Hq;
+  int32_t Hkv;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t max_parts;
+  int32_t part_size;
+  float scale_log2;
+  int32_t num_order;
+  int32_t order[kMaxOrderF8];
+};
+
+template <int DT>
+__device__ __forceinline__ f32x4 mfma_f8(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == PKV_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+}
+
+// Two E4M3 codes (the low or high half of w) -> two 16-bit elements of the product type, exact.
+template <int DT, bool HIGH>
+__device__ __forceinline__ uint32_t widen2(uint32_t w) {
+  if constexpr (DT == PKV_BF16) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
+  } else {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HIGH));
+  }
+}
+
+// Eight codes (two dwords) -> one 8-element operand fragment.
+template <int DT>
+__device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1) {
+  return u32x4{widen2<DT, false>(w0), widen2<DT, true>(w0), widen2<DT, false>(w1), widen2<DT, true>(w1)};
+}
+
+__device__ __forceinline__ u32x4 keep_first8(u32x4 v, int n) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t m = (2 * w + 1 < n) ? 0xFFFFFFFFu : ((2 * w < n) ? 0x0000FFFFu : 0u);
+    v[w] &= m;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int clamp_len_f8(const Fp8Args& a, int b) {
+  return min(a.lens[b], min(a.max_parts * a.part_size, a.max_blocks * kBlock));
+}
+__device__ __forceinline__ int clamp_blk_f8(const Fp8Args& a, int blk) { return min(max(blk, 0), a.num_blocks - 1); }
+
+template <int DT_OUT>
+__device__ __forceinline__ void emit_f8(const Fp8Args& a, int b, int hq, int p, int nparts, int d, int D, float m,
+                                        float l, float acc) {
+  if (nparts == 1) {
+    store_from_float<DT_OUT>(a.out, (static_cast<int64_t>(b) * a.Hq + hq) * D + d, acc / l);
+  } else {
+    const int64_t row = (static_cast<int64_t>(b) * a.Hq + hq) * a.max_parts + p;
+    a.part_o[row * D + d] = acc;
+    if (d == 0) {
+      a.part_ml[row * 2] = m;
+      a.part_ml[row * 2 + 1] = l;
+    }
+  }
+}
+
+// grid = (Hkv, B, max_parts); NW waves per partition, wave w takes steps w, w + NW, ...
+template <int DT, int DT_OUT, int D, int G, int NW>
+__global__ void __launch_bounds__(NW * 64) decode_fp8_kernel(Fp8Args a) {
+  static_assert(D == 64 || D == 128, "head_dim");
+  constexpr int KP = D / 64;  // 16-byte K loads per token set (two k-steps each)
+  constexpr int KS = D / 32;
+  constexpr int NB = D / 16;
+  constexpr int TILE = kBlock * D;  // bytes of one (block, head) tile
+  constexpr int kTableSteps = 32;
+
+  const int g = blockIdx.x;
+  const int b = a.num_order ? a.order[blockIdx.y] : static_cast<int>(blockIdx.y);
+  const int p = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pstart = p * a.part_size;
+  const int32_t* __restrict__ table = a.tables + static_cast<int64_t>(b) * a.max_blocks;
+  const int tab_first = table[min((pstart >> 4) + lane, a.max_blocks - 1)];
+  const int L = clamp_len_f8(a, b);
+  if (pstart >= L) return;
+  const int pend = min(pstart + a.part_size, L);
+  const int nparts = (L + a.part_size - 1) / a.part_size;
+  const int n16 = lane & 15;
+  const int q4 = lane >> 4;
+  const int nsteps = (pend - pstart + 31) >> 5;
+
+  // Query fragments in the K loads' dimension order: k-step 2p + h holds [64p + 16 q4 + 8h, +8).
+  u32x4 qf[KS];
+  {
+    const uint16_t* qrow =
+        static_cast<const uint16_t*>(a.q) + (static_cast<int64_t>(b) * a.Hq + g * G + min(n16, G - 1)) * D;
+#pragma unroll
+    for (int pp = 0; pp < KP; ++pp) {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        qf[2 * pp + hf] =
+            (n16 < G) ? *reinterpret_cast<const u32x4*>(qrow + 64 * pp + 16 * q4 + 8 * hf) : u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  // Q.K product #s row m holds token 8*(m/4) + m%4 + 4s of block m/8: lane (m = n16, q4) reads
+  // that token's dimensions [64p + 16 q4, +16).  Lane (head n16, q4) then holds the scores of step
+  // tokens 8*q4 .. 8*q4+7 (block q4/2, slots 8*(q4%2) ..), whose scales it loads.
+  const bool k_from_b = n16 >= 8;
+  const int k_in_tile = (n16 & 7) * 64 + q4 * 16;
+  const bool v_from_b = q4 >= 2;
+  const int v_in_tile = n16 * kBlock + (q4 & 1) * 8;
+  const bool s_from_b = q4 >= 2;
+  const int s_in_head = (q4 & 1) * 8;
+
+  f32x4 o[NB];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  for (int c0 = 0; c0 < nsteps; c0 += kTableSteps) {
+    const int cend = min(nsteps, c0 + kTableSteps);
+    int st = c0 + w;
+    if (st >= cend) continue;
+    const int cb0 = (pstart >> 4) + 2 * c0;
+    const int cnb = min(2 * kTableSteps, ((pend + 15) >> 4) - cb0);
+    const int tab = clamp_blk_f8(a, c0 == 0 ? tab_first : table[min(cb0 + lane, a.max_blocks - 1)]);
+
+    u32x4 kraw[2 * KP];
+    u32x2 vraw[NB];
+    f32x4 ksc[2], vsc[2];
+    auto heads = [&](int s, int64_t& hA, int64_t& hB) {
+      const int jj = 2 * (s - c0);
+      const int bA = __builtin_amdgcn_readlane(tab, jj);
+      const int bB = __builtin_amdgcn_readlane(tab, min(jj + 1, cnb - 1));  // a lone last block pairs with itself
+      hA = static_cast<int64_t>(bA) * a.Hkv + g;
+      hB = static_cast<int64_t>(bB) * a.Hkv + g;
+    };
+    auto load_k = [&](int s) {
+      int64_t hA, hB;
+      heads(s, hA, hB);
+      const uint8_t* kp = a.k + (k_from_b ? hB : hA) * TILE + k_in_tile;
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+        for (int pp = 0; pp < KP; ++pp)
+          kraw[ss * KP + pp] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + (pp * 2 + ss) * 512));
+      }
+    };
+    auto load_ks = [&](int s) {
+      int64_t hA, hB;
+      heads(s, hA, hB);
+      const float* sp = a.ksc + (s_from_b ? hB : hA) * kBlock + s_in_head;
+      ksc[0] = *reinterpret_cast<const f32x4*>(sp);
+      ksc[1] = *reinterpret_cast<const f32x4*>(sp + 4);
+    };
+    auto load_v = [&](int s) {
+      int64_t hA, hB;
+      heads(s, hA, hB);
+      const uint8_t* vp = a.v + (v_from_b ? hB : hA) * TILE + v_in_tile;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        vraw[nb] = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(vp + nb * 16 * kBlock));
+    };
+    auto load_vs = [&](int s) {
+      int64_t hA, hB;
+      heads(s, hA, hB);
+      const float* sp = a.vsc + (s_from_b ? hB : hA) * kBlock + s_in_head;
+      vsc[0] = *reinterpret_cast<const f32x4*>(sp);
+      vsc[1] = *reinterpret_cast<const f32x4*>(sp + 4);
+    };
+
+    auto step = [&](int s, const bool prefetch) {
+      const int nvalid = min(32, pend - (pstart + s * 32));
+      // Widen this step's K codes; the K registers are then free for the next step's loads.
+      u32x4 kf[2][KS];
+#pragma unroll
+      for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+        for (int pp = 0; pp < KP; ++pp) {
+          const u32x4 r = kraw[ss * KP + pp];
+          kf[ss][2 * pp] = widen8<DT>(r[0], r[1]);
+          kf[ss][2 * pp + 1] = widen8<DT>(r[2], r[3]);
+        }
+      }
+      if (prefetch) {
+        asm volatile("" ::: "memory");
+        load_k(s + NW);
+        asm volatile("" ::: "memory");
+      }
+      f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        s1 = mfma_f8<DT>(kf[0][ks], qf[ks], s1);
+        s2 = mfma_f8<DT>(kf[1][ks], qf[ks], s2);
+      }
+      const int tb = 8 * q4;
+      float sc[8];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        sc[jj] = (n16 < G && tb + jj < nvalid) ? s1[jj] * (ksc[0][jj] * a.scale_log2) : -INFINITY;
+        sc[4 + jj] = (n16 < G && tb + 4 + jj < nvalid) ? s2[jj] * (ksc[1][jj] * a.scale_log2) : -INFINITY;
+      }
+      if (prefetch) load_ks(s + NW);
+      float bmax = sc[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) bmax = fmaxf(bmax, sc[i]);
+      bmax = group4_max(bmax);
+      const bool need = (n16 < G) && (bmax > m_run + kLazyRescaleLog2F8);
+      if (__any(need)) {
+        const float m_new = need ? bmax : m_run;
+        const float alpha = need ? fast_exp2(m_run - m_new) : 1.0f;
+        l_run *= alpha;
+        m_run = m_new;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float f = __shfl(alpha, (4 * q4 + jj) % G);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) o[nb][jj] *= f;
+        }
+      }
+      float pw[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float pv = (n16 < G) ? fast_exp2(sc[i] - m_run) : 0.f;
+        psum += pv;
+        // the value scale of a token past the context may be stale (NaN): its weight is 0 anyway
+        const float vs = tb + i < nvalid ? vsc[i >> 2][i & 3] : 0.f;
+        pw[i] = pv * vs;
+      }
+      l_run += psum;
+      if (prefetch) load_vs(s + NW);
+      u32x4 hi, lo;
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        hi[wd] = pack2<DT>(pw[2 * wd], pw[2 * wd + 1]);
+        lo[wd] = pack2<DT>(pw[2 * wd] - low_half<DT>(hi[wd]), pw[2 * wd + 1] - high_half<DT>(hi[wd]));
+      }
+      u32x4 pa;
+#pragma unroll
+      for (int wd = 0; wd < 4; ++wd) {
+        const uint32_t lo_src = static_cast<uint32_t>(
+            __builtin_amdgcn_mov_dpp(static_cast<int>(lo[wd]), 0x110 + G, 0xF, 0xF, false));
+        pa[wd] = (n16 < G) ? hi[wd] : ((n16 < 2 * G) ? lo_src : 0u);
+      }
+      u32x4 vf[NB];
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) vf[nb] = widen8<DT>(vraw[nb][0], vraw[nb][1]);
+      if (prefetch) {
+        asm volatile("" ::: "memory");
+        load_v(s + NW);
+        asm volatile("" ::: "memory");
+      }
+      if (nvalid < 32) {
+        // Codes past the context are stale (possibly NaN): zero them, never multiply them.
+        const int keep = min(8, max(0, nvalid - tb));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) vf[nb] = keep_first8(vf[nb], keep);
+      }
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) o[nb] = mfma_f8<DT>(pa, vf[nb], o[nb]);
+    };
+
+    load_k(st);
+    load_ks(st);
+    load_v(st);
+    load_vs(st);
+    for (; st + NW < cend; st += NW) step(st, true);
+    step(st, false);
+  }
+
+  l_run = group4_sum(l_run);
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      if constexpr (G >= 4) {
+        o[nb][jj] += __shfl_down(o[nb][jj], 16 * (G / 4));
+      } else if (jj + G < 4) {
+        o[nb][jj] += o[nb][jj + G];
+      }
+    }
+  }
+  __shared__ float sO[NW][G][D];
+  __shared__ float sM[NW][G];
+  __shared__ float sL[NW][G];
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 4 * q4 + jj;
+      if (r < G) sO[w][r][nb * 16 + n16] = o[nb][jj];
+    }
+  }
+  if (q4 == 0 && n16 < G) {
+    sM[w][n16] = m_run;
+    sL[w][n16] = l_run;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * D; idx += NW * 64) {
+    const int h = idx / D;
+    const int d = idx % D;
+    float M = sM[0][h];
+#pragma unroll
+    for (int ww = 1; ww < NW; ++ww) M = fmaxf(M, sM[ww][h]);
+    float acc = 0.f, lsum = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) {
+      const float f = fast_exp2(sM[ww][h] - M);  // waves without a step hold m = -inf -> 0
+      acc += f * sO[ww][h][d];
+      lsum += f * sL[ww][h];
+    }
+    emit_f8<DT_OUT>(a, b, g * G + h, p, nparts, d, D, M, lsum, acc);
+  }
+}
+
+// Waves per workgroup as in the bf16 kernel: 4 for partitions of up to 512 tokens, 8 above and for
+// the single pass (so the output bits never depend on the rest of the batch); the batch-adaptive
+// single pass applies the 512-token rule to the batch's longest context.
+template <int DT, int DT_OUT, int D, int G>
+void launch_fp8(const Fp8Args& a, int B, bool wide, hipStream_t s) {
+  const dim3 grid(a.Hkv, B, a.max_parts);
+  if (wide)
+    hipLaunchKernelGGL((decode_fp8_kernel<DT, DT_OUT, D, G, 8>), grid, dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_fp8_kernel<DT, DT_OUT, D, G, 4>), grid, dim3(256), 0, s, a);
+}
+
+template <int DT, int DT_OUT, int D>
+void dispatch_fp8_group(const Fp8Args& a, int B, bool wide, hipStream_t s) {
+  switch (a.Hq / a.Hkv) {
+    case 1: launch_fp8<DT, DT_OUT, D, 1>(a, B, wide, s); break;
+    case 2: launch_fp8<DT, DT_OUT, D, 2>(a, B, wide, s); break;
+    case 4: launch_fp8<DT, DT_OUT, D, 4>(a, B, wide, s); break;
+    default: launch_fp8<DT, DT_OUT, D, 8>(a, B, wide, s); break;
+  }
+}
+
+template <int DT, int DT_OUT>
+void dispatch_fp8_dim(const Fp8Args& a, int D, int B, bool wide, hipStream_t s) {
+  if (D == 64)
+    dispatch_fp8_group<DT, DT_OUT, 64>(a, B, wide, s);
+  else
+    dispatch_fp8_group<DT, DT_OUT, 128>(a, B, wide, s);
+}
+
+size_t align256_f8(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+int fp8_partitions(const char* fn, void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                   const void* v_cache, const void* k_scale, const void* v_scale, const int32_t* block_tables,
+                   const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
+                   int32_t max_blocks, int32_t num_blocks, int32_t max_ctx, float scale, int32_t partition_size,
+                   void* workspace, size_t workspace_bytes, int32_t q_dtype, const int32_t* host_lens,
+                   pkv_stream_t stream) {
+  if (q_dtype != PKV_BF16 && q_dtype != PKV_F16)
+    return fail(PKV_EUNSUPPORTED, "%s: query dtype %d (bf16 or fp16)", fn, q_dtype);
+  if (out_dtype != PKV_F32 && out_dtype != q_dtype)
+    return fail(PKV_EINVAL, "%s: out_dtype must be PKV_F32 or the query dtype", fn);
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || max_blocks < 0 || num_blocks <= 0 || max_ctx < 0)
+    return fail(PKV_EINVAL, "%s: bad sizes", fn);
+  if (Hq % Hkv != 0) return fail(PKV_EINVAL, "%s: num_q_heads %d not a multiple of num_kv_heads %d", fn, Hq, Hkv);
+  if (bs != kBlock) return fail(PKV_EUNSUPPORTED, "%s: block_size %d (kernels implement 16)", fn, bs);
+  if (D != 64 && D != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, D);
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PKV_EUNSUPPORTED, "%s: group size %d", fn, G);
+  if (B > 65535 || Hq > 65535) return fail(PKV_EUNSUPPORTED, "%s: batch or head count above 65535", fn);
+  if (partition_size != PKV_SINGLE_PASS_ADAPTIVE && (partition_size < 0 || partition_size % bs != 0))
+    return fail(PKV_EINVAL, "%s: partition_size %d must be 0, -1 or a multiple of block_size", fn, partition_size);
+  if (partition_size > 0 && (max_ctx + static_cast<int64_t>(partition_size) - 1) / partition_size > 65535)
+    return fail(PKV_EUNSUPPORTED, "%s: more than 65535 partitions per sequence", fn);
+  if (static_cast<int64_t>(max_ctx) > static_cast<int64_t>(max_blocks) * bs)
+    return fail(PKV_EINVAL, "%s: max_context_len %d exceeds max_blocks_per_seq * block_size", fn, max_ctx);
+  if (B == 0 || max_ctx == 0) return PKV_OK;
+  if (!out || !query || !k_cache || !v_cache || !k_scale || !v_scale || !block_tables || !context_lens)
+    return fail(PKV_EINVAL, "%s: NULL pointer", fn);
+  int32_t part_size, max_parts;
+  size_t ml_bytes = 0, need = 0;
+  if (partition_size <= 0) {
+    part_size = std::max(kBlock, ((max_ctx + kBlock - 1) / kBlock) * kBlock);
+    max_parts = 1;
+  } else {
+    part_size = partition_size;
+    max_parts = (max_ctx + partition_size - 1) / partition_size;
+    ml_bytes = align256_f8(static_cast<size_t>(B) * Hq * max_parts * 2 * sizeof(float));
+    need = ml_bytes + static_cast<size_t>(B) * Hq * max_parts * D * sizeof(float);
+  }
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(PKV_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, need, workspace_bytes);
+  const uintptr_t al = reinterpret_cast<uintptr_t>(query) | reinterpret_cast<uintptr_t>(k_cache) |
+                       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(k_scale) |
+                       reinterpret_cast<uintptr_t>(v_scale) | reinterpret_cast<uintptr_t>(workspace);
+  if (al % 16 != 0) return fail(PKV_EINVAL, "%s: query, caches, scales and workspace must be 16-byte aligned", fn);
+  Fp8Args a{};
+  a.out = out;
+  a.q = query;
+  a.k = static_cast<const uint8_t*>(k_cache);
+  a.v = static_cast<const uint8_t*>(v_cache);
+  a.ksc = static_cast<const float*>(k_scale);
+  a.vsc = static_cast<const float*>(v_scale);
+  a.tables = block_tables;
+  a.lens = context_lens;
+  a.part_ml = need ? static_cast<float*>(workspace) : nullptr;
+  a.part_o = need ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + ml_bytes) : nullptr;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.max_blocks = max_blocks;
+  a.num_blocks = num_blocks;
+  a.max_parts = max_parts;
+  a.part_size = part_size;
+  a.scale_log2 = scale * kLog2eF8;
+  if (host_lens != nullptr && B <= kMaxOrderF8) {
+    for (int i = 0; i < B; ++i) a.order[i] = i;
+    std::stable_sort(a.order, a.order + B, [&](int32_t x, int32_t y) { return host_lens[x] > host_lens[y]; });
+    a.num_order = B;
+  }
+  const bool wide = partition_size == 0 || part_size > 512;
+  hipStream_t s = as_stream(stream);
+  const bool f32out = out_dtype == PKV_F32;
+  if (q_dtype == PKV_BF16) {
+    if (f32out)
+      dispatch_fp8_dim<PKV_BF16, PKV_F32>(a, D, B, wide, s);
+    else
+      dispatch_fp8_dim<PKV_BF16, PKV_BF16>(a, D, B, wide, s);
+  } else {
+    if (f32out)
+      dispatch_fp8_dim<PKV_F16, PKV_F32>(a, D, B, wide, s);
+    else
+      dispatch_fp8_dim<PKV_F16, PKV_F16>(a, D, B, wide, s);
+  }
+  return check_launch(fn);
+}
+
+}  // namespace
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" int paged_cache_append_fp8(void* k_cache, void* v_cache, void* k_scale, void* v_scale, const void* key,
+                                      const void* value, int64_t key_stride, int64_t value_stride,
+                                      const int32_t* slot_mapping, int32_t T, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t num_blocks, int32_t in_dtype, pkv_stream_t stream) {
+  const char* fn = "paged_cache_append_fp8";
+  if (!valid_dtype(in_dtype)) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, in_dtype);
+  if (T < 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 || num_blocks <= 0)
+    return fail(PKV_EINVAL, "%s: bad sizes", fn);
+  if (block_size != kBlock) return fail(PKV_EUNSUPPORTED, "%s: block_size %d (16 only)", fn, block_size);
+  if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, head_dim);
+  if (T == 0) return PKV_OK;
+  if (!k_cache || !v_cache || !k_scale || !v_scale || !key || !value || !slot_mapping)
+    return fail(PKV_EINVAL, "%s: NULL pointer", fn);
+  const int es = elem_size(in_dtype);
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (key_stride == 0) key_stride = row;
+  if (value_stride == 0) value_stride = row;
+  if (key_stride < row || value_stride < row) return fail(PKV_EINVAL, "%s: token stride below num_kv_heads*head_dim", fn);
+  if ((reinterpret_cast<uintptr_t>(key) | reinterpret_cast<uintptr_t>(value)) % es != 0 ||
+      (reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(k_scale) |
+       reinterpret_cast<uintptr_t>(v_scale)) % 8 != 0)
+    return fail(PKV_EINVAL, "%s: misaligned pointer", fn);
+  const int64_t threads = static_cast<int64_t>(T) * num_kv_heads * (head_dim / 8);
+  const int64_t grid = (threads + 255) / 256;
+  if (grid > INT32_MAX) return fail(PKV_EINVAL, "%s: too many tokens", fn);
+  hipStream_t s = as_stream(stream);
+  uint8_t* kc = static_cast<uint8_t*>(k_cache);
+  uint8_t* vc = static_cast<uint8_t*>(v_cache);
+  float* ks = static_cast<float*>(k_scale);
+  float* vs = static_cast<float*>(v_scale);
+  const uint8_t* kin = static_cast<const uint8_t*>(key);
+  const uint8_t* vin = static_cast<const uint8_t*>(value);
+  const dim3 gr(static_cast<uint32_t>(grid)), bl(256);
+#define PKV_APPEND_FP8(DT, DD)                                                                                    \
+  hipLaunchKernelGGL((append_fp8_kernel<DT, DD>), gr, bl, 0, s, kc, vc, ks, vs, kin, vin, key_stride * es,        \
+                     value_stride * es, slot_mapping, T, num_kv_heads, num_blocks)
+  if (head_dim == 64) {
+    if (in_dtype == PKV_BF16)
+      PKV_APPEND_FP8(PKV_BF16, 64);
+    else if (in_dtype == PKV_F16)
+      PKV_APPEND_FP8(PKV_F16, 64);
+    else
+      PKV_APPEND_FP8(PKV_F32, 64);
+  } else {
+    if (in_dtype == PKV_BF16)
+      PKV_APPEND_FP8(PKV_BF16, 128);
+    else if (in_dtype == PKV_F16)
+      PKV_APPEND_FP8(PKV_F16, 128);
+    else
+      PKV_APPEND_FP8(PKV_F32, 128);
+  }
+#undef PKV_APPEND_FP8
+  return check_launch(fn);
+}
+
+extern "C" int paged_attention_decode_fp8_partitions(
+    void* out, int32_t out_dtype, const void* query, const void* k_cache, const void* v_cache, const void* k_scale,
+    const void* v_scale, const int32_t* block_tables, const int32_t* context_lens, int32_t B, int32_t num_q_heads,
+    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+    int32_t max_context_len, float scale, int32_t partition_size, void* workspace, size_t workspace_bytes,
+    int32_t q_dtype, const int32_t* host_context_lens, pkv_stream_t stream) {
+  return fp8_partitions("paged_attention_decode_fp8_partitions", out, out_dtype, query, k_cache, v_cache, k_scale,
+                        v_scale, block_tables, context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size,
+                        max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size, workspace,
+                        workspace_bytes, q_dtype, host_context_lens, stream);
+}
+
+extern "C" int paged_attention_decode_fp8(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                          const void* v_cache, const void* k_scale, const void* v_scale,
+                                          const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                          int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                          int32_t max_context_len, float scale, int32_t partition_size,
+                                          void* workspace, size_t workspace_bytes, int32_t q_dtype,
+                                          const int32_t* host_context_lens, pkv_stream_t stream) {
+  int st = paged_attention_decode_fp8_partitions(out, out_dtype, query, k_cache, v_cache, k_scale, v_scale,
+                                                 block_tables, context_lens, B, num_q_heads, num_kv_heads, head_dim,
+                                                 block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
+                                                 partition_size, workspace, workspace_bytes, q_dtype,
+                                                 host_context_lens, stream);
+  if (st != PKV_OK) return st;
+  return paged_attention_decode_reduce(out, out_dtype, context_lens, B, num_q_heads, head_dim, max_context_len,
+                                       partition_size, workspace, workspace_bytes, stream);
+}

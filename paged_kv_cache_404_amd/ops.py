@@ -226,3 +226,105 @@ class PreparedAppend:
 
     def __call__(self) -> None:
         check(lib.paged_cache_append(*self.args, self.stream))
+
+
+# ---- FP8 (E4M3) cache: codes uint8 k [N][Hkv][16][D] (tile order inside), v [N][Hkv][D][16];
+# ---- scales fp32 [N][Hkv][16] for K and for V.
+def fp8_cache(num_blocks: int, num_kv_heads: int, head_dim: int, device="cuda"):
+    """Allocate (k, v, k_scale, v_scale) of an fp8 cache, filled with the NaN code / NaN scales."""
+    k = torch.full((num_blocks, num_kv_heads, 16, head_dim), 0x7F, dtype=torch.uint8, device=device)
+    v = torch.full((num_blocks, num_kv_heads, head_dim, 16), 0x7F, dtype=torch.uint8, device=device)
+    ks = torch.full((num_blocks, num_kv_heads, 16), float("nan"), dtype=torch.float32, device=device)
+    vs = torch.full_like(ks, float("nan"))
+    return k, v, ks, vs
+
+
+def _fp8_shapes(k_cache, v_cache, k_scale, v_scale):
+    _dev(k_cache, v_cache, k_scale, v_scale)
+    N, H, bs, D = k_cache.shape
+    if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
+        raise TypeError("fp8 caches are uint8 tensors of E4M3 codes")
+    if tuple(v_cache.shape) != (N, H, D, bs) or tuple(k_scale.shape) != (N, H, bs) or k_scale.shape != v_scale.shape:
+        raise ValueError("fp8 cache shapes: k [N][Hkv][16][D], v [N][Hkv][D][16], scales [N][Hkv][16]")
+    if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32:
+        raise TypeError("fp8 scales are float32")
+    return N, H, bs, D
+
+
+def paged_cache_append_fp8(k_cache, v_cache, k_scale, v_scale, key, value, slot_mapping, stream=None) -> None:
+    """Quantise key/value [T][Hkv][D] (fp32/fp16/bf16) into their slots."""
+    N, H, bs, D = _fp8_shapes(k_cache, v_cache, k_scale, v_scale)
+    _dev(key, value, slot_mapping)
+    if key.dtype != value.dtype:
+        raise TypeError("key and value must share one dtype")
+    if slot_mapping.dtype != torch.int32:
+        raise TypeError("slot_mapping must be int32")
+    T = slot_mapping.numel()
+    if key.shape != (T, H, D) or value.shape != (T, H, D):
+        raise ValueError("key/value must be [T][Hkv][D]")
+    check(lib.paged_cache_append_fp8(k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(),
+                                     key.data_ptr(), value.data_ptr(), 0, 0, slot_mapping.data_ptr(), T, H, D, bs, N,
+                                     dtype_code(key.dtype), _stream(stream)))
+
+
+def paged_cache_copy_blocks_fp8(k_cache, v_cache, k_scale, v_scale, src_dst, stream=None) -> None:
+    N, H, bs, D = _fp8_shapes(k_cache, v_cache, k_scale, v_scale)
+    _dev(src_dst)
+    if src_dst.dtype != torch.int32 or src_dst.dim() != 2 or src_dst.shape[1] != 2:
+        raise ValueError("src_dst must be int32 [n][2]")
+    check(lib.paged_cache_copy_blocks_fp8(k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(),
+                                          v_scale.data_ptr(), src_dst.data_ptr(), src_dst.shape[0], H, D, bs, N,
+                                          _stream(stream)))
+
+
+def _fp8_decode_args(out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, max_context_len,
+                     scale, partition_size, workspace, host_ptr):
+    N, Hkv, bs, D = _fp8_shapes(k_cache, v_cache, k_scale, v_scale)
+    _dev(out, query, block_tables, context_lens)
+    B, Hq, Dq = query.shape
+    if Dq != D or out.shape != query.shape:
+        raise ValueError("query/out must be [B][Hq][head_dim]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise TypeError("block_tables and context_lens must be int32")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_tables must be [B][max_blocks], context_lens [B]")
+    ws_ptr, ws_bytes = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * workspace.element_size())
+    return (out.data_ptr(), dtype_code(out.dtype), query.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            k_scale.data_ptr(), v_scale.data_ptr(), block_tables.data_ptr(), context_lens.data_ptr(), B, Hq, Hkv, D,
+            bs, block_tables.shape[1], N, int(max_context_len), float(scale), int(partition_size), ws_ptr, ws_bytes,
+            dtype_code(query.dtype), host_ptr)
+
+
+def paged_attention_decode_fp8(out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                               max_context_len, scale, partition_size=0, workspace=None, stream=None,
+                               host_context_lens=None) -> None:
+    """Decode attention over an fp8 cache; query bf16/fp16 [B][Hq][D]; out fp32 or the query dtype."""
+    hl, hp = _host_lens_ptr(host_context_lens)
+    args = _fp8_decode_args(out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                            max_context_len, scale, partition_size, workspace, hp)
+    check(lib.paged_attention_decode_fp8(*args, _stream(stream)))
+
+
+class PreparedDecodeFp8:
+    """paged_attention_decode_fp8 with its arguments marshalled once (partitions / reduce separately)."""
+
+    def __init__(self, out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, max_context_len,
+                 scale, partition_size=0, workspace=None, stream=None, host_context_lens=None):
+        self._hl, hp = _host_lens_ptr(host_context_lens)
+        self._keep = (out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, workspace)
+        self.args = _fp8_decode_args(out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                                     max_context_len, scale, partition_size, workspace, hp)
+        B, Hq, D = query.shape
+        ws_ptr, ws_bytes = self.args[19], self.args[20]
+        self.reduce_args = (out.data_ptr(), dtype_code(out.dtype), context_lens.data_ptr(), B, Hq, D,
+                            int(max_context_len), int(partition_size), ws_ptr, ws_bytes)
+        self.stream = _stream(stream)
+
+    def __call__(self) -> None:
+        check(lib.paged_attention_decode_fp8(*self.args, self.stream))
+
+    def partitions(self) -> None:
+        check(lib.paged_attention_decode_fp8_partitions(*self.args, self.stream))
+
+    def reduce(self) -> None:
+        check(lib.paged_attention_decode_reduce(*self.reduce_args, self.stream))
