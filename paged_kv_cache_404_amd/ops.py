@@ -328,3 +328,21 @@ class PreparedDecodeFp8:
 
     def reduce(self) -> None:
         check(lib.paged_attention_decode_reduce(*self.reduce_args, self.stream))
+
+
+class PreparedAppendFp8:
+    """paged_cache_append_fp8 with its arguments marshalled once."""
+
+    def __init__(self, k_cache, v_cache, k_scale, v_scale, key, value, slot_mapping, stream=None):
+        N, H, bs, D = _fp8_shapes(k_cache, v_cache, k_scale, v_scale)
+        _dev(key, value, slot_mapping)
+        T = slot_mapping.numel()
+        if key.shape != (T, H, D) or value.shape != (T, H, D) or slot_mapping.dtype != torch.int32:
+            raise ValueError("key/value must be [T][Hkv][D], slot_mapping int32 [T]")
+        self._keep = (k_cache, v_cache, k_scale, v_scale, key, value, slot_mapping)
+        self.args = (k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(), v_scale.data_ptr(), key.data_ptr(),
+                     value.data_ptr(), 0, 0, slot_mapping.data_ptr(), T, H, D, bs, N, dtype_code(key.dtype))
+        self.stream = _stream(stream)
+
+    def __call__(self) -> None:
+        check(lib.paged_cache_append_fp8(*self.args, self.stream))
