@@ -346,6 +346,102 @@ def measure_fp8(args, dev, bf16_kernel_us):
     }
 
 
+def measure_mixed(args, dev):
+    """The mixed prefix-sharing step: 16 samples forked from a 2,048-token prefix decode one token
+    each (single pass, longest first) and a 512-row chunk is prefilled after 4,096 cached tokens.
+    Attention as one paged_attention_mixed launch against the two separate launches; the step adds
+    the paged_cache_append of its 16 + 512 tokens."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_404_amd import BlockPool, ops
+
+    mw = wl.mixed_step(5, prefix_len=2048)
+    pool = BlockPool(mw.num_blocks, 16, mw.free_order)
+    s0 = pool.new_seq()
+    pool.append(s0, mw.prefix_len)
+    samples = [s0] + [pool.fork(s0) for _ in range(mw.samples - 1)]
+    pf = pool.new_seq()
+    pool.append(pf, mw.ctx_start)
+    st, _, step_slots, cow = pool.append_many(samples + [pf], [1] * mw.samples + [mw.chunk])
+    assert st == 0 and len(cow) == 0
+    dtab, dlens = pool.block_tables(samples, -(-(mw.prefix_len + 1) // 16))
+    ptab, _ = pool.block_tables([pf], -(-(mw.ctx_start + mw.chunk) // 16))
+    cache_bytes = 2 * mw.num_blocks * mw.Hkv * 16 * mw.D * 2
+    R = max(1, math.ceil((1 << 30) / cache_bytes))
+    g = torch.Generator(device=dev)
+    g.manual_seed(55)
+    tdt = torch.bfloat16
+    dt_t, dl_t = torch.from_numpy(dtab).to(dev), torch.from_numpy(dlens).to(dev)
+    pt_t = torch.from_numpy(ptab).to(dev)
+    slots_t = torch.from_numpy(step_slots).to(dev)
+    T = mw.samples + mw.chunk
+    reps = []
+    for r in range(R):
+        k = torch.randn((mw.num_blocks, mw.Hkv, 16, mw.D), generator=g, device=dev).to(tdt)
+        v = torch.randn((mw.num_blocks, mw.Hkv, mw.D, 16), generator=g, device=dev).to(tdt)
+        sk = torch.randn((T, mw.Hkv, mw.D), generator=g, device=dev).to(tdt)
+        sv = torch.randn((T, mw.Hkv, mw.D), generator=g, device=dev).to(tdt)
+        qd = torch.randn((mw.samples, mw.Hq, mw.D), generator=g, device=dev).to(tdt)
+        qp = torch.randn((mw.chunk, mw.Hq, mw.D), generator=g, device=dev).to(tdt)
+        od = torch.empty((mw.samples, mw.Hq, mw.D), dtype=torch.float32, device=dev)
+        op = torch.empty((mw.chunk, mw.Hq, mw.D), dtype=torch.float32, device=dev)
+        app = ops.PreparedAppend(k, v, sk, sv, slots_t)
+        dec = ops.PreparedDecode(od, qd, k, v, dt_t, dl_t, int(dlens.max()), mw.scale, 0, None,
+                                 host_context_lens=dlens)
+        pre = ops.PreparedPrefill(op, qp, k, v, pt_t[0], mw.ctx_start, mw.scale)
+        mix = ops.PreparedMixed(od, qd, dt_t, dl_t, int(dlens.max()), op, qp, pt_t, [mw.ctx_start], [mw.chunk],
+                                k, v, mw.scale, host_dec_lens=dlens)
+        reps.append((app, dec, pre, mix))
+    stream = torch.cuda.current_stream()
+
+    def events(fn, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def separate(i):
+        app, dec, pre, _ = reps[i % R]
+        dec()
+        pre()
+
+    def unified(i):
+        reps[i % R][3]()
+
+    def step_sep(i):
+        reps[i % R][0]()
+        separate(i)
+
+    def step_uni(i):
+        reps[i % R][0]()
+        unified(i)
+
+    n = max(20, args.steps // 4)
+    for fn in (separate, unified):
+        for i in range(5):
+            fn(i)
+    t_sep = events(separate, n)
+    t_uni = events(unified, n)
+    s_sep = events(step_sep, n)
+    s_uni = events(step_uni, n)
+    t_dec = events(lambda i: reps[i % R][1](), n)
+    t_pre = events(lambda i: reps[i % R][2](), n)
+    return {
+        "workload": "mixed_step_16_samples_prefix2048_plus_chunk512_ctx4096_gqa32x8_d128_bf16",
+        "attention_us": {"separate_launches": round(t_sep, 2), "mixed_launch": round(t_uni, 2),
+                         "decode_alone": round(t_dec, 2), "prefill_alone": round(t_pre, 2)},
+        "step_us_with_append": {"separate_launches": round(s_sep, 2), "mixed_launch": round(s_uni, 2)},
+        "mixed_speedup": round(t_sep / t_uni, 3),
+        "replicas": R,
+    }
+
+
 def measure_long(args, dev):
     """The long-context decode: batch 8 at 32,768 tokens (2,048 scattered blocks each), split-K
     over 512-token partitions, fused append; KV + Q bytes per step as in the main line."""
@@ -637,6 +733,7 @@ def main():
         res["long_context"] = measure_long(args, dev)
         res["prefix_cache"] = measure_prefix_cache()
         res["fp8_cache"] = measure_fp8(args, dev, part_us)
+        res["mixed_step"] = measure_mixed(args, dev)
     print(json.dumps(res), flush=True)
 
 

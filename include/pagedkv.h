@@ -259,6 +259,33 @@ int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const void* quer
                                   int32_t block_size, int32_t num_blocks, float scale, int32_t dtype,
                                   pkv_stream_t stream);
 
+/*
+ * paged_attention_mixed - one launch for a continuous-batching step's attention: a decode batch
+ * and up to 16 prefill chunks ([Chapter] "How the scheduler works" and [Notes] "Prefill gets in the
+ * way": a step carries the running sequences' decode tokens and a chunk of a new prompt).  The
+ * decode part is paged_attention_decode with partition_size 0 (single pass); chunk i is
+ * paged_attention_prefill_chunk over its own table row; outputs are bit for bit theirs.  Decode
+ * workgroups are dispatched first, so their cache streaming overlaps the prefill tiles' matrix
+ * work.  Either part may be empty (B_dec = 0 or num_chunks = 0).
+ *   decode:  dec_out [B_dec][Hq][D] (out_dtype), dec_query [B_dec][Hq][D], dec_block_tables
+ *            [B_dec][dec_max_blocks], dec_context_lens [B_dec] (device); dec_max_context_len and
+ *            host_dec_context_lens (NULL or a host copy, for the longest-first order) as in
+ *            paged_attention_decode; B_dec <= 512.
+ *   prefill: chunk i has host_chunk_lens[i] rows at positions host_ctx_starts[i] + r, packed one
+ *            chunk after another in pre_query / pre_out ([sum of lengths][Hq][D]); its block table
+ *            is row i of pre_block_tables [num_chunks][pre_max_blocks] (device); the chunks' K/V
+ *            are already appended.  Starts and lengths are host arrays (they size the grid).
+ *   group size Hq / Hkv must be 4 or 8 (PKV_EUNSUPPORTED otherwise); bf16 or fp16; head_dim 64/128.
+ */
+int paged_attention_mixed(void* dec_out, const void* dec_query, const int32_t* dec_block_tables,
+                          const int32_t* dec_context_lens, int32_t B_dec, int32_t dec_max_blocks,
+                          int32_t dec_max_context_len, const int32_t* host_dec_context_lens, void* pre_out,
+                          const void* pre_query, const int32_t* pre_block_tables, int32_t pre_max_blocks,
+                          const int32_t* host_ctx_starts, const int32_t* host_chunk_lens, int32_t num_chunks,
+                          int32_t out_dtype, const void* k_cache, const void* v_cache, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
+                          int32_t dtype, pkv_stream_t stream);
+
 /* ============================== FP8 K/V cache ============================== */
 /*
  * An 8-bit cache halves the bytes a bandwidth-bound decode step reads and doubles the tokens that

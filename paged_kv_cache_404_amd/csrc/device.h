@@ -66,6 +66,23 @@ __device__ __forceinline__ void store_from_float(void* base, int64_t i, float x)
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+constexpr float kLog2e = 1.4426950408889634f;
+// Lazy rescale threshold (log2 domain): the running maximum moves only when a score exceeds it
+// by more than 2^8, so softmax weights stay <= 256 and rescaling is rare.
+constexpr float kLazyRescaleLog2 = 8.0f;
+
+// One v_mfma_f32_16x16x32_{bf16,f16}: C += A (16x32) . B (32x16), fragments of 8 16-bit elements.
+template <int DT>
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  if constexpr (DT == PKV_BF16) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                   0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
+                                                  0, 0);
+  }
+}
+
 // Two floats -> two 16-bit elements of the matrix-core input type in one 32-bit word (low half =
 // a), round to nearest even: one v_cvt_pk_{bf16,f16}_f32.
 template <int DT>

@@ -154,6 +154,32 @@ def paged_attention_decode_reduce(out, context_lens, max_context_len, partition_
                                             workspace.numel() * workspace.element_size(), _stream(stream)))
 
 
+def _prefill_args(out, query, k_cache, v_cache, block_table, ctx_start, scale):
+    _dev(out, query, k_cache, v_cache, block_table)
+    C, Hq, D = query.shape
+    N, Hkv, bs, Dk = k_cache.shape
+    if Dk != D or tuple(v_cache.shape) != (N, Hkv, D, bs) or out.shape != query.shape:
+        raise ValueError("shape mismatch")
+    if block_table.dtype != torch.int32:
+        raise TypeError("block_table must be int32")
+    if block_table.numel() * bs < ctx_start + C:
+        raise ValueError("block_table too short for ctx_start + C")
+    return (out.data_ptr(), dtype_code(out.dtype), query.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            block_table.data_ptr(), int(ctx_start), C, Hq, Hkv, D, bs, N, float(scale), dtype_code(k_cache.dtype))
+
+
+class PreparedPrefill:
+    """paged_attention_prefill_chunk with its arguments marshalled once."""
+
+    def __init__(self, out, query, k_cache, v_cache, block_table, ctx_start, scale, stream=None):
+        self._keep = (out, query, k_cache, v_cache, block_table)
+        self.args = _prefill_args(out, query, k_cache, v_cache, block_table, ctx_start, scale)
+        self.stream = _stream(stream)
+
+    def __call__(self) -> None:
+        check(lib.paged_attention_prefill_chunk(*self.args, self.stream))
+
+
 def paged_attention_prefill_chunk(out, query, k_cache, v_cache, block_table, ctx_start, scale, stream=None) -> None:
     """query/out [C][Hq][D]; block_table int32 [>= ceil((ctx_start + C) / 16)] of one sequence."""
     _dev(out, query, k_cache, v_cache, block_table)
@@ -346,3 +372,66 @@ class PreparedAppendFp8:
 
     def __call__(self) -> None:
         check(lib.paged_cache_append_fp8(*self.args, self.stream))
+
+
+def _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, pre_out, pre_query, pre_tables,
+                ctx_starts, chunk_lens, k_cache, v_cache, scale, host_dec_lens):
+    N, Hkv, bs, D = k_cache.shape
+    _dev(k_cache, v_cache)
+    dtype = dtype_code(k_cache.dtype)
+    B = 0 if dec_query is None else dec_query.shape[0]
+    S = len(chunk_lens)
+    if B:
+        _dev(dec_out, dec_query, dec_tables, dec_lens)
+        if dec_tables.dtype != torch.int32 or dec_lens.dtype != torch.int32 or dec_tables.shape[0] != B:
+            raise ValueError("decode tables [B][max_blocks] and lens [B] must be int32")
+        Hq = dec_query.shape[1]
+        out_dtype = dtype_code(dec_out.dtype)
+    if S:
+        _dev(pre_out, pre_query, pre_tables)
+        if pre_tables.dtype != torch.int32 or pre_tables.shape[0] != S:
+            raise ValueError("prefill tables must be int32 [num_chunks][max_blocks]")
+        if pre_query.shape[0] != int(sum(chunk_lens)) or pre_out.shape != pre_query.shape:
+            raise ValueError("pre_query / pre_out must hold sum(chunk_lens) rows")
+        Hq = pre_query.shape[1]
+        out_dtype = dtype_code(pre_out.dtype)
+    if not B and not S:
+        return None
+    starts = np.ascontiguousarray(np.asarray(ctx_starts, dtype=np.int32))
+    lens = np.ascontiguousarray(np.asarray(chunk_lens, dtype=np.int32))
+    hl, hp = _host_lens_ptr(host_dec_lens)
+    keep = (starts, lens, hl)
+    args = (dec_out.data_ptr() if B else None, dec_query.data_ptr() if B else None,
+            dec_tables.data_ptr() if B else None, dec_lens.data_ptr() if B else None, B,
+            dec_tables.shape[1] if B else 0, int(dec_max_context_len) if B else 0, hp,
+            pre_out.data_ptr() if S else None, pre_query.data_ptr() if S else None,
+            pre_tables.data_ptr() if S else None, pre_tables.shape[1] if S else 0,
+            starts.ctypes.data if S else None, lens.ctypes.data if S else None, S, out_dtype,
+            k_cache.data_ptr(), v_cache.data_ptr(), Hq, Hkv, D, bs, N, float(scale), dtype)
+    return args, keep
+
+
+def paged_attention_mixed(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, pre_out, pre_query,
+                          pre_tables, ctx_starts, chunk_lens, k_cache, v_cache, scale, stream=None,
+                          host_dec_lens=None) -> None:
+    """One launch: single-pass decode of a batch + causal attention of prefill chunks (rows packed
+    in pre_query/pre_out; chunk i at positions ctx_starts[i] .., table row i of pre_tables)."""
+    r = _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, pre_out, pre_query, pre_tables,
+                    ctx_starts, chunk_lens, k_cache, v_cache, scale, host_dec_lens)
+    if r is None:
+        return
+    args, keep = r
+    check(lib.paged_attention_mixed(*args, _stream(stream)))
+
+
+class PreparedMixed:
+    """paged_attention_mixed with its arguments marshalled once."""
+
+    def __init__(self, *a, stream=None, host_dec_lens=None):
+        self._tensors = a
+        r = _mixed_args(*a, host_dec_lens=host_dec_lens)
+        self.args, self._keep = r
+        self.stream = _stream(stream)
+
+    def __call__(self) -> None:
+        check(lib.paged_attention_mixed(*self.args, self.stream))
