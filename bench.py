@@ -69,8 +69,11 @@ def parse():
 
 
 def source_digest() -> str:
-    p = os.path.join(ROOT, "paged_kv_cache_404_amd", "csrc", "decode.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()
+    """sha256 over the sources the decode kernel is compiled from."""
+    h = hashlib.sha256()
+    for name in ("decode.hip", "decode_part.h", "device.h"):
+        h.update(open(os.path.join(ROOT, "paged_kv_cache_404_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload: str):
@@ -81,7 +84,7 @@ def measured_traffic(workload: str):
     except (OSError, ValueError):
         return None
     entry = rec.get(workload)
-    if not entry or entry.get("decode_hip_sha256") != source_digest():
+    if not entry or entry.get("decode_sources_sha256") != source_digest():
         return None
     return entry.get("hbm_bytes_per_launch")
 
@@ -114,7 +117,7 @@ def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
     except (OSError, ValueError):
         rec = {}
     rec[workload] = {
-        "decode_hip_sha256": source_digest(),
+        "decode_sources_sha256": source_digest(),
         "hbm_bytes_per_launch": round(hbm),
         "fetch_kib_per_dispatch": round(f_dec, 1),
         "write_kib_per_dispatch": round(w_dec, 1),
