@@ -62,6 +62,9 @@ def parse():
     mode.add_argument("--separate", action="store_true",
                     help="time paged_cache_append + paged_attention_decode as two calls instead of the fused "
                          "paged_attention_decode_append")
+    ap.add_argument("--cpu-baseline-only", action="store_true",
+                    help="print the oracle CPU baseline of the workload as one JSON line and exit (no GPU use); "
+                         "the bench runs it in a child process pinned to one BLAS/OpenMP thread")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from two rocprofv3 --pmc counter_collection.csv files "
                          "(FETCH_SIZE run, WRITE_SIZE run) of this script, then exit")
@@ -219,6 +222,173 @@ def cpu_baseline_prefill(ctx, Hq, Hkv, D, scale, seconds):
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {R} of 512 chunk rows after {ctx} cached tokens, numpy fp64, {el:.1f} s"}
+
+
+def trace_partition_size(B: int, Hkv: int, max_len: int) -> int:
+    """Partition size of one trace step: 512-token partitions + reduce (fixed positions, so batch
+    invariant).  Measured on this trace against single pass (40 % of peak), 1024 and 2048 (55 %),
+    and single pass only while the batch fills the chip (55 %)."""
+    return 512
+
+
+def measure_trace(dev, choose_ps=trace_partition_size):
+    """The continuous-batching trace: 512 seeded requests (Poisson arrivals, lognormal prompts
+    around 512 tokens, geometric outputs around 200), at most 128 running, a 12,288-block pool,
+    32 q / 8 kv heads of 128, bf16.
+
+    Host phase: the library's pool retires finished requests, admits waiting ones first come first
+    served while the pool holds their tokens plus one, and appends one token per running request
+    (preempting the newest on out-of-blocks); the builders give the step's tables and lengths.
+    Its wall time is the host time.  Device phase: every step's arrays are uploaded once, then the
+    steps replay back to back: the admitted prompts' K/V (paged_cache_append), then the fused
+    append + decode over the live batch.  An event pair around each part of each step gives its
+    GPU time, so host gaps between steps are not counted."""
+    import collections
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_404_amd import BlockPool, ops
+
+    seed, N, n_req, max_active = 3, 12288, 512, 128
+    Hq, Hkv, D = 32, 8, 128
+    reqs = wl.trace_requests(seed, n=n_req)
+    pool = BlockPool(N, 16, wl.shuffled_free_order(seed, N))
+    waiting = collections.deque(range(n_req))
+    running, seq_of, generated = [], {}, [0] * n_req
+    steps, util = [], []
+    preempted, step = 0, 0
+    t0 = time.perf_counter()
+    while waiting or running:
+        for r in [r for r in running if generated[r] >= reqs[r].output_len]:
+            pool.free(seq_of.pop(r))
+            running.remove(r)
+        admitted = []
+        while waiting and len(running) < max_active and reqs[waiting[0]].arrival_step <= step:
+            r = waiting[0]
+            ntok = reqs[r].prompt_len + generated[r]
+            if pool.num_free() < wl.blocks_for(ntok + 1):
+                break
+            waiting.popleft()
+            s = pool.new_seq()
+            slots, _ = pool.append(s, ntok)
+            admitted.append(slots)
+            seq_of[r] = s
+            running.append(r)
+        if not running:
+            step += 1
+            continue
+        pending = list(running)
+        while pending:
+            status, done, _, _ = pool.append_many([seq_of[r] for r in pending], [1] * len(pending))
+            if status == 0:
+                break
+            victim = running.pop()  # the newest request gives its blocks back and waits again
+            pool.free(seq_of.pop(victim))
+            waiting.appendleft(victim)
+            preempted += 1
+            pending = [r for r in pending[done:] if r != victim]
+        for r in running:
+            generated[r] += 1
+        seqs = [seq_of[r] for r in running]
+        nblk = [pool.seq_num_blocks(s) for s in seqs]
+        tables, lens = pool.block_tables(seqs, max(nblk))
+        util.append(int(lens.sum()) / (16.0 * sum(nblk)))
+        steps.append((tables, lens, np.concatenate(admitted).astype(np.int32) if admitted else None))
+        step += 1
+    host_s = time.perf_counter() - t0
+
+    adm = [a for _, _, a in steps if a is not None]
+    max_adm = max((len(a) for a in adm), default=1)
+    flat_tab = torch.from_numpy(np.concatenate([t.ravel() for t, _, _ in steps])).to(dev)
+    flat_len = torch.from_numpy(np.concatenate([ln for _, ln, _ in steps])).to(dev)
+    flat_adm = torch.from_numpy(np.concatenate(adm)).to(dev) if adm else None
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed)
+    bf = torch.bfloat16
+    kc = torch.randn((N, Hkv, 16, D), generator=g, device=dev).to(bf)
+    vc = torch.randn((N, Hkv, D, 16), generator=g, device=dev).to(bf)
+    src_k = torch.randn((max_adm, Hkv, D), generator=g, device=dev).to(bf)
+    src_v = torch.randn((max_adm, Hkv, D), generator=g, device=dev).to(bf)
+    q = torch.randn((max_active, Hq, D), generator=g, device=dev).to(bf)
+    nk = torch.randn((max_active, Hkv, D), generator=g, device=dev).to(bf)
+    nv = torch.randn((max_active, Hkv, D), generator=g, device=dev).to(bf)
+    out = torch.empty((max_active, Hq, D), dtype=torch.float32, device=dev)
+    max_ctx = max(int(ln.max()) for _, ln, _ in steps)
+    ws = ops.decode_workspace(max_active, Hq, D, max_ctx, 512, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    calls = []
+    to = lo = ao = 0
+    kv_bytes = 0
+    for tables, lens, a in steps:
+        B, mb = tables.shape
+        app = None
+        if a is not None:
+            app = ops.PreparedAppend(kc, vc, src_k[:len(a)], src_v[:len(a)], flat_adm[ao:ao + len(a)])
+            ao += len(a)
+        ps = choose_ps(B, Hkv, int(lens.max()))
+        dec = ops.PreparedDecode(out[:B], q[:B], kc, vc, flat_tab[to:to + B * mb].view(B, mb), flat_len[lo:lo + B],
+                                 int(lens.max()), scale, ps, ws, new_key=nk[:B], new_value=nv[:B],
+                                 host_context_lens=lens)
+        to += B * mb
+        lo += B
+        kv_bytes += int(lens.sum()) * Hkv * 2 * D * 2 + B * Hq * D * 2
+        calls.append((app, dec))
+    stream = torch.cuda.current_stream()
+    for app, dec in calls[:20]:  # warm-up (loads the kernels)
+        if app is not None:
+            app()
+        dec()
+    torch.cuda.synchronize()
+    # A bounded spin kernel first, so that the host enqueues the replay ahead of the GPU and the
+    # events time the device work alone (no launch gaps inside a step).
+    probe = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    probe[0].record(stream)
+    torch.cuda._sleep(1 << 20)
+    probe[1].record(stream)
+    torch.cuda.synchronize()
+    cycles_per_ms = (1 << 20) / max(probe[0].elapsed_time(probe[1]), 1e-3)
+    evs = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in calls]
+    ends = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    torch.cuda._sleep(int(cycles_per_ms * 500))
+    w0 = time.perf_counter()
+    ends[0].record(stream)
+    for (app, dec), (e0, e1, e2) in zip(calls, evs):
+        e0.record(stream)
+        if app is not None:
+            app()
+        e1.record(stream)
+        dec()
+        e2.record(stream)
+    ends[1].record(stream)
+    enqueue_ms = (time.perf_counter() - w0) * 1e3
+    torch.cuda.synchronize()
+    total_ms = ends[0].elapsed_time(ends[1])
+    adm_us = sum(e0.elapsed_time(e1) for e0, e1, _ in evs) * 1e3
+    dec_us = sum(e1.elapsed_time(e2) for _, e1, e2 in evs) * 1e3
+    seq_steps = sum(len(ln) for _, ln, _ in steps)
+    gbs = kv_bytes / (dec_us * 1e-6) / 1e9
+    return {
+        "workload": f"trace_{n_req}_requests_max{max_active}_pool{N}_gqa{Hq}x{Hkv}_d{D}_bf16",
+        "steps": len(steps),
+        "seq_steps": seq_steps,
+        "max_running": max(len(ln) for _, ln, _ in steps),
+        "max_context": max_ctx,
+        "preemptions": preempted,
+        "prompt_tokens_appended": int(sum(len(a) for a in adm)),
+        "decode_call": "paged_attention_decode_append, 512-token partitions + reduce",
+        "gpu_ms": {"decode_steps": round(dec_us / 1e3, 3), "prompt_appends": round(adm_us / 1e3, 3)},
+        "decode_kv_plus_q_bytes": kv_bytes,
+        "decode_gbs": round(gbs, 1),
+        "decode_pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "seqs_steps_per_s_gpu": round(seq_steps / ((dec_us + adm_us) * 1e-6), 1),
+        "host_us_per_step": round(host_s / len(steps) * 1e6, 1),
+        "host_note": "pool, scheduler and builders through the Python binding, measured apart from the GPU replay",
+        "pool_utilisation": {"mean": round(float(np.mean(util)), 5), "min": round(float(np.min(util)), 5)},
+        "replay_gpu_ms": round(total_ms, 3),
+        "replay_enqueue_ms": round(enqueue_ms, 2),
+    }
 
 
 def measure_prefix_cache():
@@ -543,10 +713,42 @@ def cpu_baseline(w, seconds: float):
     }
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_one_core(args):
+    """The same oracle sample in a child process with one BLAS/OpenMP thread (half the time budget)."""
+    import subprocess
+
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1",
+               BLIS_NUM_THREADS="1", HIP_VISIBLE_DEVICES="")
+    cmd = [sys.executable, os.path.abspath(__file__), "--cpu-baseline-only", "--workload", args.workload,
+           "--cpu-seconds", str(args.cpu_seconds / 2)]
+    try:
+        p = subprocess.run(cmd, env=env, capture_output=True, text=True, timeout=120 + 4 * args.cpu_seconds)
+        one = json.loads(p.stdout.strip().splitlines()[-1])
+    except (subprocess.SubprocessError, ValueError, IndexError) as e:
+        return {"error": f"single-core run failed: {e}"}
+    return {k: one[k] for k in ("value", "unit", "cores", "sample", "seqs_steps_per_s") if k in one}
+
+
 def main():
     args = parse()
     if args.traffic_from:
         print(json.dumps(write_traffic(args.workload, *args.traffic_from)))
+        return
+    if args.cpu_baseline_only:
+        import workloads as wl
+        w = (wl.llama_decode(2, partition_size=0) if args.workload == "llama"
+             else wl.long_context_decode(4, partition_size=512))
+        print(json.dumps(cpu_baseline(w, args.cpu_seconds)), flush=True)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -654,6 +856,19 @@ def main():
     t_part = avg_us(lambda i: reps[i % R][1].partitions())
     t_red = avg_us(lambda i: reps[i % R][1].reduce())
 
+    # Per-call distribution: an event pair around each of K more steps.
+    pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(pe):
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    per_call = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in pe)
+
+    def quantile(f):
+        return round(per_call[min(len(per_call) - 1, int(f * (len(per_call) - 1) + 0.5))], 3)
+
     kv = w.kv_bytes()
     qb = w.q_bytes()
     step_bytes = kv + qb
@@ -713,6 +928,8 @@ def main():
                   f", {w.partition_size}-token partitions + log-sum-exp reduce")),
         "kernel_us": {"append": round(float(t_app), 3), "decode_partitions": round(part_us, 3),
                       "decode_reduce": round(float(t_red), 3)},
+        "per_call_us": {"median": quantile(0.5), "p10": quantile(0.1), "p90": quantile(0.9), "calls": len(per_call),
+                        "note": "an event pair around each step; the value above is K back-to-back steps"},
         "host_pool_and_builders_us_per_step": round(host_us, 1),
         "device_copy_probe_gbs": round(copy_gbs, 1),
         "roofline": {
@@ -729,6 +946,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline"]["cpu_model"] = cpu_model()
+        res["cpu_baseline"]["single_core"] = cpu_baseline_one_core(args)
     if not args.no_extra and args.workload == "llama":
         del reps
         torch.cuda.empty_cache()
@@ -737,6 +956,7 @@ def main():
         res["prefix_cache"] = measure_prefix_cache()
         res["fp8_cache"] = measure_fp8(args, dev, part_us)
         res["mixed_step"] = measure_mixed(args, dev)
+        res["trace"] = measure_trace(dev)
     print(json.dumps(res), flush=True)
 
 
