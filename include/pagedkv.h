@@ -109,6 +109,30 @@ int paged_cache_copy_blocks(void* k_cache, void* v_cache, const int32_t* src_dst
                             int32_t num_blocks, int32_t dtype, pkv_stream_t stream);
 
 /*
+ * paged_check_inputs - count the device-array values outside the kernels' contract.
+ * [Serving] Step 4 (a sequence's pages in order; token pos at page pos // block_size, offset
+ * pos % block_size) and Step 6 (attention over the stored tokens only).  The kernels clamp such
+ * values (a wrong number, never an out-of-bounds access); this call reports them, on `stream`,
+ * without synchronising.  It reads only inside the arrays it is given.
+ *
+ *   block_tables, context_lens  device int32 [B][max_blocks_per_seq] and [B], as passed to
+ *                  paged_attention_decode (may be NULL when B is 0)
+ *   slot_mapping   device int32 [T], as passed to paged_cache_append (may be NULL when T is 0)
+ *   counts         device int32 [4], written (not accumulated):
+ *                    [0] sequences whose length is outside [1, max_context_len] or longer than
+ *                        max_blocks_per_seq * block_size,
+ *                    [1] block-table entries among the first ceil(length / block_size) of a row
+ *                        (at most the row) that are outside [0, num_blocks),
+ *                    [2] the smallest sequence index counted in [0] or [1], 2147483647 when none,
+ *                    [3] slots that are neither -1 nor in [0, num_blocks * block_size).
+ * Not checked: repeated slots within one call, or a block listed twice.  PKV_EINVAL for negative
+ * sizes, num_blocks or block_size <= 0, or a NULL pointer that a non-zero size needs.
+ */
+int paged_check_inputs(const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                       int32_t max_blocks_per_seq, int32_t max_context_len, const int32_t* slot_mapping, int32_t T,
+                       int32_t num_blocks, int32_t block_size, int32_t* counts, pkv_stream_t stream);
+
+/*
  * paged_attention_decode_workspace_bytes - device workspace paged_attention_decode needs.
  * 0 when partition_size is 0 or -1 (single pass).  Otherwise room for one (max, sum, unnormalised
  * output) partial per (sequence, query head, partition).

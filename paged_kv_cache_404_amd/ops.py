@@ -59,6 +59,31 @@ def paged_cache_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
                                       H, D, bs, N, dtype_code(k_cache.dtype), _stream(stream)))
 
 
+def check_inputs(num_blocks: int, block_tables=None, context_lens=None, max_context_len: int = 0,
+                 slot_mapping=None, block_size: int = 16, stream=None) -> dict:
+    """paged_check_inputs: counts the block-table, length and slot values the kernels would clamp
+    or skip.  This helper waits for the result (the C call itself does not synchronise)."""
+    B = 0 if context_lens is None else context_lens.numel()
+    T = 0 if slot_mapping is None else slot_mapping.numel()
+    tensors = [t for t in (block_tables, context_lens, slot_mapping) if t is not None]
+    if tensors:
+        _dev(*tensors)
+    for t in tensors:
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError("block_tables, context_lens and slot_mapping must be contiguous int32")
+    if B and (block_tables is None or block_tables.dim() != 2 or block_tables.shape[0] != B):
+        raise ValueError("block_tables must be [B][max_blocks_per_seq]")
+    dev = tensors[0].device if tensors else torch.device("cuda")
+    counts = torch.empty(4, dtype=torch.int32, device=dev)
+    check(lib.paged_check_inputs(block_tables.data_ptr() if B else None, context_lens.data_ptr() if B else None, B,
+                                 block_tables.shape[1] if B else 0, int(max_context_len),
+                                 slot_mapping.data_ptr() if T else None, T, int(num_blocks), int(block_size),
+                                 counts.data_ptr(), _stream(stream)))
+    c = counts.cpu().tolist()
+    return {"bad_lengths": c[0], "bad_block_ids": c[1], "first_bad_sequence": None if c[2] == 2147483647 else c[2],
+            "bad_slots": c[3]}
+
+
 def decode_workspace_bytes(B: int, Hq: int, D: int, max_context_len: int, partition_size: int) -> int:
     return int(lib.paged_attention_decode_workspace_bytes(B, Hq, D, max_context_len, partition_size))
 
