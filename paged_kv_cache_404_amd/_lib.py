@@ -83,25 +83,25 @@ _SIGS = {
     "paged_attention_decode_fp8_partitions": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                         _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                                         _i32, _vp, _vp]),
-    "pkv_pool_create": (C.c_int, [_i32, _i32, _pi32, C.POINTER(_pool_p)]),
+    "pkv_pool_create": (C.c_int, [_i32, _i32, _vp, C.POINTER(_pool_p)]),
     "pkv_pool_destroy": (None, [_pool_p]),
-    "pkv_pool_num_free": (C.c_int, [_pool_p, _pi32]),
-    "pkv_pool_free_list": (C.c_int, [_pool_p, _pi32, _i32, _pi32]),
-    "pkv_pool_refcount": (C.c_int, [_pool_p, _i32, _pi32]),
-    "pkv_seq_new": (C.c_int, [_pool_p, _pi32]),
-    "pkv_seq_fork": (C.c_int, [_pool_p, _i32, _pi32]),
-    "pkv_seq_blocks_needed": (C.c_int, [_pool_p, _i32, _i32, _pi32]),
-    "pkv_seq_append": (C.c_int, [_pool_p, _i32, _i32, _pi32, _pi32, _pi32]),
-    "pkv_seqs_append": (C.c_int, [_pool_p, _pi32, _pi32, _i32, _pi32, _pi32, _pi32, _pi32]),
+    "pkv_pool_num_free": (C.c_int, [_pool_p, _vp]),
+    "pkv_pool_free_list": (C.c_int, [_pool_p, _vp, _i32, _vp]),
+    "pkv_pool_refcount": (C.c_int, [_pool_p, _i32, _vp]),
+    "pkv_seq_new": (C.c_int, [_pool_p, _vp]),
+    "pkv_seq_fork": (C.c_int, [_pool_p, _i32, _vp]),
+    "pkv_seq_blocks_needed": (C.c_int, [_pool_p, _i32, _i32, _vp]),
+    "pkv_seq_append": (C.c_int, [_pool_p, _i32, _i32, _vp, _vp, _vp]),
+    "pkv_seqs_append": (C.c_int, [_pool_p, _vp, _vp, _i32, _vp, _vp, _vp, _vp]),
     "pkv_seq_free": (C.c_int, [_pool_p, _i32]),
-    "pkv_seq_len": (C.c_int, [_pool_p, _i32, _pi32]),
-    "pkv_seq_num_blocks": (C.c_int, [_pool_p, _i32, _pi32]),
-    "pkv_build_block_tables": (C.c_int, [_pool_p, _pi32, _i32, _i32, _pi32, _pi32]),
-    "pkv_build_slot_mapping": (C.c_int, [_pool_p, _pi32, _pi32, _pi32, _i32, _pi32]),
-    "pkv_prefix_insert": (C.c_int, [_pool_p, _i32, _pi32, _i32, _pi32]),
-    "pkv_prefix_lookup": (C.c_int, [_pool_p, _pi32, _i32, _pi32, _pi32]),
-    "pkv_prefix_evictable": (C.c_int, [_pool_p, _pi32, _i32, _pi32]),
-    "pkv_prefix_num_registered": (C.c_int, [_pool_p, _pi32]),
+    "pkv_seq_len": (C.c_int, [_pool_p, _i32, _vp]),
+    "pkv_seq_num_blocks": (C.c_int, [_pool_p, _i32, _vp]),
+    "pkv_build_block_tables": (C.c_int, [_pool_p, _vp, _i32, _i32, _vp, _vp]),
+    "pkv_build_slot_mapping": (C.c_int, [_pool_p, _vp, _vp, _vp, _i32, _vp]),
+    "pkv_prefix_insert": (C.c_int, [_pool_p, _i32, _vp, _i32, _vp]),
+    "pkv_prefix_lookup": (C.c_int, [_pool_p, _vp, _i32, _vp, _vp]),
+    "pkv_prefix_evictable": (C.c_int, [_pool_p, _vp, _i32, _vp]),
+    "pkv_prefix_num_registered": (C.c_int, [_pool_p, _vp]),
 }
 
 for _name, (_res, _args) in _SIGS.items():

@@ -11,8 +11,9 @@ import numpy as np
 from ._lib import check, lib
 
 
-def _ptr(a: np.ndarray):
-    return a.ctypes.data_as(C.POINTER(C.c_int32))
+def _ptr(a: np.ndarray) -> int:
+    # the raw address (the C declarations take void*): a quarter of the cost of ctypes.data_as
+    return a.ctypes.data
 
 
 def _i32(a) -> np.ndarray:
@@ -83,25 +84,32 @@ class BlockPool:
         return slots[: int(n)], ([(int(cow[0]), int(cow[1]))] if ncow.value else [])
 
     def append_many(self, seqs, counts):
-        """Batched append in order.  Returns (status, done, slots, cow_pairs [n_cow, 2])."""
+        """Batched append in order.  Returns (status, done, slots, cow_pairs [n_cow, 2]); on an
+        error the slots of the sequences not appended are -1."""
         s, c = _i32(seqs), _i32(counts)
         total = int(c.sum()) if c.size else 0
-        slots = np.zeros(max(total, 1), dtype=np.int32)
-        cow = np.zeros((max(len(s), 1), 2), dtype=np.int32)
+        slots = np.empty(max(total, 1), dtype=np.int32)
+        cow = np.empty((max(len(s), 1), 2), dtype=np.int32)
         ncow, done = C.c_int32(), C.c_int32()
         st = lib.pkv_seqs_append(self._h, _ptr(s), _ptr(c), len(s), _ptr(slots), _ptr(cow), C.byref(ncow),
                                  C.byref(done))
-        return st, done.value, slots[:total], cow[: ncow.value].copy()
+        if st != 0:
+            slots[int(c[: done.value].sum()) if done.value else 0:] = -1
+        return st, done.value, slots[:total], cow[: ncow.value]
 
     def free(self, seq: int) -> None:
         check(lib.pkv_seq_free(self._h, int(seq)))
 
     def block_tables(self, seqs, max_blocks: int):
+        """(tables int32 [n][max_blocks], -1 padded; lens int32 [n]); the C builder writes every entry."""
         s = _i32(seqs)
-        tables = np.zeros((max(len(s), 1), max(int(max_blocks), 1)), dtype=np.int32)
-        lens = np.zeros(max(len(s), 1), dtype=np.int32)
-        check(lib.pkv_build_block_tables(self._h, _ptr(s), len(s), int(max_blocks), _ptr(tables), _ptr(lens)))
-        return tables[: len(s), : int(max_blocks)].copy(), lens[: len(s)].copy()
+        n, mb = len(s), int(max_blocks)
+        tables = np.empty((max(n, 1), max(mb, 1)), dtype=np.int32)
+        lens = np.empty(max(n, 1), dtype=np.int32)
+        check(lib.pkv_build_block_tables(self._h, _ptr(s), n, mb, _ptr(tables), _ptr(lens)))
+        if n >= 1 and mb >= 1:
+            return tables, lens
+        return np.full((n, mb), -1, dtype=np.int32), lens[:n].copy()
 
     def slot_mapping(self, seqs, starts, counts) -> np.ndarray:
         s, st, c = _i32(seqs), _i32(starts), _i32(counts)
