@@ -316,18 +316,19 @@ def measure_trace(dev, choose_ps=trace_partition_size):
     nv = torch.randn((max_active, Hkv, D), generator=g, device=dev).to(bf)
     out = torch.empty((max_active, Hq, D), dtype=torch.float32, device=dev)
     max_ctx = max(int(ln.max()) for _, ln, _ in steps)
-    ws = ops.decode_workspace(max_active, Hq, D, max_ctx, 512, device=dev)
+    step_ps = [choose_ps(len(ln), Hkv, int(ln.max())) for _, ln, _ in steps]
+    ws_bytes = max(ops.decode_workspace_bytes(len(ln), Hq, D, int(ln.max()), ps) for (_, ln, _), ps in zip(steps, step_ps))
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(D)
     calls = []
     to = lo = ao = 0
     kv_bytes = 0
-    for tables, lens, a in steps:
+    for (tables, lens, a), ps in zip(steps, step_ps):
         B, mb = tables.shape
         app = None
         if a is not None:
             app = ops.PreparedAppend(kc, vc, src_k[:len(a)], src_v[:len(a)], flat_adm[ao:ao + len(a)])
             ao += len(a)
-        ps = choose_ps(B, Hkv, int(lens.max()))
         dec = ops.PreparedDecode(out[:B], q[:B], kc, vc, flat_tab[to:to + B * mb].view(B, mb), flat_len[lo:lo + B],
                                  int(lens.max()), scale, ps, ws, new_key=nk[:B], new_value=nv[:B],
                                  host_context_lens=lens)
@@ -388,6 +389,8 @@ def measure_trace(dev, choose_ps=trace_partition_size):
         "pool_utilisation": {"mean": round(float(np.mean(util)), 5), "min": round(float(np.min(util)), 5)},
         "replay_gpu_ms": round(total_ms, 3),
         "replay_enqueue_ms": round(enqueue_ms, 2),
+        # The 500 ms spin covers the enqueue, so no step waited for the host (its events time the GPU only).
+        "enqueue_within_spin": bool(enqueue_ms < 500.0),
     }
 
 
