@@ -667,9 +667,9 @@ def measure_long(args, dev):
     }
 
 
-def cpu_baseline(w, seconds: float):
+def cpu_baseline(w, seconds: float, max_seqs: int = 8):
     """The oracle (numpy fp64 gather + softmax attention) on a bounded sample of the same workload:
-    the first S sequences, inputs drawn on the host with the same generators."""
+    the first S = min(B, max_seqs) sequences, inputs drawn on the host with the same generators."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -677,7 +677,7 @@ def cpu_baseline(w, seconds: float):
     from oracle import CacheModel, PoolModel
     from oracle import attention as oatt
 
-    S = 8 if w.B >= 8 else w.B
+    S = min(w.B, max_seqs)
     lens = w.lens[:S]
     need = sum(wl.blocks_for(int(L)) for L in lens)
     rng = np.random.default_rng(1000 + w.seed)
@@ -967,6 +967,9 @@ def main():
         torch.cuda.empty_cache()
         res["prefill"] = measure_prefill(args, dev)
         res["long_context"] = measure_long(args, dev)
+        if not args.no_cpu_baseline:
+            res["long_context"]["cpu_baseline"] = cpu_baseline(wl.long_context_decode(4), args.cpu_seconds / 2,
+                                                               max_seqs=1)
         res["prefix_cache"] = measure_prefix_cache()
         res["fp8_cache"] = measure_fp8(args, dev, part_us)
         res["mixed_step"] = measure_mixed(args, dev)
