@@ -164,6 +164,24 @@ def paged_attention_decode_newest(out, query, new_key, new_value, k_cache, v_cac
     check(lib.paged_attention_decode_newest(*_fused_args(args, new_key, new_value), _stream(stream)))
 
 
+def paged_attention_decode_append_partitions(out, query, new_key, new_value, k_cache, v_cache, block_tables,
+                                             context_lens, max_context_len, scale, partition_size, workspace,
+                                             stream=None) -> None:
+    """paged_attention_decode_append's split-K as two launches: this, then paged_attention_decode_reduce."""
+    args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                        partition_size, workspace)
+    check(lib.paged_attention_decode_append_partitions(*_fused_args(args, new_key, new_value), _stream(stream)))
+
+
+def paged_attention_decode_newest_partitions(out, query, new_key, new_value, k_cache, v_cache, block_tables,
+                                             context_lens, max_context_len, scale, partition_size, workspace,
+                                             stream=None) -> None:
+    """paged_attention_decode_newest's split-K as two launches: this, then paged_attention_decode_reduce."""
+    args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                        partition_size, workspace)
+    check(lib.paged_attention_decode_newest_partitions(*_fused_args(args, new_key, new_value), _stream(stream)))
+
+
 def paged_attention_decode_partitions(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                                       partition_size, workspace, stream=None) -> None:
     args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
