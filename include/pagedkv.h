@@ -174,9 +174,13 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_he
  *   workspace      device scratch of at least paged_attention_decode_workspace_bytes(...) bytes
  *                  (may be NULL when that is 0); contents on entry do not matter.
  *   host_context_lens  NULL, or a host copy of context_lens (B <= 512 entries): used only to
- *                  hand out the work longest sequence first, which shortens the launch's tail.
- *                  The output does not depend on it (every sequence's arithmetic is the same
- *                  whatever its position in the order).
+ *                  schedule the work, which shortens the launch's tail: sequences are handed out
+ *                  by the size of their last partition (the whole context for a single pass),
+ *                  largest first, and each sequence's partitions are rotated over the grid's
+ *                  partition slices so that its last (ragged) one is dispatched in the final
+ *                  slice.  The output does not depend on it, even when it disagrees with
+ *                  context_lens (every partition's arithmetic is the same wherever it runs, and
+ *                  the rotation covers every partition exactly once).
  * Accumulation is fp32 whatever the input type.
  */
 int paged_attention_decode(void* out, int32_t out_dtype, const void* query, const void* k_cache,

@@ -58,8 +58,8 @@ template <int DT, int DT_OUT, int D>
 __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
   constexpr int E = DT == PKV_F32 ? 4 : 8;  // elements per 16-byte chunk of the K tile
   const int hq = blockIdx.x;
-  const int b = a.num_order ? a.order[blockIdx.y] : static_cast<int>(blockIdx.y);
-  const int p = blockIdx.z;
+  int b, p;
+  work_item(a, blockIdx.y, blockIdx.z, b, p);
   const int G = a.Hq / a.Hkv;
   const int g = hq / G;
   const int L = clamp_len(a, b);
@@ -405,9 +405,25 @@ int partitions_impl(const char* fn, void* out, int32_t out_dtype, const void* qu
   a.k_out = k_out;
   a.v_out = v_out;
   if (host_lens != nullptr && B <= kMaxOrder) {
-    // Longest sequences first (ties by index): the scheduling order only, never the arithmetic.
-    for (int i = 0; i < B; ++i) a.order[i] = i;
-    std::stable_sort(a.order, a.order + B, [&](int32_t x, int32_t y) { return host_lens[x] > host_lens[y]; });
+    // Largest work last-dispatched-least: rows sorted by the size of their sequence's last
+    // partition (the whole context for a single pass), largest first, ties longest first; and
+    // each sequence's partitions rotated so that its last one falls in the grid's last slice.
+    // Full partitions are then all dispatched before the ragged last ones, which go smallest
+    // last.  The schedule only: every partition's arithmetic is the same wherever it runs.
+    int32_t nparts[kMaxOrder], last[kMaxOrder], idx[kMaxOrder];
+    for (int i = 0; i < B; ++i) {
+      const int L = std::max(0, std::min(host_lens[i], max_ctx));
+      nparts[i] = (L + pl.part_size - 1) / pl.part_size;
+      last[i] = L - std::max(0, nparts[i] - 1) * pl.part_size;
+      idx[i] = i;
+    }
+    std::stable_sort(idx, idx + B, [&](int32_t x, int32_t y) {
+      return last[x] != last[y] ? last[x] > last[y] : host_lens[x] > host_lens[y];
+    });
+    for (int i = 0; i < B; ++i) {
+      const uint32_t rot = static_cast<uint32_t>(nparts[idx[i]] % pl.max_parts);
+      a.order[i] = static_cast<uint32_t>(idx[i]) | (rot << 16);
+    }
     a.num_order = B;
   }
   launch_partitions(a, dtype, out_dtype, D, B, partition_size == 0, as_stream(stream));

@@ -30,9 +30,25 @@ struct DecodeArgs {
   const void* new_v;
   void* k_out;        // fused append: the caches, written at that token's slot
   void* v_out;
-  int32_t num_order;  // 0, or B: workgroup row y works on sequence order[y]
-  int32_t order[kMaxOrder];
+  int32_t num_order;  // 0, or B: workgroup row y works on the sequence named by order[y]
+  // Low 16 bits: the sequence; high 16 bits: a rotation r < max_parts of its partitions, grid
+  // slice z working on partition (z + r) % max_parts.  Both only move work between workgroups.
+  uint32_t order[kMaxOrder];
 };
+
+// The (sequence, partition) of grid row y, slice z.  The rotation is a bijection on
+// [0, max_parts), so every partition is computed exactly once whatever the order says.
+__device__ __forceinline__ void work_item(const DecodeArgs& a, int y, int z, int& b, int& p) {
+  if (a.num_order) {
+    const uint32_t o = a.order[y];
+    b = static_cast<int>(o & 0xFFFFu);
+    p = z + static_cast<int>(o >> 16);
+    if (p >= a.max_parts) p -= a.max_parts;
+  } else {
+    b = y;
+    p = z;
+  }
+}
 
 // Zero the 16-bit elements i >= n of an 8-element fragment (n in [0, 8]).
 __device__ __forceinline__ u32x4 keep_first(u32x4 v, int n) {
@@ -97,9 +113,10 @@ constexpr int decode_smem_floats() {
 }
 
 // The body of one workgroup: KV head g, batch row yb (the sequence is order[yb] when a work order
-// is given), partition p.  smem: decode_smem_floats<D, G, NW>() floats of LDS.
+// is given), grid slice pz (partition pz, rotated when a work order is given).  smem:
+// decode_smem_floats<D, G, NW>() floats of LDS.
 template <int DT, int DT_OUT, int D, int G, int NW, bool NEWTOK>
-__device__ __forceinline__ void decode_mfma_part(const DecodeArgs& a, int g, int yb, int p, float* smem) {
+__device__ __forceinline__ void decode_mfma_part(const DecodeArgs& a, int g, int yb, int pz, float* smem) {
   static_assert(D == 64 || D == 128, "head_dim");
   static_assert(G == 1 || G == 2 || G == 4 || G == 8, "group size");
   constexpr int KS = D / 32;        // k-steps of Q.K
@@ -107,7 +124,8 @@ __device__ __forceinline__ void decode_mfma_part(const DecodeArgs& a, int g, int
   constexpr int TILE = kBlock * D;  // elements of one (block, head) tile
   constexpr int kTableSteps = 32;   // steps covered by one block-id load (64 blocks, one per lane)
 
-  const int b = a.num_order ? a.order[yb] : yb;
+  int b, p;
+  work_item(a, yb, pz, b, p);
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int pstart = p * a.part_size;

@@ -162,7 +162,7 @@ extern "C" int paged_attention_mixed(void* dec_out, const void* dec_query, const
   if (has_dec && host_dec_context_lens != nullptr) {
     for (int i = 0; i < B_dec; ++i) a.order[i] = i;
     std::stable_sort(a.order, a.order + B_dec,
-                     [&](int32_t x, int32_t y) { return host_dec_context_lens[x] > host_dec_context_lens[y]; });
+                     [&](uint32_t x, uint32_t y) { return host_dec_context_lens[x] > host_dec_context_lens[y]; });
     a.num_order = B_dec;
   }
   int64_t wg = has_dec ? (static_cast<int64_t>(num_kv_heads) * B_dec + 7) / 8 * 8 : 0;

@@ -186,9 +186,11 @@ def test_copy_on_write_shared_prefix_decode():
     _check(out, ref)
 
 
-@pytest.mark.parametrize("ps", [0, 512])
+@pytest.mark.parametrize("ps", [0, 128, 512])
 def test_longest_first_order_is_bitwise_invariant(ps):
-    """host_context_lens only orders the work: the output bits are the same with or without it."""
+    """host_context_lens only schedules the work (row order, and with partitions the rotation that
+    puts each sequence's last partition in the grid's last slice): the output bits are the same
+    with or without it, and also when the host copy disagrees with the device lengths."""
     w = wl.custom_decode(91, [300, 17, 2048, 1, 900, 513, 64, 1500], 32, 8, 128, "bf16", partition_size=ps)
     t = wl.decode_tensors(w)
     m, seqs = build_decode(w, t)
@@ -196,12 +198,14 @@ def test_longest_first_order_is_bitwise_invariant(ps):
     q = to_dev(t.q, "bf16")
     mcl = int(lens.max())
     outs = []
-    for hl in (None, lens):
+    wrong = [np.ones_like(lens), np.full_like(lens, mcl), lens[::-1].copy(), (lens * 7) % (mcl + 1)]
+    for hl in [None, lens] + wrong:
         out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
         ops.paged_attention_decode(out, q, m.k, m.v, i32(tables), i32(lens), mcl, w.scale, ps,
                                    ops.decode_workspace(w.B, w.Hq, w.D, mcl, ps), host_context_lens=hl)
         torch.cuda.synchronize()
         outs.append(out)
-    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    for o in outs[1:]:
+        assert torch.equal(outs[0].view(torch.int32), o.view(torch.int32))
     ref = oatt.paged_decode(t.q, m.cache, tables, lens, w.scale)
     _check(outs[1], ref)
