@@ -742,6 +742,40 @@ def cpu_baseline_one_core(args):
     return {k: one[k] for k in ("value", "unit", "cores", "sample", "seqs_steps_per_s") if k in one}
 
 
+def measure_read_probe(dev, step_bytes: int) -> dict:
+    """Achievable HBM read bandwidth: paged_probe_stream_read (16-byte nontemporal loads, the decode
+    kernel's load form) over a 4 GiB buffer and over windows of one decode step's byte count,
+    rotated through the 4 GiB so that no window is re-read from the 256 MB last-level cache.  The
+    best of five grid sizes; HIP events on the launch stream around 20 back-to-back launches."""
+    import torch
+
+    from paged_kv_cache_404_amd import ops
+
+    total = 4 << 30
+    buf = torch.empty(total, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, size in (("4GiB", total), ("step_bytes", step_bytes // 16 * 16)):
+        windows = max(1, total // size)
+        best = 0.0
+        for wgs in (2048, 4096, 8192, 16384, 32768):
+            n = 20
+            ops.probe_stream_read(buf, size, sink, wgs)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(n):
+                off = (i % windows) * size
+                ops.probe_stream_read(buf[off:off + size], size, sink, wgs)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            best = max(best, size * n / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        out[name] = round(best, 1)
+    del buf
+    return out
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -891,6 +925,7 @@ def main():
     part_us = float(t_part)
     achieved = step_bytes / (part_us * 1e-6) / 1e9
     traffic = measured_traffic(args.workload)
+    read_probe = measure_read_probe(dev, step_bytes)
 
     # Achievable streaming bandwidth: a plain device copy of 1 GiB.
     src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -946,6 +981,13 @@ def main():
                         "note": "an event pair around each step; the value above is K back-to-back steps"},
         "host_pool_and_builders_us_per_step": round(host_us, 1),  # median of 50 steps
         "device_copy_probe_gbs": round(copy_gbs, 1),
+        "achievable_read": {
+            "probe": "paged_probe_stream_read, 16-byte nontemporal loads, 8 in flight per lane, best of 5 grid sizes",
+            "gbs": read_probe,
+            "pct_of_peak_hbm": {k: round(100 * v / PEAK_HBM_GBS, 2) for k, v in read_probe.items()},
+            "decode_kernel_frac_of_achievable_at_step_bytes": round(achieved / read_probe["step_bytes"], 4),
+            "step_frac_of_achievable_at_step_bytes": round(value / read_probe["step_bytes"], 4),
+        },
         "roofline": {
             "bound": "hbm",
             "kernel": "decode_mfma_kernel" + ("" if args.separate else " (new tokens from the input rows)"

@@ -133,6 +133,21 @@ int paged_check_inputs(const int32_t* block_tables, const int32_t* context_lens,
                        int32_t num_blocks, int32_t block_size, int32_t* counts, pkv_stream_t stream);
 
 /*
+ * paged_probe_stream_read - a measuring aid, not part of the attention path: reads `bytes` of
+ * device memory once with 16-byte nontemporal loads (the decode kernel's load form) over a
+ * grid-stride walk, and writes nothing but (never, in practice) one word to `sink`.  Timing it
+ * gives the HBM read bandwidth a plain streaming kernel achieves, the yardstick beside the 8 TB/s
+ * nameplate for the bandwidth-bound decode ([Notes] "Continuous batching and PagedAttention:
+ * serving many users from one GPU": every sequence's attention reads its own KV cache, so decode
+ * time is set by bytes read).
+ *   buf        device, 16-byte aligned; bytes a multiple of 16.
+ *   sink       device uint32 (one word, caller-owned).
+ *   workgroups grid size in [1, 65536] (256 threads each).
+ * Enqueued on `stream`, no synchronisation.  PKV_EINVAL on a NULL pointer, misalignment or bad size.
+ */
+int paged_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t workgroups, pkv_stream_t stream);
+
+/*
  * paged_attention_decode_workspace_bytes - device workspace paged_attention_decode needs.
  * 0 when partition_size is 0 or -1 (single pass).  Otherwise room for one (max, sum, unnormalised
  * output) partial per (sequence, query head, partition).

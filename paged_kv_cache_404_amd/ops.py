@@ -84,6 +84,14 @@ def check_inputs(num_blocks: int, block_tables=None, context_lens=None, max_cont
             "bad_slots": c[3]}
 
 
+def probe_stream_read(buf, nbytes: int, sink, workgroups: int = 2048, stream=None) -> None:
+    """paged_probe_stream_read over the first nbytes of buf (a measuring aid, no result)."""
+    _dev(buf, sink)
+    if nbytes > buf.numel() * buf.element_size():
+        raise ValueError("nbytes exceeds the buffer")
+    check(lib.paged_probe_stream_read(buf.data_ptr(), int(nbytes), sink.data_ptr(), int(workgroups), _stream(stream)))
+
+
 def decode_workspace_bytes(B: int, Hq: int, D: int, max_context_len: int, partition_size: int) -> int:
     return int(lib.paged_attention_decode_workspace_bytes(B, Hq, D, max_context_len, partition_size))
 

@@ -95,3 +95,18 @@ def test_empty_and_bad_arguments():
                                     "bad_slots": 0}
     with pytest.raises(PagedKVError):
         ops.check_inputs(0, slot_mapping=torch.zeros(3, dtype=torch.int32, device="cuda"))
+
+
+def test_probe_stream_read_reads_without_writing():
+    """The bandwidth probe runs on any 16-byte multiple, checks its arguments on the host, and
+    leaves the sink alone for ordinary data."""
+    import paged_kv_cache_404_amd as pkv
+
+    buf = torch.arange(1 << 18, dtype=torch.int32, device="cuda").view(torch.uint8)  # 1 MiB
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    for nbytes, wgs in ((1 << 20, 2048), (16, 1), ((1 << 20) - 48, 3)):
+        ops.probe_stream_read(buf, nbytes, sink, wgs)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 7
+    assert pkv.lib.paged_probe_stream_read(buf.data_ptr(), 24, sink.data_ptr(), 8, None) == pkv.PKV_EINVAL
+    assert pkv.lib.paged_probe_stream_read(buf.data_ptr(), 32, sink.data_ptr(), 0, None) == pkv.PKV_EINVAL
