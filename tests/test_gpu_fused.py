@@ -190,3 +190,55 @@ def test_fused_rejects_fp32():
         ops.paged_attention_decode_append(out, to_dev(t.q, "f32"), to_dev(t.step_k, "f32"), to_dev(t.step_v, "f32"),
                                           m.k, m.v, i32(tables), i32(lens), int(lens.max()), w.scale)
     assert e.value.status == PKV_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("ps", [0, 512])
+def test_llama_shaped_step_as_benched(ps):
+    """The step bench.py times, at full size: the Llama-3-8B-shaped batch (64 sequences, 32 q / 8 kv
+    heads of 128, bf16, contexts U[128, 2048]) through the fused append + decode with the host copy
+    of the lengths (the benched schedule).  Every output against the fp64 oracle; the cache bytes,
+    the 64 new tokens included, bit for bit."""
+    w = wl.llama_decode(2)
+    t = wl.decode_tensors(w)
+    m, seqs = _prefix(w, t)
+    slots, _ = _reserve(m, seqs)
+    tables, lens = m.tables(seqs, w.max_blocks_per_seq)
+    mcl = int(lens.max())
+    q = to_dev(t.q, w.dtype)
+    sk, sv = to_dev(t.step_k, w.dtype), to_dev(t.step_v, w.dtype)
+    out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
+    ops.paged_attention_decode_append(out, q, sk, sv, m.k, m.v, i32(tables), i32(lens), mcl, w.scale, ps,
+                                      ops.decode_workspace(w.B, w.Hq, w.D, mcl, ps), host_context_lens=lens)
+    torch.cuda.synchronize()
+    m.cache.append(t.step_k, t.step_v, slots)
+    m.assert_cache_bit_exact()
+    ref = oatt.paged_decode(t.q, m.cache, tables, lens, w.scale)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert float(np.abs(got - ref).max()) <= ATOL
+
+
+def test_long_context_step_as_benched_sampled():
+    """The long-context step bench.py times (8 sequences of 32,768 tokens, 512-token partitions +
+    reduce, fused append, host lengths): two sequences against the oracle, the rest finite, and the
+    8 new tokens' cache bytes bit for bit."""
+    w = wl.long_context_decode(4)
+    t = wl.decode_tensors(w)
+    m, seqs = _prefix(w, t)
+    slots, _ = _reserve(m, seqs)
+    tables, lens = m.tables(seqs, w.max_blocks_per_seq)
+    mcl = int(lens.max())
+    q = to_dev(t.q, w.dtype)
+    sk, sv = to_dev(t.step_k, w.dtype), to_dev(t.step_v, w.dtype)
+    out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
+    ops.paged_attention_decode_append(out, q, sk, sv, m.k, m.v, i32(tables), i32(lens), mcl, w.scale,
+                                      w.partition_size, ops.decode_workspace(w.B, w.Hq, w.D, mcl, w.partition_size),
+                                      host_context_lens=lens)
+    torch.cuda.synchronize()
+    m.cache.append(t.step_k, t.step_v, slots)
+    m.assert_cache_bit_exact()
+    sample = [0, 5]
+    ref = oatt.paged_decode(t.q[sample], m.cache, tables[sample], lens[sample], w.scale)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert float(np.abs(got[sample] - ref).max()) <= ATOL
