@@ -388,6 +388,31 @@ int paged_attention_decode_fp8_partitions(void* out, int32_t out_dtype, const vo
                                           void* workspace, size_t workspace_bytes, int32_t q_dtype,
                                           const int32_t* host_context_lens, pkv_stream_t stream);
 
+/*
+ * paged_attention_decode_append_fp8 - paged_attention_decode_append over an fp8 cache: one decode
+ * step with the step's quantising append fused in.  [Serving] Steps 4 and 6 in one launch, over
+ * the quantised cache the [Notes] section "Memory, not compute, caps the batch" asks for: every
+ * sequence's newest token (position context_lens[b] - 1) is quantised exactly as
+ * paged_cache_append_fp8 quantises it (per (token, head): scale = amax / 448, codes = E4M3
+ * nearest-even of x * (448 / amax)), its codes and scales are written into its slot, and
+ * attention over all context_lens[b] tokens uses them.  Output, codes and scales equal, bit for
+ * bit, paged_cache_append_fp8 of those tokens followed by paged_attention_decode_fp8.
+ *   new_key, new_value device [B][num_kv_heads][head_dim] of q_dtype (bf16 or fp16), 16-byte aligned.
+ *   k_cache, v_cache, k_scale, v_scale  device, written at the B new slots' blocks only (each
+ *                  such block's code tiles and scale rows are stored back whole, the other slots
+ *                  with the bytes they held).
+ *   Other arguments as paged_attention_decode_fp8.  The slots must be private to their sequences
+ *   (copy-on-write copies done first) and distinct.
+ */
+int paged_attention_decode_append_fp8(void* out, int32_t out_dtype, const void* query, const void* new_key,
+                                      const void* new_value, void* k_cache, void* v_cache, void* k_scale,
+                                      void* v_scale, const int32_t* block_tables, const int32_t* context_lens,
+                                      int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                      int32_t max_context_len, float scale, int32_t partition_size,
+                                      void* workspace, size_t workspace_bytes, int32_t q_dtype,
+                                      const int32_t* host_context_lens, pkv_stream_t stream);
+
 /* ============================== host block pool ============================== */
 /*
  * [Serving] Step 4: a pool of physical block ids with a free list; allocation takes the id at the

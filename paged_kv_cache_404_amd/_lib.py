@@ -84,6 +84,9 @@ _SIGS = {
     "paged_attention_decode_fp8_partitions": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                         _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                                         _i32, _vp, _vp]),
+    "paged_attention_decode_append_fp8": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                                                    _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
+                                                    _i32, _vp, _vp]),
     "pkv_pool_create": (C.c_int, [_i32, _i32, _vp, C.POINTER(_pool_p)]),
     "pkv_pool_destroy": (None, [_pool_p]),
     "pkv_pool_num_free": (C.c_int, [_pool_p, _vp]),

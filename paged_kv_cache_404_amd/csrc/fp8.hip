@@ -138,6 +138,12 @@ struct Fp8Args {
   int32_t max_parts;
   int32_t part_size;
   float scale_log2;
+  const void* new_k;  // fused append: [B][Hkv][D] of the query's type, the token at position L - 1
+  const void* new_v;
+  uint8_t* k_out;     // fused append: the caches and scales, written at that token's slot
+  uint8_t* v_out;
+  float* ksc_out;
+  float* vsc_out;
   int32_t num_order;
   int32_t order[kMaxOrderF8];
 };
@@ -198,8 +204,23 @@ __device__ __forceinline__ void emit_f8(const Fp8Args& a, int b, int hq, int p, 
   }
 }
 
+// Largest magnitude over the 16 lanes of each 16-lane row (every lane takes part).
+__device__ __forceinline__ float row16_max(float x) {
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
 // grid = (Hkv, B, max_parts); NW waves per partition, wave w takes steps w, w + NW, ...
-template <int DT, int DT_OUT, int D, int G, int NW>
+//
+// NEWTOK (fused append): the token at position L - 1 is this step's new token; its K/V come from
+// the input rows new_k / new_v.  The wave that owns the last step of the sequence's last
+// partition quantises them exactly as append_fp8_kernel does (one scale per (token, head):
+// amax / 448, codes RNE of x * (448 / amax)), puts the codes and scales into its operand
+// registers in place of the slot's stale contents, and stores the block's whole K and V code
+// tiles and both scale rows back (every other slot with the bytes it was loaded with).  The last
+// block of a sequence is private to it, so no other workgroup touches that block in the launch.
+template <int DT, int DT_OUT, int D, int G, int NW, bool NEWTOK>
 __global__ void __launch_bounds__(NW * 64) decode_fp8_kernel(Fp8Args a) {
   static_assert(D == 64 || D == 128, "head_dim");
   constexpr int KP = D / 64;  // 16-byte K loads per token set (two k-steps each)
@@ -223,6 +244,40 @@ __global__ void __launch_bounds__(NW * 64) decode_fp8_kernel(Fp8Args a) {
   const int n16 = lane & 15;
   const int q4 = lane >> 4;
   const int nsteps = (pend - pstart + 31) >> 5;
+
+  // Fused append: where the new token sits in the operand registers of its step.  K codes: lanes
+  // n16 == nk_lane (all q4), token set nk_set; V codes and both scales: lanes q4 == nv_q4, byte /
+  // element (L - 1) % 8.  The owner's lanes load the token's input values at kernel start.
+  const int last_st = nsteps - 1;
+  const bool owner = NEWTOK && p == nparts - 1 && w == last_st % NW;
+  const int nu = (L - 1) - (pstart + last_st * 32);  // index of the new token inside its step
+  const bool nin_b = (nu >> 4) != 0;                // in the step's second block
+  const int ntt = (L - 1) & 15;                     // offset inside its block
+  const int nk_lane = (nin_b ? 8 : 0) + (ntt >> 3) * 4 + (ntt & 3);
+  const int nk_set = (ntt >> 2) & 1;
+  const int nv_q4 = (nin_b ? 2 : 0) + (ntt >> 3);
+  u32x4 nk[2 * KP];    // lane (nk_lane, q4): dims [64 pp + 16 q4, +16) as two 8-element pieces
+  uint32_t nvx[NB];   // lane (n16, nv_q4): dim 16 nb + n16
+#pragma unroll
+  for (int i = 0; i < 2 * KP; ++i) nk[i] = u32x4{0, 0, 0, 0};
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) nvx[nb] = 0;
+  if (owner) {
+    const int64_t row = (static_cast<int64_t>(b) * a.Hkv + g) * D;
+    const uint16_t* krow = static_cast<const uint16_t*>(a.new_k) + row;
+    const uint16_t* vrow = static_cast<const uint16_t*>(a.new_v) + row;
+    if ((lane & 15) == nk_lane) {
+#pragma unroll
+      for (int pp = 0; pp < KP; ++pp) {
+        nk[2 * pp] = *reinterpret_cast<const u32x4*>(krow + 64 * pp + 16 * (lane >> 4));
+        nk[2 * pp + 1] = *reinterpret_cast<const u32x4*>(krow + 64 * pp + 16 * (lane >> 4) + 8);
+      }
+    }
+    if ((lane >> 4) == nv_q4) {
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) nvx[nb] = vrow[nb * 16 + (lane & 15)];
+    }
+  }
 
   // Query fragments in the K loads' dimension order: k-step 2p + h holds [64p + 16 q4 + 8h, +8).
   u32x4 qf[KS];
@@ -308,6 +363,103 @@ __global__ void __launch_bounds__(NW * 64) decode_fp8_kernel(Fp8Args a) {
 
     auto step = [&](int s, const bool prefetch) {
       const int nvalid = min(32, pend - (pstart + s * 32));
+      if (!prefetch && owner && s == last_st) {
+        // The owner's last step (never issued with a successor) holds the new token's block.
+        // The asm operands keep the compiler from waiting for the token's loads any earlier.
+#pragma unroll
+        for (int i = 0; i < 2 * KP; ++i) asm volatile("" : "+v"(nk[i]));
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) asm volatile("" : "+v"(nvx[nb]));
+        // K: amax over the token's D values (4 lanes x 16 KP), then codes of x * (448 / amax).
+        float kx[2 * KP][8];
+        float ka = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2 * KP; ++i) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t bits = (nk[i][e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            kx[i][e] = DT == PKV_BF16 ? bf16_bits_to_float(bits) : f16_bits_to_float(bits);
+            ka = fmaxf(ka, fabsf(kx[i][e]));
+          }
+        }
+        // Full over the token's 4 lanes, then from its lane to all (the scale goes to lanes of
+        // every row: those of the q4 group that holds the token's scores).
+        ka = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, group4_max(ka)), nk_lane));
+        const float kscale = __fdiv_rn(ka, kE4M3Max);
+        const float kinv = ka > 0.f ? __fdiv_rn(kE4M3Max, ka) : 0.f;
+        // V: amax over the token's D values (16 lanes x NB).
+        float vx[NB];
+        float va = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+          vx[nb] = DT == PKV_BF16 ? bf16_bits_to_float(nvx[nb]) : f16_bits_to_float(nvx[nb]);
+          va = fmaxf(va, fabsf(vx[nb]));
+        }
+        va = row16_max(va);  // full in the lanes q4 == nv_q4, the only ones that use it
+        const float vscale = __fdiv_rn(va, kE4M3Max);
+        const float vinv = va > 0.f ? __fdiv_rn(kE4M3Max, va) : 0.f;
+        if ((lane & 15) == nk_lane) {
+#pragma unroll
+          for (int pp = 0; pp < KP; ++pp) {
+            u32x4 c;
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+              const float* x = &kx[2 * pp + (wd >> 1)][4 * (wd & 1)];
+              c[wd] = pack4_fp8(x[0] * kinv, x[1] * kinv, x[2] * kinv, x[3] * kinv);
+            }
+            if (nk_set)
+              kraw[KP + pp] = c;
+            else
+              kraw[pp] = c;
+          }
+        }
+        if (q4 == nv_q4) {
+          const int e = ntt & 7;
+          const uint32_t sh = 8 * (e & 3);
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+            const uint32_t code = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(vx[nb] * vinv, 0.f, 0, false)) &
+                                  0xFFu;
+#pragma unroll
+            for (int wd = 0; wd < 2; ++wd) {
+              if (wd == (e >> 2)) vraw[nb][wd] = (vraw[nb][wd] & ~(0xFFu << sh)) | (code << sh);
+            }
+          }
+#pragma unroll
+          for (int jj = 0; jj < 8; ++jj) {
+            if (jj == e) {
+              ksc[jj >> 2][jj & 3] = kscale;
+              vsc[jj >> 2][jj & 3] = vscale;
+            }
+          }
+        }
+        // Store the block's tiles and scale rows back with the loads' own lane patterns (every
+        // line written whole).
+        int64_t hA, hB;
+        heads(s, hA, hB);
+        const int64_t hN = nin_b ? hB : hA;
+        if (k_from_b == nin_b) {
+          uint8_t* kp = a.k_out + hN * TILE + k_in_tile;
+#pragma unroll
+          for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+            for (int pp = 0; pp < KP; ++pp) *reinterpret_cast<u32x4*>(kp + (pp * 2 + ss) * 512) = kraw[ss * KP + pp];
+          }
+        }
+        if (v_from_b == nin_b) {
+          uint8_t* vp = a.v_out + hN * TILE + v_in_tile;
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<u32x2*>(vp + nb * 16 * kBlock) = vraw[nb];
+        }
+        if (s_from_b == nin_b && n16 == 0) {
+          float* kso = a.ksc_out + hN * kBlock + s_in_head;
+          float* vso = a.vsc_out + hN * kBlock + s_in_head;
+          *reinterpret_cast<f32x4*>(kso) = ksc[0];
+          *reinterpret_cast<f32x4*>(kso + 4) = ksc[1];
+          *reinterpret_cast<f32x4*>(vso) = vsc[0];
+          *reinterpret_cast<f32x4*>(vso + 4) = vsc[1];
+        }
+      }
       // Widen this step's K codes; the K registers are then free for the next step's loads.
       u32x4 kf[2][KS];
 #pragma unroll
@@ -457,10 +609,18 @@ __global__ void __launch_bounds__(NW * 64) decode_fp8_kernel(Fp8Args a) {
 template <int DT, int DT_OUT, int D, int G>
 void launch_fp8(const Fp8Args& a, int B, bool wide, hipStream_t s) {
   const dim3 grid(a.Hkv, B, a.max_parts);
-  if (wide)
-    hipLaunchKernelGGL((decode_fp8_kernel<DT, DT_OUT, D, G, 8>), grid, dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_fp8_kernel<DT, DT_OUT, D, G, 4>), grid, dim3(256), 0, s, a);
+  const bool fused = a.new_k != nullptr;
+  if (wide) {
+    if (fused)
+      hipLaunchKernelGGL((decode_fp8_kernel<DT, DT_OUT, D, G, 8, true>), grid, dim3(512), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_fp8_kernel<DT, DT_OUT, D, G, 8, false>), grid, dim3(512), 0, s, a);
+  } else {
+    if (fused)
+      hipLaunchKernelGGL((decode_fp8_kernel<DT, DT_OUT, D, G, 4, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_fp8_kernel<DT, DT_OUT, D, G, 4, false>), grid, dim3(256), 0, s, a);
+  }
 }
 
 template <int DT, int DT_OUT, int D>
@@ -488,7 +648,7 @@ int fp8_partitions(const char* fn, void* out, int32_t out_dtype, const void* que
                    const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
                    int32_t max_blocks, int32_t num_blocks, int32_t max_ctx, float scale, int32_t partition_size,
                    void* workspace, size_t workspace_bytes, int32_t q_dtype, const int32_t* host_lens,
-                   pkv_stream_t stream) {
+                   pkv_stream_t stream, const void* new_k = nullptr, const void* new_v = nullptr) {
   if (q_dtype != PKV_BF16 && q_dtype != PKV_F16)
     return fail(PKV_EUNSUPPORTED, "%s: query dtype %d (bf16 or fp16)", fn, q_dtype);
   if (out_dtype != PKV_F32 && out_dtype != q_dtype)
@@ -527,6 +687,11 @@ int fp8_partitions(const char* fn, void* out, int32_t out_dtype, const void* que
                        reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(k_scale) |
                        reinterpret_cast<uintptr_t>(v_scale) | reinterpret_cast<uintptr_t>(workspace);
   if (al % 16 != 0) return fail(PKV_EINVAL, "%s: query, caches, scales and workspace must be 16-byte aligned", fn);
+  if (new_k != nullptr || new_v != nullptr) {
+    if (!new_k || !new_v) return fail(PKV_EINVAL, "%s: NULL new_key or new_value", fn);
+    if ((reinterpret_cast<uintptr_t>(new_k) | reinterpret_cast<uintptr_t>(new_v)) % 16 != 0)
+      return fail(PKV_EINVAL, "%s: new_key and new_value must be 16-byte aligned", fn);
+  }
   Fp8Args a{};
   a.out = out;
   a.q = query;
@@ -545,6 +710,14 @@ int fp8_partitions(const char* fn, void* out, int32_t out_dtype, const void* que
   a.max_parts = max_parts;
   a.part_size = part_size;
   a.scale_log2 = scale * kLog2eF8;
+  if (new_k != nullptr) {
+    a.new_k = new_k;
+    a.new_v = new_v;
+    a.k_out = const_cast<uint8_t*>(a.k);
+    a.v_out = const_cast<uint8_t*>(a.v);
+    a.ksc_out = const_cast<float*>(a.ksc);
+    a.vsc_out = const_cast<float*>(a.vsc);
+  }
   if (host_lens != nullptr && B <= kMaxOrderF8) {
     for (int i = 0; i < B; ++i) a.order[i] = i;
     std::stable_sort(a.order, a.order + B, [&](int32_t x, int32_t y) { return host_lens[x] > host_lens[y]; });
@@ -652,6 +825,24 @@ extern "C" int paged_attention_decode_fp8(void* out, int32_t out_dtype, const vo
                                                  block_size, max_blocks_per_seq, num_blocks, max_context_len, scale,
                                                  partition_size, workspace, workspace_bytes, q_dtype,
                                                  host_context_lens, stream);
+  if (st != PKV_OK) return st;
+  return paged_attention_decode_reduce(out, out_dtype, context_lens, B, num_q_heads, head_dim, max_context_len,
+                                       partition_size, workspace, workspace_bytes, stream);
+}
+
+extern "C" int paged_attention_decode_append_fp8(void* out, int32_t out_dtype, const void* query, const void* new_key,
+                                                 const void* new_value, void* k_cache, void* v_cache, void* k_scale,
+                                                 void* v_scale, const int32_t* block_tables,
+                                                 const int32_t* context_lens, int32_t B, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                                 int32_t max_blocks_per_seq, int32_t num_blocks,
+                                                 int32_t max_context_len, float scale, int32_t partition_size,
+                                                 void* workspace, size_t workspace_bytes, int32_t q_dtype,
+                                                 const int32_t* host_context_lens, pkv_stream_t stream) {
+  int st = fp8_partitions("paged_attention_decode_append_fp8", out, out_dtype, query, k_cache, v_cache, k_scale,
+                          v_scale, block_tables, context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size,
+                          max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size, workspace,
+                          workspace_bytes, q_dtype, host_context_lens, stream, new_key, new_value);
   if (st != PKV_OK) return st;
   return paged_attention_decode_reduce(out, out_dtype, context_lens, B, num_q_heads, head_dim, max_context_len,
                                        partition_size, workspace, workspace_bytes, stream);

@@ -382,15 +382,41 @@ def paged_attention_decode_fp8(out, query, k_cache, v_cache, k_scale, v_scale, b
     check(lib.paged_attention_decode_fp8(*args, _stream(stream)))
 
 
+def _fp8_fused_args(args, new_key, new_value):
+    """Argument tuple of paged_attention_decode_append_fp8 from a _fp8_decode_args tuple."""
+    _dev(new_key, new_value)
+    B, Hkv, D = args[9], args[11], args[12]
+    for t in (new_key, new_value):
+        if tuple(t.shape) != (B, Hkv, D) or dtype_code(t.dtype) != args[21]:
+            raise ValueError("new_key/new_value must be [B][Hkv][D] of the query dtype")
+    return args[:3] + (new_key.data_ptr(), new_value.data_ptr()) + args[3:]
+
+
+def paged_attention_decode_append_fp8(out, query, new_key, new_value, k_cache, v_cache, k_scale, v_scale,
+                                      block_tables, context_lens, max_context_len, scale, partition_size=0,
+                                      workspace=None, stream=None, host_context_lens=None) -> None:
+    """One decode step over an fp8 cache with the quantising append fused in: token
+    context_lens[b] - 1 of every sequence (new_key/new_value [B][Hkv][D], the query's dtype) is
+    quantised into its slot and attended over."""
+    hl, hp = _host_lens_ptr(host_context_lens)
+    args = _fp8_decode_args(out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                            max_context_len, scale, partition_size, workspace, hp)
+    check(lib.paged_attention_decode_append_fp8(*_fp8_fused_args(args, new_key, new_value), _stream(stream)))
+
+
 class PreparedDecodeFp8:
-    """paged_attention_decode_fp8 with its arguments marshalled once (partitions / reduce separately)."""
+    """paged_attention_decode_fp8 with its arguments marshalled once (partitions / reduce separately);
+    with new_key/new_value, calling it runs paged_attention_decode_append_fp8 instead."""
 
     def __init__(self, out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, max_context_len,
-                 scale, partition_size=0, workspace=None, stream=None, host_context_lens=None):
+                 scale, partition_size=0, workspace=None, stream=None, host_context_lens=None, new_key=None,
+                 new_value=None):
         self._hl, hp = _host_lens_ptr(host_context_lens)
-        self._keep = (out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, workspace)
+        self._keep = (out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, workspace,
+                      new_key, new_value)
         self.args = _fp8_decode_args(out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
                                      max_context_len, scale, partition_size, workspace, hp)
+        self.fused_args = None if new_key is None else _fp8_fused_args(self.args, new_key, new_value)
         B, Hq, D = query.shape
         ws_ptr, ws_bytes = self.args[19], self.args[20]
         self.reduce_args = (out.data_ptr(), dtype_code(out.dtype), context_lens.data_ptr(), B, Hq, D,
@@ -398,7 +424,10 @@ class PreparedDecodeFp8:
         self.stream = _stream(stream)
 
     def __call__(self) -> None:
-        check(lib.paged_attention_decode_fp8(*self.args, self.stream))
+        if self.fused_args is not None:
+            check(lib.paged_attention_decode_append_fp8(*self.fused_args, self.stream))
+        else:
+            check(lib.paged_attention_decode_fp8(*self.args, self.stream))
 
     def partitions(self) -> None:
         check(lib.paged_attention_decode_fp8_partitions(*self.args, self.stream))

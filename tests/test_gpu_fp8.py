@@ -189,3 +189,61 @@ def test_decode_fp8_batch_invariant(ps):
                       host_lens=True)
     for j, i in enumerate(rev):
         assert torch.equal(r[j].view(torch.int32), full[i].view(torch.int32))
+
+
+FUSED = [
+    # (context lengths after the step, Hq, Hkv, D, partition size, query / input dtype)
+    ("b64_single", [1, 2, 15, 16, 17, 31, 32, 33, 47, 48, 63, 64, 65, 100, 511, 512, 513, 1000], 32, 8, 128, 0,
+     "bf16"),
+    ("split512", [1, 16, 17, 33, 513, 1025, 2049], 32, 8, 128, 512, "bf16"),
+    ("d64_f16_split128", [5, 40, 300, 777], 32, 4, 64, 128, "f16"),
+    ("mha", [3, 19, 250], 8, 8, 128, 0, "bf16"),
+    ("group8_split256", [9, 80, 129, 1200], 64, 8, 128, 256, "bf16"),
+]
+
+
+@pytest.mark.parametrize("case", FUSED, ids=[c[0] for c in FUSED])
+def test_fused_append_fp8_matches_append_then_decode(case):
+    """paged_attention_decode_append_fp8: the step's tokens quantised into their slots inside the
+    decode launch.  Codes and scales bit for bit against the oracle's quantising append and against
+    paged_cache_append_fp8 on a copy of the caches; the output bit for bit against that append
+    followed by paged_attention_decode_fp8, and within 2e-3 of the oracle's attention."""
+    name, lens, Hq, Hkv, D, ps, qd = case
+    seed = 300 + FUSED.index(case)
+    N = int(np.ceil(1.1 * sum(-(-L // 16) for L in lens))) + 2
+    m, seqs, rng = _build([L - 1 for L in lens], Hkv, D, seed, in_dtype=qd, N=N)
+    B = len(seqs)
+    st, _, slots, cow = m.pool.append_many(seqs, [1] * B)
+    assert st == 0 and len(cow) == 0
+    oslots = []
+    for s in seqs:
+        sl, cw = m.opool.append(s, 1)
+        oslots += sl
+    assert slots.tolist() == oslots
+    tables, lens_np = m.tables(seqs)
+    assert lens_np.tolist() == lens
+    mcl = int(lens_np.max())
+    scale = 1.0 / np.sqrt(D)
+    sk, sv = wl.normal_bits(rng, (B, Hkv, D), qd), wl.normal_bits(rng, (B, Hkv, D), qd)
+    q = wl.normal_bits(rng, (B, Hq, D), qd)
+    qt, skt, svt = to_dev(q, qd), to_dev(sk, qd), to_dev(sv, qd)
+    k2, v2, ks2, vs2 = m.k.clone(), m.v.clone(), m.ks.clone(), m.vs.clone()
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    ops.paged_attention_decode_append_fp8(out, qt, skt, svt, m.k, m.v, m.ks, m.vs, i32(tables), i32(lens_np), mcl,
+                                          scale, ps, ops.decode_workspace(B, Hq, D, mcl, ps),
+                                          host_context_lens=lens_np)
+    out2 = torch.full_like(out, float("nan"))
+    ops.paged_cache_append_fp8(k2, v2, ks2, vs2, skt, svt, i32(slots))
+    ops.paged_attention_decode_fp8(out2, qt, k2, v2, ks2, vs2, i32(tables), i32(lens_np), mcl, scale, ps,
+                                   ops.decode_workspace(B, Hq, D, mcl, ps))
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int32), out2.view(torch.int32))
+    assert torch.equal(m.k, k2) and torch.equal(m.v, v2)
+    assert torch.equal(m.ks.view(torch.int32), ks2.view(torch.int32))
+    assert torch.equal(m.vs.view(torch.int32), vs2.view(torch.int32))
+    m.cache.append(_f32(sk, qd), _f32(sv, qd), oslots)
+    m.assert_bit_exact()
+    ref = oatt.paged_decode(q, m.cache, tables, lens_np, scale, q_dtype=qd)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert float(np.abs(got - ref).max()) <= ATOL
