@@ -522,7 +522,7 @@ def measure_fp8(args, dev, bf16_kernel_us):
         "kernel_us": {"append_fp8": round(app_us, 3), "decode_fp8": round(kern_us, 3),
                       "decode_fp8_fused_append": round(step_us, 3)},
         "decode_speedup_over_bf16_cache": round(bf16_kernel_us / kern_us, 3),
-        "roofline": {"bound": "hbm", "kernel": "decode_fp8_kernel", "achieved": round(achieved, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_fp8_kernel (decode alone, no append)", "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": None},
         "format_error_vs_bf16_cache": err,
