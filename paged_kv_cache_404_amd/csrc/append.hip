@@ -13,22 +13,30 @@
 namespace pkv {
 namespace {
 
-// One thread per (token, head, 16-byte chunk of the head vector).
+// A workgroup writes one head of a window of TW = 256 / chunks consecutive input tokens (16 at
+// D = 128 bf16), one thread per (token, 16-byte chunk of the head vector).  The dim-major V tile
+// takes each token as 2- or 4-byte pieces spread over its rows, so a cache line of V is complete
+// only once all the tokens of its block are written: for a prompt those are consecutive tokens,
+// and keeping them in one workgroup, with consecutive windows of a head on the same XCD
+// (workgroup w runs on XCD w % 8; the logical window index is remapped so that each XCD owns a
+// contiguous range), lets one L2 merge every line before it is written back.
 template <int ESIZE>
 __global__ void __launch_bounds__(256) append_kernel(uint8_t* __restrict__ k_cache, uint8_t* __restrict__ v_cache,
                                                      const uint8_t* __restrict__ key,
                                                      const uint8_t* __restrict__ value, int64_t key_stride_b,
                                                      int64_t value_stride_b, const int32_t* __restrict__ slots,
                                                      int32_t T, int32_t H, int32_t D, int32_t bs,
-                                                     int32_t num_blocks) {
+                                                     int32_t num_blocks, int32_t windows) {
   constexpr int EPC = 16 / ESIZE;  // elements per 16-byte chunk
   const int32_t chunks = D / EPC;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  const int64_t total = static_cast<int64_t>(T) * H * chunks;
-  if (gid >= total) return;
-  const int32_t c = static_cast<int32_t>(gid % chunks);
-  const int32_t h = static_cast<int32_t>((gid / chunks) % H);
-  const int32_t t = static_cast<int32_t>(gid / (static_cast<int64_t>(chunks) * H));
+  const int32_t tw = 256 / chunks;  // tokens per window (chunks <= 256 is checked on the host)
+  const int64_t per_xcd = gridDim.x / 8;  // the grid is a multiple of 8
+  const int64_t logical = static_cast<int64_t>(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (logical >= static_cast<int64_t>(H) * windows || static_cast<int32_t>(threadIdx.x) >= tw * chunks) return;
+  const int32_t h = static_cast<int32_t>(logical / windows);
+  const int32_t c = static_cast<int32_t>(threadIdx.x) % chunks;
+  const int64_t t = (logical % windows) * tw + static_cast<int32_t>(threadIdx.x) / chunks;
+  if (t >= T) return;
   const int32_t slot = slots[t];
   if (slot < 0 || slot / bs >= num_blocks) return;  // -1 = skip; out-of-pool slots are never written
   const int64_t blk = slot / bs;
@@ -94,20 +102,24 @@ extern "C" int paged_cache_append(void* k_cache, void* v_cache, const void* key,
       (key_stride * es) % 16 != 0 || (value_stride * es) % 16 != 0)
     return fail(PKV_EINVAL, "paged_cache_append: key/value/cache pointers and strides must be 16-byte aligned");
   const int chunks = head_dim * es / 16;
-  const int64_t total = static_cast<int64_t>(T) * num_kv_heads * chunks;
-  const int64_t grid = (total + 255) / 256;
-  if (grid > INT32_MAX) return fail(PKV_EINVAL, "paged_cache_append: too many tokens");
+  if (chunks > 256) return fail(PKV_EUNSUPPORTED, "paged_cache_append: head_dim*elem_size above 4 KiB");
+  const int tw = 256 / chunks;  // tokens per window
+  const int64_t windows = (static_cast<int64_t>(T) + tw - 1) / tw;
+  const int64_t grid = (static_cast<int64_t>(num_kv_heads) * windows + 7) / 8 * 8;
+  if (grid > INT32_MAX || windows > INT32_MAX) return fail(PKV_EINVAL, "paged_cache_append: too many tokens");
   hipStream_t s = as_stream(stream);
   if (es == 2) {
     hipLaunchKernelGGL(append_kernel<2>, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s,
                        static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
                        static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value), key_stride * es,
-                       value_stride * es, slot_mapping, T, num_kv_heads, head_dim, block_size, num_blocks);
+                       value_stride * es, slot_mapping, T, num_kv_heads, head_dim, block_size, num_blocks,
+                       static_cast<int32_t>(windows));
   } else {
     hipLaunchKernelGGL(append_kernel<4>, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, s,
                        static_cast<uint8_t*>(k_cache), static_cast<uint8_t*>(v_cache),
                        static_cast<const uint8_t*>(key), static_cast<const uint8_t*>(value), key_stride * es,
-                       value_stride * es, slot_mapping, T, num_kv_heads, head_dim, block_size, num_blocks);
+                       value_stride * es, slot_mapping, T, num_kv_heads, head_dim, block_size, num_blocks,
+                       static_cast<int32_t>(windows));
   }
   return check_launch("paged_cache_append");
 }
