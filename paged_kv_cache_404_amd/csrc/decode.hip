@@ -122,11 +122,10 @@ __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Log-sum-exp merge of partitions.  grid = (Hq, B), 128 threads.  MAXP >= max_parts (up to 64):
-// every partial of the row is loaded at once, together with the context length (one memory
-// latency), (m, l) through LDS; the sequence's own partition count then selects which take
-// part.  Rows of single-partition sequences were written by the partition pass and are left
-// alone.
+// Log-sum-exp merge of partitions.  grid = (Hq, B), 128 threads.  MAXP >= max_parts (up to 64).
+// The context length comes first: rows of single-partition sequences were written by the
+// partition pass and end here, and the others load only their own partitions' partials (all at
+// once: (m, l) through LDS, one dimension of every partial per thread), not max_parts of them.
 // ------------------------------------------------------------------------------------------
 template <int DT_OUT, int MAXP>
 __global__ void __launch_bounds__(128) decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ part_ml,
@@ -136,21 +135,22 @@ __global__ void __launch_bounds__(128) decode_reduce_kernel(void* __restrict__ o
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int d = threadIdx.x;
+  const int L = min(lens[b], max_parts * part_size);
+  const int nparts = (L + part_size - 1) / part_size;
+  if (nparts <= 1) return;
   const int64_t row0 = (static_cast<int64_t>(b) * Hq + h) * max_parts;
   __shared__ float sm[MAXP], sl[MAXP];
   // Thread p fetches partition p's (m, l); every thread fetches its dimension of every partial.
   if (d < MAXP) {
-    const bool in = d < max_parts;
+    const bool in = d < nparts;
     sm[d] = in ? part_ml[(row0 + d) * 2] : -INFINITY;
     sl[d] = in ? part_ml[(row0 + d) * 2 + 1] : 0.f;
   }
   float o[MAXP];
 #pragma unroll
-  for (int p = 0; p < MAXP; ++p) o[p] = (p < max_parts && d < D) ? part_o[(row0 + p) * D + d] : 0.f;
-  const int L = min(lens[b], max_parts * part_size);
-  const int nparts = (L + part_size - 1) / part_size;
+  for (int p = 0; p < MAXP; ++p) o[p] = (p < nparts && d < D) ? part_o[(row0 + p) * D + d] : 0.f;
   __syncthreads();
-  if (nparts <= 1 || d >= D) return;
+  if (d >= D) return;
   float M = -INFINITY;
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) M = p < nparts ? fmaxf(M, sm[p]) : M;
