@@ -59,22 +59,29 @@ __device__ __forceinline__ uint32_t pack4_fp8(float a, float b, float c, float d
   return static_cast<uint32_t>(w);
 }
 
-// R = D / 8 lanes per (token, head) row; lane j quantises dimensions [8j, 8j + 8).
+// R = D / 8 lanes per (token, head) row; lane j quantises dimensions [8j, 8j + 8).  A workgroup
+// takes one head of a window of 256 / R consecutive input tokens, and consecutive windows of a
+// head run on the same XCD (workgroup w runs on XCD w % 8; the logical window index is remapped
+// so that each XCD owns a contiguous range): the byte-wide V codes of a prompt's block then reach
+// one L2, which merges each line before writing it back.
 template <int DT_IN, int D>
 __global__ void __launch_bounds__(256) append_fp8_kernel(uint8_t* __restrict__ kc, uint8_t* __restrict__ vc,
                                                          float* __restrict__ ksc, float* __restrict__ vsc,
                                                          const uint8_t* __restrict__ key,
                                                          const uint8_t* __restrict__ value, int64_t key_stride_b,
                                                          int64_t value_stride_b, const int32_t* __restrict__ slots,
-                                                         int32_t T, int32_t H, int32_t num_blocks) {
+                                                         int32_t T, int32_t H, int32_t num_blocks, int32_t windows) {
   constexpr int R = D / 8;
+  constexpr int TW = 256 / R;  // tokens per window
   constexpr int ES = DT_IN == PKV_F32 ? 4 : 2;
-  const int64_t gid = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t row = gid / R;
-  const int j = static_cast<int>(gid % R);
-  const bool active = row < static_cast<int64_t>(T) * H;
-  const int t = active ? static_cast<int>(row / H) : 0;
-  const int h = active ? static_cast<int>(row % H) : 0;
+  const int64_t per_xcd = gridDim.x / 8;  // the grid is a multiple of 8
+  const int64_t logical = static_cast<int64_t>(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int j = static_cast<int>(threadIdx.x % R);
+  const int64_t tt = (logical % windows) * TW + threadIdx.x / R;
+  // Every lane takes part in the row maximum below, so out-of-range lanes stay, inactive.
+  const bool active = logical < static_cast<int64_t>(H) * windows && tt < T;
+  const int t = active ? static_cast<int>(tt) : 0;
+  const int h = active ? static_cast<int>(logical / windows) : 0;
   const int slot = active ? slots[t] : -1;
   const bool ok = slot >= 0 && slot / kBlock < num_blocks;  // -1 = skip; out-of-pool slots are never written
   float kx[8], vx[8];
@@ -767,9 +774,10 @@ extern "C" int paged_cache_append_fp8(void* k_cache, void* v_cache, void* k_scal
       (reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(k_scale) |
        reinterpret_cast<uintptr_t>(v_scale)) % 8 != 0)
     return fail(PKV_EINVAL, "%s: misaligned pointer", fn);
-  const int64_t threads = static_cast<int64_t>(T) * num_kv_heads * (head_dim / 8);
-  const int64_t grid = (threads + 255) / 256;
-  if (grid > INT32_MAX) return fail(PKV_EINVAL, "%s: too many tokens", fn);
+  const int tw = 256 / (head_dim / 8);  // tokens per workgroup window
+  const int64_t windows = (static_cast<int64_t>(T) + tw - 1) / tw;
+  const int64_t grid = (static_cast<int64_t>(num_kv_heads) * windows + 7) / 8 * 8;
+  if (grid > INT32_MAX || windows > INT32_MAX) return fail(PKV_EINVAL, "%s: too many tokens", fn);
   hipStream_t s = as_stream(stream);
   uint8_t* kc = static_cast<uint8_t*>(k_cache);
   uint8_t* vc = static_cast<uint8_t*>(v_cache);
@@ -780,7 +788,7 @@ extern "C" int paged_cache_append_fp8(void* k_cache, void* v_cache, void* k_scal
   const dim3 gr(static_cast<uint32_t>(grid)), bl(256);
 #define PKV_APPEND_FP8(DT, DD)                                                                                    \
   hipLaunchKernelGGL((append_fp8_kernel<DT, DD>), gr, bl, 0, s, kc, vc, ks, vs, kin, vin, key_stride * es,        \
-                     value_stride * es, slot_mapping, T, num_kv_heads, num_blocks)
+                     value_stride * es, slot_mapping, T, num_kv_heads, num_blocks, static_cast<int32_t>(windows))
   if (head_dim == 64) {
     if (in_dtype == PKV_BF16)
       PKV_APPEND_FP8(PKV_BF16, 64);
