@@ -405,11 +405,12 @@ int partitions_impl(const char* fn, void* out, int32_t out_dtype, const void* qu
   a.k_out = k_out;
   a.v_out = v_out;
   if (host_lens != nullptr && B <= kMaxOrder) {
-    // Largest work last-dispatched-least: rows sorted by the size of their sequence's last
-    // partition (the whole context for a single pass), largest first, ties longest first; and
-    // each sequence's partitions rotated so that its last one falls in the grid's last slice.
-    // Full partitions are then all dispatched before the ragged last ones, which go smallest
-    // last.  The schedule only: every partition's arithmetic is the same wherever it runs.
+    // Work order (largest work first, smallest last): rows sorted by the size of their
+    // sequence's last partition (the whole context for a single pass), largest first, ties
+    // longest first; and each sequence's partitions rotated so that its last one falls in the
+    // grid's last slice.  Full partitions are then all dispatched before the ragged last ones,
+    // which go smallest last.  The schedule only: every partition's arithmetic is the same
+    // wherever it runs.
     int32_t nparts[kMaxOrder], last[kMaxOrder], idx[kMaxOrder];
     for (int i = 0; i < B; ++i) {
       const int L = std::max(0, std::min(host_lens[i], max_ctx));

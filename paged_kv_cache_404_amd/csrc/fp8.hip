@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(256) append_fp8_kernel(uint8_t* __restrict__ k
   const int64_t logical = static_cast<int64_t>(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   const int j = static_cast<int>(threadIdx.x % R);
   const int64_t tt = (logical % windows) * TW + threadIdx.x / R;
-  // Every lane takes part in the row maximum below, so out-of-range lanes stay, inactive.
+  // Every lane takes part in the row maximum below, so out-of-range lanes stay (inactive).
   const bool active = logical < static_cast<int64_t>(H) * windows && tt < T;
   const int t = active ? static_cast<int>(tt) : 0;
   const int h = active ? static_cast<int>(logical / windows) : 0;
