@@ -260,18 +260,18 @@ __device__ __forceinline__ void decode_mfma_part(const DecodeArgs& a, int g, int
             }
           }
         }
-        // The registers now hold the new token's whole K tile (the other slots as loaded):
-        // store it back with the load's own lane pattern, so every cache line is written whole.
-        // Without k_out the caller writes the cache itself (paged_attention_decode_newest).
+        // The registers now hold the new token's K (the other slots as loaded).  Its bytes lie
+        // in the half of the tile that holds its 4-token set (token order above): those 16 lines
+        // (8 tokens each, one 16-byte chunk of each) are stored back with the load's own lane
+        // pattern, so every line written is written whole.  Without k_out the caller writes the
+        // cache itself (paged_attention_decode_newest).
         if (a.k_out != nullptr && k_from_b == in_b) {
           int64_t tA, tB;
           tiles(s, tA, tB);
-          uint16_t* kp = static_cast<uint16_t*>(a.k_out) + (in_b ? tB : tA) + k_in_tile;
+          uint16_t* kp = static_cast<uint16_t*>(a.k_out) + (in_b ? tB : tA) + k_in_tile + nk_set * 256;
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            *reinterpret_cast<u32x4*>(kp + (2 * ks) * 256) = kf[ks];
-            *reinterpret_cast<u32x4*>(kp + (2 * ks + 1) * 256) = kf[KS + ks];
-          }
+          for (int ks = 0; ks < KS; ++ks)
+            *reinterpret_cast<u32x4*>(kp + (2 * ks) * 256) = nk_set ? kf[KS + ks] : kf[ks];
         }
       }
       f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = {0.f, 0.f, 0.f, 0.f};

@@ -224,9 +224,10 @@ __device__ __forceinline__ float row16_max(float x) {
 // the input rows new_k / new_v.  The wave that owns the last step of the sequence's last
 // partition quantises them exactly as append_fp8_kernel does (one scale per (token, head):
 // amax / 448, codes RNE of x * (448 / amax)), puts the codes and scales into its operand
-// registers in place of the slot's stale contents, and stores the block's whole K and V code
-// tiles and both scale rows back (every other slot with the bytes it was loaded with).  The last
-// block of a sequence is private to it, so no other workgroup touches that block in the launch.
+// registers in place of the slot's stale contents, and stores back whole lines: the half of the
+// block's K code tile that holds the token's 4-token set, the whole V code tile and both scale
+// rows (every other slot with the bytes it was loaded with).  The last block of a sequence is
+// private to it, so no other workgroup touches that block in the launch.
 template <int DT, int DT_OUT, int D, int G, int NW, bool NEWTOK>
 __global__ void __launch_bounds__(NW * 64) decode_fp8_kernel(Fp8Args a) {
   static_assert(D == 64 || D == 128, "head_dim");
@@ -440,18 +441,17 @@ __global__ void __launch_bounds__(NW * 64) decode_fp8_kernel(Fp8Args a) {
             }
           }
         }
-        // Store the block's tiles and scale rows back with the loads' own lane patterns (every
-        // line written whole).
+        // Store back, with the loads' own lane patterns (every line written whole): the half of
+        // the K code tile that holds the token's 4-token set (its codes lie nowhere else), the
+        // whole V code tile (the token has a byte in every line of it) and both scale rows.
         int64_t hA, hB;
         heads(s, hA, hB);
         const int64_t hN = nin_b ? hB : hA;
         if (k_from_b == nin_b) {
-          uint8_t* kp = a.k_out + hN * TILE + k_in_tile;
+          uint8_t* kp = a.k_out + hN * TILE + k_in_tile + nk_set * 512;
 #pragma unroll
-          for (int ss = 0; ss < 2; ++ss) {
-#pragma unroll
-            for (int pp = 0; pp < KP; ++pp) *reinterpret_cast<u32x4*>(kp + (pp * 2 + ss) * 512) = kraw[ss * KP + pp];
-          }
+          for (int pp = 0; pp < KP; ++pp)
+            *reinterpret_cast<u32x4*>(kp + pp * 2 * 512) = nk_set ? kraw[KP + pp] : kraw[pp];
         }
         if (v_from_b == nin_b) {
           uint8_t* vp = a.v_out + hN * TILE + v_in_tile;
