@@ -28,9 +28,14 @@
  *     share one element type (`dtype`).
  *   - Cache layout (one layer; K and V are separate tensors, both indexed by physical block id):
  *         k_cache [num_blocks][num_kv_heads][K tile]                 see below
- *         v_cache [num_blocks][num_kv_heads][head_dim][block_size]   head-dim rows
+ *         v_cache [num_blocks][num_kv_heads][V tile]                 see below
  *     Slot s means block s / block_size, offset s % block_size.  One (block, head) tile of either
  *     tensor is contiguous (4 KiB at 16 x 128 bf16), and a whole block is one contiguous span.
+ *     V tile: [block_size / 8][head_dim][8], i.e. element d of token t is at tile offset
+ *     ((t / 8) * head_dim + d) * 8 + t % 8: eight consecutive tokens of one dimension are one
+ *     16-byte operand of the P.V product, and the eight tokens of a half block own whole cache
+ *     lines.  (A torch view of shape [num_blocks][num_kv_heads][head_dim][16] holds it; only the
+ *     byte order inside a tile is this one.)
  *     K tile: the 16 x head_dim elements of one (block, head) are stored as 16-byte chunks
  *     (E = 16 / element size elements each, so head_dim * element size must be a multiple of 64
  *     bytes).  With token t = 8*hi + 4*set + low and chunk c = 4*cq + cr of the token's head

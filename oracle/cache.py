@@ -67,6 +67,15 @@ class CacheModel:
         # stored order [cq][set][cr][hi][low][e]
         return np.ascontiguousarray(t.transpose(0, 1, 5, 3, 6, 2, 4, 7)).reshape(n, H, bs * D)
 
+    def v_physical(self, blocks=slice(None)) -> np.ndarray:
+        """V of the given blocks in stored order: per (block, head) the token halves, then the
+        dimensions, then 8 tokens ([bs / 8][D][8]); returned as [n][num_kv_heads][block_size * head_dim]."""
+        v = self.v[blocks]  # [n][H][D][bs]
+        n, H, D, bs = v.shape
+        if bs != 16:
+            raise ValueError("the V tile order needs 16-token blocks")
+        return np.ascontiguousarray(v.reshape(n, H, D, 2, 8).transpose(0, 1, 3, 2, 4)).reshape(n, H, bs * D)
+
     def token_k(self, slot: int) -> np.ndarray:
         blk, off = divmod(int(slot), self.bs)
         return self.k[blk, :, off, :]

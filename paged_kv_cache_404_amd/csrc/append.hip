@@ -5,7 +5,8 @@
 // physical page id.  Here the slot of every token is computed on the host by the block pool, so
 // the kernels only move bytes.  Layout: K [N][Hkv][tile] with each token's head vector cut into
 // 16-byte chunks placed in the matrix-core tile order of k_chunk_pos (16-byte stores), V
-// [N][Hkv][D][bs] (a token is one column per head, written element by element).
+// [N][Hkv][bs / 8][D][8] (per (block, head): token half, dimension, 8 tokens; a token is written
+// element by element, its 8 dimensions of one chunk into one 128-byte line at bf16).
 // Copy-on-write ([Chapter] "PagedAttention: KV cache memory"): a shared block that a sequence is
 // about to write is first copied whole.
 #include "device.h"
@@ -14,9 +15,9 @@ namespace pkv {
 namespace {
 
 // A workgroup writes one head of a window of TW = 256 / chunks consecutive input tokens (16 at
-// D = 128 bf16), one thread per (token, 16-byte chunk of the head vector).  The dim-major V tile
-// takes each token as 2- or 4-byte pieces spread over its rows, so a cache line of V is complete
-// only once all the tokens of its block are written: for a prompt those are consecutive tokens,
+// D = 128 bf16), one thread per (token, 16-byte chunk of the head vector).  The V tile takes
+// each token as 2- or 4-byte pieces, 8 tokens to a line, so a cache line of V is complete only
+// once all the tokens of its half block are written: for a prompt those are consecutive tokens,
 // and keeping them in one workgroup, with consecutive windows of a head on the same XCD
 // (workgroup w runs on XCD w % 8; the logical window index is remapped so that each XCD owns a
 // contiguous range), lets one L2 merge every line before it is written back.
@@ -46,15 +47,18 @@ __global__ void __launch_bounds__(256) append_kernel(uint8_t* __restrict__ k_cac
   const u32x4 vv = *reinterpret_cast<const u32x4*>(value + t * value_stride_b + src_off);
   const int64_t head = blk * H + h;
   *reinterpret_cast<u32x4*>(k_cache + (head * bs * D) * ESIZE + static_cast<int64_t>(k_chunk_pos(off, c)) * 16) = kv;
-  uint8_t* vcol = v_cache + ((head * D + static_cast<int64_t>(c) * EPC) * bs + off) * ESIZE;
+  // Element (dimension d, token off) of the tile at ((off / 8) * D + d) * 8 + off % 8.
+  uint8_t* vcol =
+      v_cache + (head * D * bs + (static_cast<int64_t>(off >> 3) * D + static_cast<int64_t>(c) * EPC) * 8 + (off & 7)) *
+                    ESIZE;
   if constexpr (ESIZE == 2) {
     const uint16_t* e = reinterpret_cast<const uint16_t*>(&vv);
 #pragma unroll
-    for (int i = 0; i < EPC; ++i) reinterpret_cast<uint16_t*>(vcol)[static_cast<int64_t>(i) * bs] = e[i];
+    for (int i = 0; i < EPC; ++i) reinterpret_cast<uint16_t*>(vcol)[static_cast<int64_t>(i) * 8] = e[i];
   } else {
     const uint32_t* e = reinterpret_cast<const uint32_t*>(&vv);
 #pragma unroll
-    for (int i = 0; i < EPC; ++i) reinterpret_cast<uint32_t*>(vcol)[static_cast<int64_t>(i) * bs] = e[i];
+    for (int i = 0; i < EPC; ++i) reinterpret_cast<uint32_t*>(vcol)[static_cast<int64_t>(i) * 8] = e[i];
   }
 }
 

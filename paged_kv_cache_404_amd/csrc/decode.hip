@@ -18,8 +18,9 @@
 // matrix cores with v_mfma_f32_16x16x32_{bf16,f16}:
 //   S^T[token][head] = K[token][:] . Q[head][:]      (A = K rows, B = Q^T, heads padded to 16)
 //   O[row][d]       += P[row][token] . V[token][d]    (A = P rows, B = V^T tile)
-// The V cache is stored dim-major per block ([D][16]) so that eight consecutive tokens of one
-// dimension are one 16-byte load, which is what the P.V operand wants.  The softmax weights are
+// The V tile of a (block, head) is stored [token half][D][8 tokens], so that eight consecutive
+// tokens of one dimension are one 16-byte load, which is what the P.V operand wants, and sixteen
+// dimensions of one half are 256 contiguous bytes.  The softmax weights are
 // fed as two 16-bit rows, hi = round(p) and lo = round(p - hi), in the padding rows of the same
 // MFMA, so P.V keeps ~16 mantissa bits at no extra matrix instruction.  Scores use exp2 with
 // log2(e) folded into the scale; the running maximum is only raised when a score exceeds it by
@@ -109,7 +110,7 @@ __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
 #pragma unroll
       for (int k = 0; k < DPL; ++k) {
         const int d = lane + 64 * k;
-        if (d < D) o[k] += pi * elem_to_float<DT>(a.v, ti + static_cast<int64_t>(d) * kBlock + oi);
+        if (d < D) o[k] += pi * elem_to_float<DT>(a.v, ti + static_cast<int64_t>((oi >> 3) * D + d) * 8 + (oi & 7));
       }
     }
     m_run = m_new;

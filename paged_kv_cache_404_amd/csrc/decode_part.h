@@ -188,11 +188,12 @@ __device__ __forceinline__ void decode_mfma_part(const DecodeArgs& a, int g, int
   // (s = 0, 1) row m holds token 8*(m/4) + m%4 + 4s of block m/8 (the K tile order puts exactly
   // these rows of one k-step in one 512-byte run per block).  Lane (head, q4) then holds the
   // scores of step tokens 8*q4 .. 8*q4+7, the k-range its P row covers in P.V, whose V operand
-  // (8 consecutive tokens of one dimension) is one 16-byte load from the dim-major V tile.
+  // (8 consecutive tokens of one dimension) is one 16-byte load from the V tile ([token half]
+  // [D][8 tokens]: 16 lanes of one half read 256 contiguous bytes).
   const int k_in_tile = (q4 * 8 + (n16 & 7)) * 8;  // chunk (k-step 0, set 0) of this lane, in elements
   const bool k_from_b = n16 >= 8;
   const bool v_from_b = q4 >= 2;
-  const int v_in_tile = n16 * kBlock + (q4 & 1) * 8;
+  const int v_in_tile = (q4 & 1) * D * 8 + n16 * 8;
 
   f32x4 o[NB];
 #pragma unroll
@@ -232,7 +233,7 @@ __device__ __forceinline__ void decode_mfma_part(const DecodeArgs& a, int g, int
       const uint16_t* vp = vc + (v_from_b ? tB : tA) + v_in_tile;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb)
-        vf[nb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + nb * 16 * kBlock));
+        vf[nb] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + nb * 16 * 8));
     };
 
     // One 32-token step; with `prefetch` the successor's loads are issued as registers free up.
@@ -354,13 +355,15 @@ __device__ __forceinline__ void decode_mfma_part(const DecodeArgs& a, int g, int
             }
           }
         }
-        // Likewise the whole V tile, before the tail past the context is zeroed below.
-        if (a.v_out != nullptr && v_from_b == in_b) {
+        // Likewise the half of the V tile that holds the new token's 8-token half (the lanes
+        // q4 == nv_q4: 16 dimensions x 8 tokens per store, whole lines), before the tail past
+        // the context is zeroed below.
+        if (a.v_out != nullptr && q4 == nv_q4) {
           int64_t tA, tB;
           tiles(s, tA, tB);
           uint16_t* vp = static_cast<uint16_t*>(a.v_out) + (in_b ? tB : tA) + v_in_tile;
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<u32x4*>(vp + nb * 16 * kBlock) = vf[nb];
+          for (int nb = 0; nb < NB; ++nb) *reinterpret_cast<u32x4*>(vp + nb * 16 * 8) = vf[nb];
         }
       }
       if (nvalid < 32) {

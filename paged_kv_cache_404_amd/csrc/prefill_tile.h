@@ -109,7 +109,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
   const bool k_from_b = n16 >= 8;
   const int k_in_tile = (q4 * 8 + (n16 & 7)) * 8;
   const bool v_from_b = q4 >= 2;
-  const int v_in_tile = n16 * kBlock + (q4 & 1) * 8;
+  const int v_in_tile = (q4 & 1) * D * 8 + n16 * 8;  // V tile [token half][D][8 tokens]
 
   f32x4 o[HPW][NB];
   float m_run[HPW], l_run[HPW];  // per head: reference maximum (log2 domain) and this lane's sum
@@ -161,7 +161,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
       tiles(st, tA, tB);
       const uint16_t* vp = vc + (v_from_b ? tB : tA) + v_in_tile;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vf[nb] = *reinterpret_cast<const u32x4*>(vp + nb * 16 * kBlock);
+      for (int nb = 0; nb < NB; ++nb) vf[nb] = *reinterpret_cast<const u32x4*>(vp + nb * 16 * 8);
     };
 
     // One 32-key step for all HPW heads; with `prefetch` the next step's loads are issued as

@@ -33,7 +33,8 @@ def _stream(stream) -> int:
 
 
 def paged_cache_append(k_cache, v_cache, key, value, slot_mapping, stream=None) -> None:
-    """k_cache [N][Hkv][16][D], v_cache [N][Hkv][D][16]; key/value [T][Hkv][D]; slot_mapping int32 [T]."""
+    """k_cache [N][Hkv][16][D] and v_cache [N][Hkv][D][16] tensors holding the K and V tiles in their
+    stored orders (include/pagedkv.h); key/value [T][Hkv][D]; slot_mapping int32 [T]."""
     _dev(k_cache, v_cache, key, value, slot_mapping)
     N, H, bs, D = k_cache.shape
     if tuple(v_cache.shape) != (N, H, D, bs):

@@ -103,7 +103,8 @@ class Mirror:
             b1 = min(self.N, b0 + step)
             kb = to_bits(self.k[b0:b1], self.dtype).reshape(b1 - b0, self.Hkv, 16 * self.D)
             assert np.array_equal(kb, self.cache.k_physical(slice(b0, b1))), f"K blocks {b0}:{b1}"
-            assert np.array_equal(to_bits(self.v[b0:b1], self.dtype), self.cache.v[b0:b1]), f"V blocks {b0}:{b1}"
+            vb = to_bits(self.v[b0:b1], self.dtype).reshape(b1 - b0, self.Hkv, 16 * self.D)
+            assert np.array_equal(vb, self.cache.v_physical(slice(b0, b1))), f"V blocks {b0}:{b1}"
 
 
 def build_decode(w: wl.DecodeWorkload, t: wl.DecodeTensors):

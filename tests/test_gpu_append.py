@@ -4,7 +4,7 @@ The slot mappings mix what a serving step hands over: prompts (runs of consecuti
 blocks, ragged at their ends, so the kernel's token windows straddle blocks), scattered single
 slots, -1 entries (skipped) and slots outside the pool (never written).  After each of two calls
 on the same cache, its bytes are compared with the oracle's cache model bit for bit (K in the
-tile order, V dim-major, every untouched slot still the NaN sentinel or its earlier value)."""
+tile order, V in its half-split order, every untouched slot still the NaN sentinel or its earlier value)."""
 import numpy as np
 import pytest
 import torch
@@ -74,4 +74,4 @@ def test_append_matches_oracle_bit_for_bit(dtype, Hkv, D, T):
         assert kc.dtype == TORCH_DT[dtype]
         got_k = to_bits(kc, dtype).reshape(N, Hkv, 16 * D)
         assert np.array_equal(got_k, cache.k_physical()), "K tiles"
-        assert np.array_equal(to_bits(vc, dtype), cache.v), "V tiles"
+        assert np.array_equal(to_bits(vc, dtype).reshape(N, Hkv, 16 * D), cache.v_physical()), "V tiles"

@@ -461,3 +461,24 @@ def test_prefix_cache_eviction_unregisters_the_blocks_below():
     assert n == 0
     p.free_seq(y)  # 4 and 3 are unregistered: both to the free list
     assert p.free == [4, 3] and p.lru == []
+
+
+@pytest.mark.parametrize("dt,D", [("bf16", 128), ("f32", 64), ("f16", 64)])
+def test_v_tile_order_by_brute_force(dt, D):
+    """The stored V order, element by element: (block, head, dimension d, token t) sits at
+    ((t // 8) * D + d) * 8 + t % 8 of its tile; 16 dimensions of one 8-token half are 256
+    contiguous bytes at 16-bit elements (one half-wave operand load)."""
+    rng = np.random.default_rng(7)
+    N, H = 3, 2
+    cache = CacheModel(N, H, D, dt, fill_nan=False)
+    cache.v[:] = rng.integers(1, 2**15, size=cache.v.shape).astype(cache.v.dtype)
+    phys = cache.v_physical()
+    for b in range(N):
+        for h in range(H):
+            for d in range(D):
+                for t in range(16):
+                    assert phys[b, h, ((t // 8) * D + d) * 8 + t % 8] == cache.v[b, h, d, t]
+    esize = cache.v.dtype.itemsize
+    if esize == 2:
+        # a half-wave's 16 lanes (dimensions 16 nb .. 16 nb + 15 of one half) read 256 contiguous bytes
+        assert (16 * 8 * esize) == 256
