@@ -247,3 +247,34 @@ def test_fused_append_fp8_matches_append_then_decode(case):
     got = out.cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all()
     assert float(np.abs(got - ref).max()) <= ATOL
+
+
+def test_fused_append_fp8_llama_shaped_as_benched():
+    """The fp8 step bench.py times, at full size: batch 64, 32/8 heads x 128, contexts U[128, 2048],
+    the new tokens quantised inside the single-pass decode with the host copy of the lengths.
+    Codes and scales of the whole cache bit for bit against the oracle; every output within 2e-3
+    of the oracle's attention over the dequantised cache."""
+    w = wl.llama_decode(2)
+    lens = [int(L) for L in w.lens]
+    m, seqs, rng = _build([L - 1 for L in lens], 8, 128, 78, N=w.num_blocks)
+    st, _, slots, cow = m.pool.append_many(seqs, [1] * w.B)
+    assert st == 0 and len(cow) == 0
+    oslots = []
+    for s in seqs:
+        sl, _ = m.opool.append(s, 1)
+        oslots += sl
+    tables, lens_np = m.tables(seqs, w.max_blocks_per_seq)
+    mcl = int(lens_np.max())
+    sk, sv = wl.normal_bits(rng, (w.B, 8, 128), "bf16"), wl.normal_bits(rng, (w.B, 8, 128), "bf16")
+    q = wl.normal_bits(rng, (w.B, 32, 128), "bf16")
+    out = torch.full((w.B, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ops.paged_attention_decode_append_fp8(out, to_dev(q, "bf16"), to_dev(sk, "bf16"), to_dev(sv, "bf16"), m.k, m.v,
+                                          m.ks, m.vs, i32(tables), i32(lens_np), mcl, w.scale, 0, None,
+                                          host_context_lens=lens_np)
+    torch.cuda.synchronize()
+    m.cache.append(_f32(sk, "bf16"), _f32(sv, "bf16"), oslots)
+    m.assert_bit_exact()
+    ref = oatt.paged_decode(q, m.cache, tables, lens_np, w.scale, q_dtype="bf16")
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    assert float(np.abs(got - ref).max()) <= ATOL
