@@ -401,6 +401,8 @@ def measure_trace(dev, choose_ps=trace_partition_size):
         "replay_enqueue_ms": round(enqueue_ms, 2),
         # The 500 ms spin covers the enqueue, so no step waited for the host (its events time the GPU only).
         "enqueue_within_spin": bool(enqueue_ms < 500.0),
+        # lengths of the step with the median batch, for the oracle's sampled baseline (popped by main)
+        "_median_step_lens": sorted((ln for _, ln, _ in steps), key=len)[len(steps) // 2].tolist(),
     }
 
 
@@ -1034,6 +1036,17 @@ def main():
         res["fp8_cache"] = measure_fp8(args, dev, part_us)
         res["mixed_step"] = measure_mixed(args, dev)
         res["trace"] = measure_trace(dev)
+        med = res["trace"].pop("_median_step_lens")
+        if not args.no_cpu_baseline:
+            # The oracle on 8 sequences of the trace's median-batch step, its GB/s extrapolated to the
+            # trace's total decode bytes (running it on every step would take hours).
+            w_med = wl.custom_decode(3, med, 32, 8, 128, "bf16")
+            cb = cpu_baseline(w_med, args.cpu_seconds / 4, max_seqs=8)
+            total_s = res["trace"]["decode_kv_plus_q_bytes"] / (cb["value"] * 1e9)
+            cb["sample"] = f"median-batch step of the trace ({len(med)} sequences): " + cb["sample"]
+            cb["extrapolated_trace_decode_s"] = round(total_s, 1)
+            cb["extrapolated_seqs_steps_per_s"] = round(res["trace"]["seq_steps"] / total_s, 1)
+            res["trace"]["cpu_baseline"] = cb
     print(json.dumps(res), flush=True)
 
 
