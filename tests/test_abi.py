@@ -83,6 +83,11 @@ def test_decode_host_validation(kw, status):
     assert pkv.last_error()
 
 
+def test_empty_batch_is_a_no_op():
+    assert _decode(B=0) == pkv.PKV_OK
+    assert _decode(B=0, ps=512, ws=1 << 12, ws_bytes=1 << 20) == pkv.PKV_OK
+
+
 def test_workspace_size_formula():
     n = pkv.lib.paged_attention_decode_workspace_bytes(8, 32, 128, 32768, 512)
     parts = 64

@@ -209,3 +209,29 @@ def test_longest_first_order_is_bitwise_invariant(ps):
         assert torch.equal(outs[0].view(torch.int32), o.view(torch.int32))
     ref = oatt.paged_decode(t.q, m.cache, tables, lens, w.scale)
     _check(outs[1], ref)
+
+
+@pytest.mark.parametrize("ps", [0, 64])
+def test_batch_beyond_the_order_table(ps):
+    """600 sequences, more than the 512 entries of the host-built work order: the launch then runs
+    rows in batch order (host lengths ignored), and still matches the oracle on short ragged
+    contexts (1 to 200 tokens, block edges included)."""
+    rng = np.random.default_rng(1234 + ps)
+    lens = rng.integers(1, 201, size=600)
+    lens[:8] = [1, 15, 16, 17, 31, 32, 33, 200]
+    w = wl.custom_decode(97, lens.tolist(), 32, 8, 128, "bf16", partition_size=ps)
+    t = wl.decode_tensors(w)
+    m, seqs = build_decode(w, t)
+    tables, dlens = m.tables(seqs)
+    q = to_dev(t.q, "bf16")
+    mcl = int(dlens.max())
+    outs = []
+    for hl in (None, dlens):
+        out = torch.full((w.B, w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
+        ops.paged_attention_decode(out, q, m.k, m.v, i32(tables), i32(dlens), mcl, w.scale, ps,
+                                   ops.decode_workspace(w.B, w.Hq, w.D, mcl, ps), host_context_lens=hl)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
+    ref = oatt.paged_decode(t.q, m.cache, tables, dlens, w.scale)
+    _check(outs[1], ref)
