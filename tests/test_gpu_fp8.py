@@ -199,6 +199,9 @@ FUSED = [
     ("d64_f16_split128", [5, 40, 300, 777], 32, 4, 64, 128, "f16"),
     ("mha", [3, 19, 250], 8, 8, 128, 0, "bf16"),
     ("group8_split256", [9, 80, 129, 1200], 64, 8, 128, 256, "bf16"),
+    # more sequences than the host-built work order holds: rows run in batch order
+    ("b600_split64", [1, 2, 16, 17, 32, 33, 64, 65] + np.random.default_rng(600).integers(1, 201, 592).tolist(),
+     32, 8, 128, 64, "bf16"),
 ]
 
 

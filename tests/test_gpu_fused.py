@@ -103,6 +103,20 @@ def test_fused_append_decode(dtype, Hq, Hkv, D, lens, ps):
     _fused_vs_all(m, seqs, w, t, slots, ps)
 
 
+@pytest.mark.parametrize("ps", [0, 64])
+def test_fused_batch_beyond_the_order_table(ps):
+    """600 sequences (more than the host-built work order holds): rows run in batch order, the
+    owner of each new token still writes it, and cache and output match as in every case above."""
+    rng = np.random.default_rng(4321 + ps)
+    lens = rng.integers(1, 201, size=600)
+    lens[:8] = [1, 2, 16, 17, 32, 33, 64, 65]
+    w = wl.custom_decode(98, lens.tolist(), 32, 8, 128, "bf16", partition_size=ps)
+    t = wl.decode_tensors(w)
+    m, seqs = _prefix(w, t)
+    slots, _ = _reserve(m, seqs)
+    _fused_vs_all(m, seqs, w, t, slots, ps)
+
+
 @pytest.mark.parametrize("ps", [512, 0])
 def test_fused_llama_shaped_full_size(ps):
     w = wl.llama_decode(2)
