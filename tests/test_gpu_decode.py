@@ -60,6 +60,9 @@ CASES = [
     ("f16", 32, 4, 64, [16, 48, 95], 32),
     ("f32", 16, 8, 128, [1, 20, 65, 300], 0),
     ("f32", 8, 2, 64, [7, 33, 200], 64),
+    # more than 16 partitions: the sliced reduce (47 at D = 64; 125 with fp16)
+    ("bf16", 16, 8, 64, [2, 64, 129, 700, 1500], 32),
+    ("f16", 32, 8, 128, [4, 33, 250, 777, 2000], 16),
 ]
 
 
@@ -75,14 +78,15 @@ def test_decode_shapes_and_edges(dtype, Hq, Hkv, D, lens, ps):
     _check(out, ref)
 
 
+@pytest.mark.parametrize("ps", [128, 16])
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_output_in_input_dtype(dtype):
-    w = wl.custom_decode(31, [9, 130, 600], 32, 8, 128, dtype, partition_size=128)
+def test_output_in_input_dtype(dtype, ps):
+    w = wl.custom_decode(31, [9, 130, 600], 32, 8, 128, dtype, partition_size=ps)
     t = wl.decode_tensors(w)
     m, seqs = build_decode(w, t)
     tables, lens = m.tables(seqs)
     ref = oatt.paged_decode(t.q, m.cache, tables, lens, w.scale)
-    out, _, _ = run_decode(m, seqs, t.q, w.Hq, w.scale, 128, out_dtype=torch.bfloat16 if dtype == "bf16" else
+    out, _, _ = run_decode(m, seqs, t.q, w.Hq, w.scale, ps, out_dtype=torch.bfloat16 if dtype == "bf16" else
                            torch.float16)
     # one rounding of the output to the storage type on top of the fp32 tolerance
     half_ulp = 2.0 ** -9 if dtype == "bf16" else 2.0 ** -12
