@@ -5,16 +5,18 @@ id and writes token ``pos`` of a sequence at (page, pos % block_size).  This lib
 stores one layer's K and V as two such tensors.  Layout (a fixed part of the library's
 interface, restated here independently):
 
-    V: [num_blocks][num_kv_heads][head_dim][block_size]   (dim rows, tokens contiguous)
+    V: [num_blocks][num_kv_heads][tile], one tile per (block, head) nested
+       [token half t // 8][head_dim][8 tokens t % 8]
     K: [num_blocks][num_kv_heads][tile], one tile of block_size (16) tokens x head_dim
        elements per (block, head), in 16-byte chunks (E = 16 / element size elements each).
        Number the tokens t = 8*hi + 4*set + low and the chunks of a token's head vector
        c = 4*cq + cr; the tile stores the chunks in the nested order
        [cq][set][cr][hi][low], each chunk's E elements in order.
 
-``self.k`` holds K in the logical order [num_blocks][num_kv_heads][block_size][head_dim]
-(what attention reads); ``k_physical()`` rearranges it into the stored byte order above,
-which is what the library's device tensor must hold byte for byte.
+``self.k`` holds K in the logical order [num_blocks][num_kv_heads][block_size][head_dim] and
+``self.v`` holds V as [num_blocks][num_kv_heads][head_dim][block_size] (what attention reads);
+``k_physical()`` and ``v_physical()`` rearrange them into the stored orders above, which is what
+the library's device tensors must hold byte for byte.
 
 Slot ``s`` means block ``s // block_size``, offset ``s % block_size``; slot -1 is skipped.
 Values are held as raw storage bits (uint16 for bf16/fp16, uint32 for fp32), so append and

@@ -112,6 +112,11 @@ class Fp8CacheModel:
         v = e4m3_decode(self.v[blocks]) * self.v_scale[blocks][:, :, None, :].astype(np.float64)
         return k, v
 
+    def v_physical(self, blocks=slice(None)) -> np.ndarray:
+        """V codes in the library's tile order ([D][16] per tile): [n][H][16 * D] bytes."""
+        v = self.v[blocks]
+        return np.ascontiguousarray(v).reshape(v.shape[0], self.H, self.D * self.bs)
+
     def k_physical(self, blocks=slice(None)) -> np.ndarray:
         """K codes in the library's tile order: [n][H][16 * D] bytes."""
         k = self.k[blocks]

@@ -181,21 +181,24 @@ class PoolModel:
     # ---- prefix cache ([Serving] The Build, Step 8) ------------------------------------
     def prefix_lookup(self, tokens):
         """New sequence holding the longest registered block-aligned prefix of ``tokens``.
-        Returns (seq, matched token count)."""
+        Returns (seq, matched token count).  The prefix grows one block at a time; every
+        registered one replaces the previous hit, so the last hit is the longest."""
         s = self.new_seq()
         bs = self.block_size
-        for n in range(len(tokens) // bs * bs, 0, -bs):
-            key = tuple(int(t) for t in tokens[:n])
-            if key in self.entries:
-                blocks = self.entries[key]
-                for b in blocks:
-                    if self.refcnt[b] == 0:
-                        self.lru.remove(b)
-                    self.refcnt[b] += 1
-                self.tables[s] = list(blocks)
-                self.lens[s] = n
-                return s, n
-        return s, 0
+        hit, blocks = 0, []
+        prefix: tuple = ()
+        for k in range(len(tokens) // bs):
+            prefix = prefix + tuple(int(t) for t in tokens[k * bs:(k + 1) * bs])
+            chain = self.entries.get(prefix)
+            if chain is not None:
+                hit, blocks = len(prefix), chain
+        for b in blocks:
+            if self.refcnt[b] == 0:
+                self.lru.remove(b)
+            self.refcnt[b] += 1
+        self.tables[s] = list(blocks)
+        self.lens[s] = hit
+        return s, hit
 
     def prefix_insert(self, seq: int, tokens) -> int:
         """Register seq's full blocks under their token prefixes.  Returns how many of seq's

@@ -5,6 +5,9 @@ largest finite value, the NaN codes, the subnormal step), to a round trip over e
 to a brute-force nearest-even search over the whole code table; the quantisation to its error
 bounds and special cases; the tile layout to being a bijection with the contiguity the kernels
 rely on."""
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -107,3 +110,40 @@ def test_fp8_cache_attention_is_attention_on_dequantised_values():
     # one-token context returns the dequantised value row exactly
     one = oatt.paged_decode(q_bits, c, [[1]], [1], 0.125, q_dtype="bf16")
     assert np.array_equal(one[0, 0], V[16, 0]) and np.array_equal(one[0, 3], V[16, 1])
+
+
+def _golden(name):
+    with open(os.path.join(os.path.dirname(__file__), "golden", name)) as f:
+        return json.load(f)
+
+
+def test_fp8_k_tile_order_fixture():
+    """Hand-worked byte positions of the FP8 K tile: the offset formula, and a code written by
+    the model's append landing there (and nowhere else) in the stored order."""
+    for case in _golden("fp8_k_tile_order.json")["cases"]:
+        D, t, d, off = case["head_dim"], case["token"], case["dim"], case["byte_offset"]
+        assert fp8.k_byte_offset(t, d) == off, case
+        c = Fp8CacheModel(2, 2, D)
+        c.k[:] = 0
+        row = np.zeros((1, 2, D), dtype=np.float32)
+        row[0, 1, d] = 3.0  # amax = 3 -> code 448 (0x7E) at d, code 0 elsewhere
+        c.append(row, row, [16 + t])
+        phys = c.k_physical()
+        assert phys[1, 1, off] == 0x7E, case
+        assert np.count_nonzero(phys) == 1, case
+
+
+def test_fp8_v_tile_order_fixture():
+    """Hand-worked byte positions of the FP8 V code tile ([dimension][16 tokens])."""
+    for case in _golden("v_tile_order.json")["cases"]:
+        if case["dtype"] != "fp8":
+            continue
+        D, t, d, off = case["head_dim"], case["token"], case["dim"], case["element_offset"]
+        c = Fp8CacheModel(2, 2, D)
+        c.v[:] = 0
+        row = np.zeros((1, 2, D), dtype=np.float32)
+        row[0, 0, d] = -0.5  # amax = 0.5 -> code -448 (0xFE) at d
+        c.append(row, row, [t])
+        phys = c.v_physical()
+        assert phys[0, 0, off] == 0xFE, case
+        assert np.count_nonzero(phys) == 1, case

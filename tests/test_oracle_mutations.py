@@ -8,8 +8,11 @@ import numpy as np
 import pytest
 
 import oracle.attention as att
+import oracle.cache as ocache
+import oracle.fp8 as ofp8
 import oracle.pool as opool
 import tests.test_oracle_attention as TA
+import tests.test_oracle_fp8 as TF
 import tests.test_oracle_pool as TP
 
 
@@ -234,3 +237,26 @@ def test_prefix_lru_freed_to_free_list_caught(monkeypatch):
 
     monkeypatch.setattr(opool.PoolModel, "_release", release_always_free)
     assert _fails(*PREFIX_PINS) >= 1
+
+
+# ---- stored tile orders ---------------------------------------------------------------------
+def test_fp8_k_order_within_run_permutation_caught(monkeypatch):
+    """Tokens of a 512-byte run nested [low][hi] instead of [hi][low]: a bijection that keeps
+    every run contiguous, so only the hand-worked positions can tell it apart."""
+    def k_offset_low_hi(t, d):
+        return ((d // 64) * 2 + (t // 4) % 2) * 512 + ((t % 4) * 2 + t // 8) * 64 + d % 64
+
+    monkeypatch.setattr(ofp8, "k_byte_offset", k_offset_low_hi)
+    TF.test_k_layout_bijection_and_runs(128)  # the structural pins still pass
+    assert _fails(TF.test_fp8_k_tile_order_fixture) == 1
+
+
+def test_v_order_dimension_major_caught(monkeypatch):
+    """The 16-bit V tile stored [D][16] (dimension rows of all 16 tokens) instead of
+    [token half][D][8]."""
+    def v_dim_major(self, blocks=slice(None)):
+        v = self.v[blocks]
+        return np.ascontiguousarray(v).reshape(v.shape[0], self.H, self.D * self.bs)
+
+    monkeypatch.setattr(ocache.CacheModel, "v_physical", v_dim_major)
+    assert _fails(TP.test_v_tile_order_fixture) == 1

@@ -482,3 +482,20 @@ def test_v_tile_order_by_brute_force(dt, D):
     if esize == 2:
         # a half-wave's 16 lanes (dimensions 16 nb .. 16 nb + 15 of one half) read 256 contiguous bytes
         assert (16 * 8 * esize) == 256
+
+
+def test_v_tile_order_fixture():
+    """Hand-worked element positions of the 16-bit and fp32 V tile ([token half][D][8 tokens]):
+    a token appended with one marked element lands there in the stored order, and nowhere else."""
+    for case in _golden("v_tile_order.json")["cases"]:
+        dt = case["dtype"]
+        if dt == "fp8":
+            continue
+        D, t, d, off = case["head_dim"], case["token"], case["dim"], case["element_offset"]
+        c = CacheModel(2, 2, D, dt, fill_nan=False)
+        row = np.zeros((1, 2, D), dtype=c.v.dtype)
+        row[0, 1, d] = 5
+        c.append(row, row, [16 + t])
+        phys = c.v_physical()
+        assert phys[1, 1, off] == 5, case
+        assert np.count_nonzero(phys) == 1, case
