@@ -165,8 +165,8 @@ def measure_prefill(args, dev):
     table, _ = pool.block_tables([s], wl.blocks_for(ctx + C))
     g = torch.Generator(device=dev)
     g.manual_seed(w.seed)
-    k = torch.randn((w.num_blocks, Hkv, 16, D), generator=g, device=dev).to(torch.bfloat16)
-    v = torch.randn((w.num_blocks, Hkv, D, 16), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((w.num_blocks, Hkv, 16 * D), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((w.num_blocks, Hkv, 16 * D), generator=g, device=dev).to(torch.bfloat16)
     q = torch.randn((C, Hq, D), generator=g, device=dev).to(torch.bfloat16)
     out = torch.empty((C, Hq, D), dtype=torch.float32, device=dev)
     tb = torch.from_numpy(table[0]).to(dev)
@@ -308,8 +308,8 @@ def measure_trace(dev, choose_ps=trace_partition_size):
     g = torch.Generator(device=dev)
     g.manual_seed(seed)
     bf = torch.bfloat16
-    kc = torch.randn((N, Hkv, 16, D), generator=g, device=dev).to(bf)
-    vc = torch.randn((N, Hkv, D, 16), generator=g, device=dev).to(bf)
+    kc = torch.randn((N, Hkv, 16 * D), generator=g, device=dev).to(bf)
+    vc = torch.randn((N, Hkv, 16 * D), generator=g, device=dev).to(bf)
     src_k = torch.randn((max_adm, Hkv, D), generator=g, device=dev).to(bf)
     src_v = torch.randn((max_adm, Hkv, D), generator=g, device=dev).to(bf)
     q = torch.randn((max_active, Hq, D), generator=g, device=dev).to(bf)
@@ -477,8 +477,8 @@ def measure_fp8(args, dev, bf16_kernel_us):
         out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev)
         ws = ops.decode_workspace(w.B, w.Hq, w.D, maxL, 0, device=dev)
         if r == 0:  # the same K/V through a bf16 cache: the format's own error on this batch
-            k16 = torch.empty((w.num_blocks, w.Hkv, 16, w.D), dtype=torch.bfloat16, device=dev)
-            v16 = torch.empty((w.num_blocks, w.Hkv, w.D, 16), dtype=torch.bfloat16, device=dev)
+            k16 = torch.empty((w.num_blocks, w.Hkv, 16 * w.D), dtype=torch.bfloat16, device=dev)
+            v16 = torch.empty((w.num_blocks, w.Hkv, 16 * w.D), dtype=torch.bfloat16, device=dev)
             ops.paged_cache_append(k16, v16, kb, vb, pre_t)
             ops.paged_cache_append(k16, v16, sk, sv, step_t)
             ops.paged_cache_append_fp8(k, v, ks, vs, sk, sv, step_t)
@@ -575,8 +575,8 @@ def measure_mixed(args, dev):
     T = mw.samples + mw.chunk
     reps = []
     for r in range(R):
-        k = torch.randn((mw.num_blocks, mw.Hkv, 16, mw.D), generator=g, device=dev).to(tdt)
-        v = torch.randn((mw.num_blocks, mw.Hkv, mw.D, 16), generator=g, device=dev).to(tdt)
+        k = torch.randn((mw.num_blocks, mw.Hkv, 16 * mw.D), generator=g, device=dev).to(tdt)
+        v = torch.randn((mw.num_blocks, mw.Hkv, 16 * mw.D), generator=g, device=dev).to(tdt)
         sk = torch.randn((T, mw.Hkv, mw.D), generator=g, device=dev).to(tdt)
         sv = torch.randn((T, mw.Hkv, mw.D), generator=g, device=dev).to(tdt)
         qd = torch.randn((mw.samples, mw.Hq, mw.D), generator=g, device=dev).to(tdt)
@@ -655,8 +655,8 @@ def measure_long(args, dev):
     tables, lens = pool.block_tables(seqs, w.max_blocks_per_seq)
     g = torch.Generator(device=dev)
     g.manual_seed(w.seed)
-    k = torch.randn((w.num_blocks, w.Hkv, 16, w.D), generator=g, device=dev).to(torch.bfloat16)
-    v = torch.randn((w.num_blocks, w.Hkv, w.D, 16), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((w.num_blocks, w.Hkv, 16 * w.D), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((w.num_blocks, w.Hkv, 16 * w.D), generator=g, device=dev).to(torch.bfloat16)
     q = torch.randn((w.B, w.Hq, w.D), generator=g, device=dev).to(torch.bfloat16)
     sk = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev).to(torch.bfloat16)
     sv = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev).to(torch.bfloat16)
@@ -861,8 +861,8 @@ def main():
     side = torch.cuda.Stream(device=dev) if args.overlap else None
     reps = []
     for r in range(R):
-        k = torch.randn((w.num_blocks, w.Hkv, 16, w.D), generator=g, device=dev, dtype=torch.float32).to(tdt)
-        v = torch.randn((w.num_blocks, w.Hkv, w.D, 16), generator=g, device=dev, dtype=torch.float32).to(tdt)
+        k = torch.randn((w.num_blocks, w.Hkv, 16 * w.D), generator=g, device=dev, dtype=torch.float32).to(tdt)
+        v = torch.randn((w.num_blocks, w.Hkv, 16 * w.D), generator=g, device=dev, dtype=torch.float32).to(tdt)
         q = torch.randn((w.B, w.Hq, w.D), generator=g, device=dev, dtype=torch.float32).to(tdt)
         sk = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev, dtype=torch.float32).to(tdt)
         sv = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev, dtype=torch.float32).to(tdt)

@@ -34,8 +34,7 @@
  *     V tile: [block_size / 8][head_dim][8], i.e. element d of token t is at tile offset
  *     ((t / 8) * head_dim + d) * 8 + t % 8: eight consecutive tokens of one dimension are one
  *     16-byte operand of the P.V product, and the eight tokens of a half block own whole cache
- *     lines.  (A torch view of shape [num_blocks][num_kv_heads][head_dim][16] holds it; only the
- *     byte order inside a tile is this one.)
+ *     lines.
  *     K tile: the 16 x head_dim elements of one (block, head) are stored as 16-byte chunks
  *     (E = 16 / element size elements each, so head_dim * element size must be a multiple of 64
  *     bytes).  With token t = 8*hi + 4*set + low and chunk c = 4*cq + cr of the token's head
@@ -43,6 +42,9 @@
  *     token t is at tile offset (((cq*2 + set)*4 + cr)*8 + hi*4 + low)*E + d % E with c = d / E.
  *     This is the matrix-core operand order of the decode and prefill kernels: one 32-dimension
  *     k-step of eight tokens of a block is one contiguous 512-byte run.
+ *     Neither tile is a [16][head_dim] array: callers treat a tile as opaque bytes (the Python
+ *     binding's cache tensors are [num_blocks][num_kv_heads][16 * head_dim]) and write it only
+ *     through paged_cache_append and the fused appends.
  *   - Grouped-query attention: query head h reads KV head h / (num_q_heads / num_kv_heads).
  *   - Supported kernel shapes: block_size 16, head_dim 64 or 128, num_q_heads / num_kv_heads in
  *     {1, 2, 4, 8}.  Other values return PKV_EUNSUPPORTED (paged_cache_append and
@@ -143,8 +145,8 @@ int paged_check_inputs(const int32_t* block_tables, const int32_t* context_lens,
  * grid-stride walk, and writes nothing but (never, in practice) one word to `sink`.  Timing it
  * gives the HBM read bandwidth a plain streaming kernel achieves, the yardstick beside the 8 TB/s
  * nameplate for the bandwidth-bound decode ([Notes] "Continuous batching and PagedAttention:
- * serving many users from one GPU": every sequence's attention reads its own KV cache, so decode
- * time is set by bytes read).
+ * serving many users from one GPU", "Why batching is almost free": every sequence's attention
+ * reads its own KV cache, so decode time is set by bytes read).
  *   buf        device, 16-byte aligned; bytes a multiple of 16.
  *   sink       device uint32 (one word, caller-owned).
  *   workgroups grid size in [1, 65536] (256 threads each).
@@ -188,9 +190,9 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_he
  *                  order, max_context_len, max_blocks_per_seq, host_context_lens, or whether the
  *                  step's token comes through the fused append.  Partition boundaries are token
  *                  positions and the waves per workgroup depend on partition_size alone.
- *                  [Notes] "Continuous batching and PagedAttention: serving many users from one
- *                  GPU" names batch-dependent reduction order as the source of nondeterministic
- *                  outputs at temperature 0.
+ *                  [Chapter] "Continuous batching and PagedAttention", "Follow-up questions":
+ *                  a reduction order that moves with the batch size is what makes outputs at
+ *                  temperature 0 nondeterministic; batch-invariant kernels are the fix.
  *   workspace      device scratch of at least paged_attention_decode_workspace_bytes(...) bytes
  *                  (may be NULL when that is 0); contents on entry do not matter.
  *   host_context_lens  NULL, or a host copy of context_lens (B <= 512 entries): used only to

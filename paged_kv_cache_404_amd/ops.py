@@ -32,13 +32,35 @@ def _stream(stream) -> int:
     return s.cuda_stream
 
 
+# ---- cache tensors ---------------------------------------------------------------------------
+# One layer's K and V caches are two tensors of shape [num_blocks][num_kv_heads][16 * head_dim]:
+# entry [b, h, :] is the whole (block, head) tile, in the stored order include/pagedkv.h defines
+# (the K tile as 16-byte operand chunks, the V tile as [token half][head_dim][8 tokens]).  The last
+# axis is deliberately flat: a [16][head_dim] shape would invite k[b, h, t, d] indexing, which does
+# not name token t's dimension d.  Write the cache with paged_cache_append only.
+
+def kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype=torch.bfloat16, device="cuda"):
+    """Allocate an uninitialised (k_cache, v_cache) pair, each [num_blocks][num_kv_heads][16 * head_dim]."""
+    shape = (num_blocks, num_kv_heads, 16 * head_dim)
+    return torch.empty(shape, dtype=dtype, device=device), torch.empty(shape, dtype=dtype, device=device)
+
+
+def cache_dims(k_cache, v_cache, head_dim: int | None = None):
+    """(num_blocks, num_kv_heads, head_dim) of a cache pair; checks the flat tile shape."""
+    if k_cache.dim() != 3 or tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[2] % 16:
+        raise ValueError("k_cache and v_cache must both be [num_blocks][num_kv_heads][16 * head_dim] tiles")
+    N, H, tile = k_cache.shape
+    D = tile // 16
+    if head_dim is not None and head_dim != D:
+        raise ValueError(f"cache tiles hold head_dim {D}, the call has {head_dim}")
+    return N, H, D
+
+
 def paged_cache_append(k_cache, v_cache, key, value, slot_mapping, stream=None) -> None:
-    """k_cache [N][Hkv][16][D] and v_cache [N][Hkv][D][16] tensors holding the K and V tiles in their
-    stored orders (include/pagedkv.h); key/value [T][Hkv][D]; slot_mapping int32 [T]."""
+    """k_cache/v_cache [N][Hkv][16 * D] tiles (kv_cache); key/value [T][Hkv][D]; slot_mapping int32 [T]."""
     _dev(k_cache, v_cache, key, value, slot_mapping)
-    N, H, bs, D = k_cache.shape
-    if tuple(v_cache.shape) != (N, H, D, bs):
-        raise ValueError("v_cache must be [N][Hkv][D][block_size]")
+    N, H, D = cache_dims(k_cache, v_cache, key.shape[-1] if key.dim() == 3 else None)
+    bs = 16
     if key.dtype != k_cache.dtype or value.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
         raise TypeError("key, value and caches must share one dtype")
     if slot_mapping.dtype != torch.int32:
@@ -53,7 +75,8 @@ def paged_cache_append(k_cache, v_cache, key, value, slot_mapping, stream=None) 
 def paged_cache_copy_blocks(k_cache, v_cache, src_dst, stream=None) -> None:
     """src_dst int32 [n][2] on the GPU."""
     _dev(k_cache, v_cache, src_dst)
-    N, H, bs, D = k_cache.shape
+    N, H, D = cache_dims(k_cache, v_cache)
+    bs = 16
     if src_dst.dtype != torch.int32 or src_dst.dim() != 2 or src_dst.shape[1] != 2:
         raise ValueError("src_dst must be int32 [n][2]")
     check(lib.paged_cache_copy_blocks(k_cache.data_ptr(), v_cache.data_ptr(), src_dst.data_ptr(), src_dst.shape[0],
@@ -112,10 +135,11 @@ def _host_lens_ptr(host_context_lens):
 def _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale, partition_size,
                  workspace, host_ptr=None):
     _dev(out, query, k_cache, v_cache, block_tables, context_lens)
+    if query.dim() != 3:
+        raise ValueError("query must be [B][Hq][D]")
     B, Hq, D = query.shape
-    N, Hkv, bs, Dk = k_cache.shape
-    if Dk != D or tuple(v_cache.shape) != (N, Hkv, D, bs):
-        raise ValueError("cache shapes do not match the query")
+    N, Hkv, _ = cache_dims(k_cache, v_cache, D)
+    bs = 16
     if out.shape != query.shape:
         raise ValueError("out must be [B][Hq][D]")
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
@@ -208,10 +232,13 @@ def paged_attention_decode_reduce(out, context_lens, max_context_len, partition_
 
 def _prefill_args(out, query, k_cache, v_cache, block_table, ctx_start, scale):
     _dev(out, query, k_cache, v_cache, block_table)
+    if query.dim() != 3 or out.shape != query.shape:
+        raise ValueError("query and out must be [C][Hq][D]")
     C, Hq, D = query.shape
-    N, Hkv, bs, Dk = k_cache.shape
-    if Dk != D or tuple(v_cache.shape) != (N, Hkv, D, bs) or out.shape != query.shape:
-        raise ValueError("shape mismatch")
+    N, Hkv, _ = cache_dims(k_cache, v_cache, D)
+    bs = 16
+    if query.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+        raise TypeError("query and caches must share one dtype")
     if block_table.dtype != torch.int32:
         raise TypeError("block_table must be int32")
     if block_table.numel() * bs < ctx_start + C:
@@ -234,19 +261,8 @@ class PreparedPrefill:
 
 def paged_attention_prefill_chunk(out, query, k_cache, v_cache, block_table, ctx_start, scale, stream=None) -> None:
     """query/out [C][Hq][D]; block_table int32 [>= ceil((ctx_start + C) / 16)] of one sequence."""
-    _dev(out, query, k_cache, v_cache, block_table)
-    C, Hq, D = query.shape
-    N, Hkv, bs, Dk = k_cache.shape
-    if Dk != D or tuple(v_cache.shape) != (N, Hkv, D, bs) or out.shape != query.shape:
-        raise ValueError("shape mismatch")
-    if block_table.dtype != torch.int32:
-        raise TypeError("block_table must be int32")
-    if block_table.numel() * bs < ctx_start + C:
-        raise ValueError("block_table too short for ctx_start + C")
-    check(lib.paged_attention_prefill_chunk(out.data_ptr(), dtype_code(out.dtype), query.data_ptr(),
-                                            k_cache.data_ptr(), v_cache.data_ptr(), block_table.data_ptr(),
-                                            int(ctx_start), C, Hq, Hkv, D, bs, N, float(scale),
-                                            dtype_code(k_cache.dtype), _stream(stream)))
+    check(lib.paged_attention_prefill_chunk(*_prefill_args(out, query, k_cache, v_cache, block_table, ctx_start,
+                                                           scale), _stream(stream)))
 
 
 class PreparedDecode:
@@ -294,8 +310,11 @@ class PreparedAppend:
     def __init__(self, k_cache, v_cache, key, value, slot_mapping, stream=None):
         _dev(k_cache, v_cache, key, value, slot_mapping)
         self._keep = (k_cache, v_cache, key, value, slot_mapping)
-        N, H, bs, D = k_cache.shape
+        N, H, D = cache_dims(k_cache, v_cache)
+        bs = 16
         T = slot_mapping.numel()
+        if key.dtype != k_cache.dtype or value.dtype != k_cache.dtype or v_cache.dtype != k_cache.dtype:
+            raise TypeError("key, value and caches must share one dtype")
         if key.shape != (T, H, D) or value.shape != (T, H, D) or slot_mapping.dtype != torch.int32:
             raise ValueError("key/value must be [T][Hkv][D], slot_mapping int32 [T]")
         self.args = (k_cache.data_ptr(), v_cache.data_ptr(), key.data_ptr(), value.data_ptr(), 0, 0,
@@ -306,12 +325,13 @@ class PreparedAppend:
         check(lib.paged_cache_append(*self.args, self.stream))
 
 
-# ---- FP8 (E4M3) cache: codes uint8 k [N][Hkv][16][D] (tile order inside), v [N][Hkv][D][16];
-# ---- scales fp32 [N][Hkv][16] for K and for V.
+# ---- FP8 (E4M3) cache: code tiles uint8 k and v [N][Hkv][16 * D] (stored orders of
+# ---- include/pagedkv.h, flat for the same reason as kv_cache); scales fp32 [N][Hkv][16] for K and
+# ---- for V (entry [b, h, t] is slot t's scale).
 def fp8_cache(num_blocks: int, num_kv_heads: int, head_dim: int, device="cuda"):
     """Allocate (k, v, k_scale, v_scale) of an fp8 cache, filled with the NaN code / NaN scales."""
-    k = torch.full((num_blocks, num_kv_heads, 16, head_dim), 0x7F, dtype=torch.uint8, device=device)
-    v = torch.full((num_blocks, num_kv_heads, head_dim, 16), 0x7F, dtype=torch.uint8, device=device)
+    k = torch.full((num_blocks, num_kv_heads, 16 * head_dim), 0x7F, dtype=torch.uint8, device=device)
+    v = torch.full_like(k, 0x7F)
     ks = torch.full((num_blocks, num_kv_heads, 16), float("nan"), dtype=torch.float32, device=device)
     vs = torch.full_like(ks, float("nan"))
     return k, v, ks, vs
@@ -319,11 +339,12 @@ def fp8_cache(num_blocks: int, num_kv_heads: int, head_dim: int, device="cuda"):
 
 def _fp8_shapes(k_cache, v_cache, k_scale, v_scale):
     _dev(k_cache, v_cache, k_scale, v_scale)
-    N, H, bs, D = k_cache.shape
+    N, H, D = cache_dims(k_cache, v_cache)
+    bs = 16
     if k_cache.dtype != torch.uint8 or v_cache.dtype != torch.uint8:
         raise TypeError("fp8 caches are uint8 tensors of E4M3 codes")
-    if tuple(v_cache.shape) != (N, H, D, bs) or tuple(k_scale.shape) != (N, H, bs) or k_scale.shape != v_scale.shape:
-        raise ValueError("fp8 cache shapes: k [N][Hkv][16][D], v [N][Hkv][D][16], scales [N][Hkv][16]")
+    if tuple(k_scale.shape) != (N, H, bs) or k_scale.shape != v_scale.shape:
+        raise ValueError("fp8 scales must be [N][Hkv][16]")
     if k_scale.dtype != torch.float32 or v_scale.dtype != torch.float32:
         raise TypeError("fp8 scales are float32")
     return N, H, bs, D
@@ -457,29 +478,52 @@ class PreparedAppendFp8:
 
 def _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, pre_out, pre_query, pre_tables,
                 ctx_starts, chunk_lens, k_cache, v_cache, scale, host_dec_lens):
-    N, Hkv, bs, D = k_cache.shape
-    _dev(k_cache, v_cache)
+    """Every shape and dtype is checked before the tensors' device (so a mismatch is reported as
+    such), and all of it before the launch."""
+    N, Hkv, D = cache_dims(k_cache, v_cache)
+    bs = 16
+    if v_cache.dtype != k_cache.dtype:
+        raise TypeError("k_cache and v_cache must share one dtype")
     dtype = dtype_code(k_cache.dtype)
     B = 0 if dec_query is None else dec_query.shape[0]
     S = len(chunk_lens)
+    Hq = out_dtype = None
     if B:
-        _dev(dec_out, dec_query, dec_tables, dec_lens)
-        if dec_tables.dtype != torch.int32 or dec_lens.dtype != torch.int32 or dec_tables.shape[0] != B:
-            raise ValueError("decode tables [B][max_blocks] and lens [B] must be int32")
+        if dec_query.dim() != 3 or dec_query.shape[2] != D:
+            raise ValueError("dec_query must be [B][Hq][head_dim]")
+        if tuple(dec_out.shape) != tuple(dec_query.shape):
+            raise ValueError("dec_out must have dec_query's shape [B][Hq][D]")
+        if dec_query.dtype != k_cache.dtype:
+            raise TypeError("dec_query must have the cache dtype")
+        if dec_tables.dtype != torch.int32 or dec_lens.dtype != torch.int32:
+            raise TypeError("decode tables and lens must be int32")
+        if dec_tables.dim() != 2 or dec_tables.shape[0] != B or tuple(dec_lens.shape) != (B,):
+            raise ValueError("decode tables must be [B][max_blocks] and lens [B]")
         Hq = dec_query.shape[1]
-        out_dtype = dtype_code(dec_out.dtype)
+        out_dtype = dec_out.dtype
     if S:
-        _dev(pre_out, pre_query, pre_tables)
-        if pre_tables.dtype != torch.int32 or pre_tables.shape[0] != S:
+        if pre_query.dim() != 3 or pre_query.shape[2] != D:
+            raise ValueError("pre_query must be [rows][Hq][head_dim]")
+        if pre_query.dtype != k_cache.dtype:
+            raise TypeError("pre_query must have the cache dtype")
+        if pre_tables.dtype != torch.int32 or pre_tables.dim() != 2 or pre_tables.shape[0] != S:
             raise ValueError("prefill tables must be int32 [num_chunks][max_blocks]")
-        if pre_query.shape[0] != int(sum(chunk_lens)) or pre_out.shape != pre_query.shape:
+        if pre_query.shape[0] != int(sum(chunk_lens)) or tuple(pre_out.shape) != tuple(pre_query.shape):
             raise ValueError("pre_query / pre_out must hold sum(chunk_lens) rows")
+        if Hq is not None and pre_query.shape[1] != Hq:
+            raise ValueError("decode and prefill queries must have the same number of heads")
+        if out_dtype is not None and pre_out.dtype != out_dtype:
+            raise TypeError("dec_out and pre_out must share one dtype (one out_dtype per launch)")
         Hq = pre_query.shape[1]
-        out_dtype = dtype_code(pre_out.dtype)
+        out_dtype = pre_out.dtype
     if not B and not S:
         return None
     starts = np.ascontiguousarray(np.asarray(ctx_starts, dtype=np.int32))
     lens = np.ascontiguousarray(np.asarray(chunk_lens, dtype=np.int32))
+    if len(starts) != S:
+        raise ValueError("ctx_starts and chunk_lens must have one entry per chunk")
+    _dev(k_cache, v_cache, *((dec_out, dec_query, dec_tables, dec_lens) if B else ()),
+         *((pre_out, pre_query, pre_tables) if S else ()))
     hl, hp = _host_lens_ptr(host_dec_lens)
     keep = (starts, lens, hl)
     args = (dec_out.data_ptr() if B else None, dec_query.data_ptr() if B else None,
@@ -487,7 +531,7 @@ def _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, p
             dec_tables.shape[1] if B else 0, int(dec_max_context_len) if B else 0, hp,
             pre_out.data_ptr() if S else None, pre_query.data_ptr() if S else None,
             pre_tables.data_ptr() if S else None, pre_tables.shape[1] if S else 0,
-            starts.ctypes.data if S else None, lens.ctypes.data if S else None, S, out_dtype,
+            starts.ctypes.data if S else None, lens.ctypes.data if S else None, S, dtype_code(out_dtype),
             k_cache.data_ptr(), v_cache.data_ptr(), Hq, Hkv, D, bs, N, float(scale), dtype)
     return args, keep
 

@@ -38,8 +38,8 @@ class Mirror:
         self.opool = PoolModel(N, 16, free_order)
         _, ti = INT_VIEW[dtype]
         sentinel = int(np.array(wl.NAN_BITS[dtype], dtype=wl.storage_np_dtype(dtype)).view(INT_VIEW[dtype][0]))
-        self.k = torch.full((N, Hkv, 16, D), sentinel, dtype=ti, device="cuda").view(TORCH_DT[dtype])
-        self.v = torch.full((N, Hkv, D, 16), sentinel, dtype=ti, device="cuda").view(TORCH_DT[dtype])
+        self.k = torch.full((N, Hkv, 16 * D), sentinel, dtype=ti, device="cuda").view(TORCH_DT[dtype])
+        self.v = torch.full((N, Hkv, 16 * D), sentinel, dtype=ti, device="cuda").view(TORCH_DT[dtype])
         self.cache = CacheModel(N, Hkv, D, dtype)
 
     def new_seq(self) -> int:

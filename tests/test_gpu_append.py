@@ -62,8 +62,8 @@ def test_append_matches_oracle_bit_for_bit(dtype, Hkv, D, T):
     N = 2 * (-(-T // 16)) + 40
     free_blocks = rng.permutation(N).tolist()
     cache = CacheModel(N, Hkv, D, dtype)
-    kc = to_dev(wl.nan_filled((N, Hkv, 16, D), dtype), dtype)
-    vc = to_dev(wl.nan_filled((N, Hkv, D, 16), dtype), dtype)
+    kc = to_dev(wl.nan_filled((N, Hkv, 16 * D), dtype), dtype)
+    vc = to_dev(wl.nan_filled((N, Hkv, 16 * D), dtype), dtype)
     for _ in range(2):
         lib_slots, orc_slots = _slot_mapping(rng, free_blocks, T, N)
         kb = wl.normal_bits(rng, (T, Hkv, D), dtype)

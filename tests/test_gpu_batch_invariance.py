@@ -5,8 +5,8 @@ bits depend only on its own query, its own cached K/V and its own length: not on
 sequences share the call, which ones, in what order, on max_context_len, on the width of the
 block-table rows, on the host copy of the lengths (work order), or on whether the step's token is
 appended by the fused call.  The pages name reduction orders that move with the batch as the
-source of temperature-0 nondeterminism ([Notes] "Continuous batching and PagedAttention: serving
-many users from one GPU"); here partition boundaries are fixed token positions and the waves per
+source of temperature-0 nondeterminism ([Chapter] "Continuous batching and PagedAttention",
+"Follow-up questions"); here partition boundaries are fixed token positions and the waves per
 workgroup depend on partition_size alone (the single pass always uses 8)."""
 import numpy as np
 import pytest

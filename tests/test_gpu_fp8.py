@@ -69,7 +69,7 @@ class Fp8Mirror:
         torch.cuda.synchronize()
         kb = self.k.cpu().numpy().reshape(self.N, self.Hkv, 16 * self.D)
         assert np.array_equal(kb, self.cache.k_physical()), "K codes"
-        assert np.array_equal(self.v.cpu().numpy(), self.cache.v), "V codes"
+        assert np.array_equal(self.v.cpu().numpy(), self.cache.v_physical()), "V codes"
         assert np.array_equal(self.ks.cpu().numpy().view(np.uint32), self.cache.k_scale.view(np.uint32)), "K scales"
         assert np.array_equal(self.vs.cpu().numpy().view(np.uint32), self.cache.v_scale.view(np.uint32)), "V scales"
 
@@ -162,17 +162,16 @@ def test_decode_fp8_parity(q_dtype, Hq, Hkv, D, lens, ps):
     assert float(np.abs(got - ref).max()) <= ATOL
 
 
-def test_decode_fp8_llama_shaped_sampled():
-    """Batch 64, 32/8 heads x 128, lengths U[128, 2048], single pass: ten sequences against the oracle,
-    every output finite."""
+def test_decode_fp8_llama_shaped():
+    """Batch 64, 32/8 heads x 128, lengths U[128, 2048], single pass: every output of every
+    sequence against the oracle."""
     w = wl.llama_decode(2)
     m, seqs, rng = _build([int(L) for L in w.lens], 8, 128, 77)
     q = wl.normal_bits(rng, (w.B, 32, 128), "bf16")
     out, tables, lens_a = _decode(m, seqs, q, "bf16", w.scale, 0, host_lens=True)
-    sample = list(range(0, 64, 7))
-    ref = oatt.paged_decode(q[sample], m.cache, tables[sample], lens_a[sample], w.scale, q_dtype="bf16")
-    assert float(np.abs(out.cpu().numpy()[sample].astype(np.float64) - ref).max()) <= ATOL
     assert torch.isfinite(out).all()
+    ref = oatt.paged_decode(q, m.cache, tables, lens_a, w.scale, q_dtype="bf16")
+    assert float(np.abs(out.cpu().numpy().astype(np.float64) - ref).max()) <= ATOL
 
 
 @pytest.mark.parametrize("ps", [0, 512])

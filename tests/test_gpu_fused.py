@@ -232,10 +232,10 @@ def test_llama_shaped_step_as_benched(ps):
     assert float(np.abs(got - ref).max()) <= ATOL
 
 
-def test_long_context_step_as_benched_sampled():
+def test_long_context_step_as_benched():
     """The long-context step bench.py times (8 sequences of 32,768 tokens, 512-token partitions +
-    reduce, fused append, host lengths): two sequences against the oracle, the rest finite, and the
-    8 new tokens' cache bytes bit for bit."""
+    reduce, fused append, host lengths): every output of all 8 sequences against the oracle, and
+    the 8 new tokens' cache bytes bit for bit."""
     w = wl.long_context_decode(4)
     t = wl.decode_tensors(w)
     m, seqs = _prefix(w, t)
@@ -251,8 +251,7 @@ def test_long_context_step_as_benched_sampled():
     torch.cuda.synchronize()
     m.cache.append(t.step_k, t.step_v, slots)
     m.assert_cache_bit_exact()
-    sample = [0, 5]
-    ref = oatt.paged_decode(t.q[sample], m.cache, tables[sample], lens[sample], w.scale)
+    ref = oatt.paged_decode(t.q, m.cache, tables, lens, w.scale)
     got = out.cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all()
-    assert float(np.abs(got[sample] - ref).max()) <= ATOL
+    assert float(np.abs(got - ref).max()) <= ATOL

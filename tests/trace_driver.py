@@ -77,8 +77,8 @@ def run_trace(seed: int = 3, num_blocks: int = 12288, n_requests: int = 512, max
 
         _, ti = INT_VIEW[dtype]
         sentinel = int(np.array(wl.NAN_BITS[dtype], dtype=wl.storage_np_dtype(dtype)).view(INT_VIEW[dtype][0]))
-        kc = torch.full((num_blocks, Hkv, 16, D), sentinel, dtype=ti, device="cuda").view(TORCH_DT[dtype])
-        vc = torch.full((num_blocks, Hkv, D, 16), sentinel, dtype=ti, device="cuda").view(TORCH_DT[dtype])
+        kc = torch.full((num_blocks, Hkv, 16 * D), sentinel, dtype=ti, device="cuda").view(TORCH_DT[dtype])
+        vc = torch.full((num_blocks, Hkv, 16 * D), sentinel, dtype=ti, device="cuda").view(TORCH_DT[dtype])
         cache = CacheModel(num_blocks, Hkv, D, dtype)
         max_ctx_cap = 16 * num_blocks
         ws = ops.decode_workspace(max_active, Hq, D, max_ctx_cap, partition_size, device="cuda")
