@@ -214,6 +214,29 @@ int paged_attention_decode(void* out, int32_t out_dtype, const void* query, cons
                            const int32_t* host_context_lens, pkv_stream_t stream);
 
 /*
+ * paged_attention_decode_noalloc - paged_attention_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments without workspace / workspace_bytes, the same kernels and results, bit for bit.
+ * The split-K partials live in a static device array of the library, PKV_NOALLOC_SCRATCH_BYTES
+ * per GPU, held by each GPU the call runs on until the process ends; its address on a device is
+ * looked up once, on the first call with that device current (the stream must belong to the
+ * current device).  The call allocates nothing, then or later.
+ *   - PKV_EINVAL, before anything else, when the partials need more than
+ *     PKV_NOALLOC_SCRATCH_BYTES (paged_attention_decode_workspace_bytes(...) > the limit); a
+ *     single pass (partition_size 0 or -1) needs none.
+ *   - Every call on one GPU shares that GPU's array, and a call's partials are written and read
+ *     by its own two launches: calls that overlap on one GPU (concurrent streams, or host threads)
+ *     race.  Serialise them.  Nothing in the array needs an initial value.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+int paged_attention_decode_noalloc(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                   int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                   int32_t max_context_len, float scale, int32_t partition_size, int32_t dtype,
+                                   const int32_t* host_context_lens, pkv_stream_t stream);
+
+/*
  * paged_attention_decode_partitions / paged_attention_decode_reduce - the two launches of
  * paged_attention_decode when partition_size > 0, exposed separately (same arguments) so that a
  * caller can time or overlap them.  _partitions writes out[b] directly for every sequence that

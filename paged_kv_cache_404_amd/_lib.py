@@ -22,6 +22,9 @@ PKV_BF16 = 2
 # partition_size value: a batch-adaptive single pass (faster on short contexts, not batch invariant).
 PKV_SINGLE_PASS_ADAPTIVE = -1
 
+# Size of the static device scratch behind paged_attention_decode_noalloc, per GPU.
+PKV_NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
+
 
 class PagedKVError(RuntimeError):
     def __init__(self, status: int, message: str):
@@ -57,6 +60,8 @@ _SIGS = {
     "paged_attention_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "paged_attention_decode": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp]),
+    "paged_attention_decode_noalloc": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                 _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp]),
     "paged_attention_decode_partitions": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                                     _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp]),
     "paged_attention_decode_reduce": (C.c_int, [_vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),

@@ -27,6 +27,7 @@
 // more than 2^8 (lazy rescaling: exact, and p stays <= 256), which makes rescaling rare.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 #include "decode_part.h"
@@ -225,7 +226,8 @@ Plan make_plan(int32_t B, int32_t Hq, int32_t D, int32_t max_ctx, int32_t partit
 int validate(const char* fn, void* out, int32_t out_dtype, const void* query, const void* k_cache,
              const void* v_cache, const int32_t* block_tables, const int32_t* context_lens, int32_t B, int32_t Hq,
              int32_t Hkv, int32_t D, int32_t bs, int32_t max_blocks, int32_t num_blocks, int32_t max_ctx,
-             int32_t partition_size, const void* workspace, size_t workspace_bytes, int32_t dtype) {
+             int32_t partition_size, const void* workspace, size_t workspace_bytes, int32_t dtype,
+             bool check_workspace = true) {
   if (!valid_dtype(dtype)) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
   if (out_dtype != PKV_F32 && out_dtype != dtype)
     return fail(PKV_EINVAL, "%s: out_dtype must be PKV_F32 or the input dtype", fn);
@@ -247,7 +249,7 @@ int validate(const char* fn, void* out, int32_t out_dtype, const void* query, co
   if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens)
     return fail(PKV_EINVAL, "%s: NULL pointer", fn);
   const Plan pl = make_plan(B, Hq, D, max_ctx, partition_size);
-  if (pl.need_bytes > 0 && (!workspace || workspace_bytes < pl.need_bytes))
+  if (check_workspace && pl.need_bytes > 0 && (!workspace || workspace_bytes < pl.need_bytes))
     return fail(PKV_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, pl.need_bytes, workspace_bytes);
   const uintptr_t al = reinterpret_cast<uintptr_t>(query) | reinterpret_cast<uintptr_t>(k_cache) |
                        reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(workspace);
@@ -546,4 +548,75 @@ extern "C" int paged_attention_decode_newest(void* out, int32_t out_dtype, const
   if (st != PKV_OK) return st;
   return paged_attention_decode_reduce(out, out_dtype, context_lens, B, num_q_heads, head_dim, max_context_len,
                                        partition_size, workspace, workspace_bytes, stream);
+}
+
+// ------------------------------------------------------------------------------------------
+// paged_attention_decode_noalloc: the split-K workspace comes from a fixed device array of the
+// library instead of the caller, for callers that cannot allocate device memory.
+// ------------------------------------------------------------------------------------------
+namespace pkv {
+namespace {
+
+constexpr size_t kScratchBytes = static_cast<size_t>(PKV_NOALLOC_SCRATCH_BYTES);
+constexpr int kMaxDevices = 64;
+
+// One copy per GPU, held until the process ends.  In host code the name is only a stand-in for
+// the symbol: the device address of each GPU's copy is looked up once (scratch_on_current_device)
+// and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`, looked up on the first call on that
+// device (with it current) and kept.
+int scratch_on_current_device(const char* fn, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PKV_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_EUNSUPPORTED, "%s: device %d beyond %d", fn, dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(PKV_EHIP, "%s: hipGetSymbolAddress(scratch) on device %d: %s", fn, dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+}  // namespace pkv
+
+extern "C" int paged_attention_decode_noalloc(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                              const void* v_cache, const int32_t* block_tables,
+                                              const int32_t* context_lens, int32_t B, int32_t num_q_heads,
+                                              int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                              int32_t max_blocks_per_seq, int32_t num_blocks,
+                                              int32_t max_context_len, float scale, int32_t partition_size,
+                                              int32_t dtype, const int32_t* host_context_lens, pkv_stream_t stream) {
+  const char* fn = "paged_attention_decode_noalloc";
+  const size_t need = paged_attention_decode_workspace_bytes(B, num_q_heads, head_dim, max_context_len,
+                                                             partition_size);
+  if (need > kScratchBytes)
+    return fail(PKV_EINVAL, "%s: split-K partials need %zu bytes, more than the %zu-byte static scratch", fn, need,
+                kScratchBytes);
+  // Everything the host can check is checked before the scratch is touched.
+  int st = validate(fn, out, out_dtype, query, k_cache, v_cache, block_tables, context_lens, B, num_q_heads,
+                    num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                    partition_size, nullptr, 0, dtype, /*check_workspace=*/false);
+  if (st != PKV_OK || B == 0 || max_context_len == 0) return st;
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_on_current_device(fn, &ws);
+    if (st != PKV_OK) return st;
+  }
+  // The partials need no initial value: every one the reduce reads is written by the partition
+  // pass of the same call.
+  return paged_attention_decode(out, out_dtype, query, k_cache, v_cache, block_tables, context_lens, B, num_q_heads,
+                                num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks, max_context_len,
+                                scale, partition_size, ws, need ? kScratchBytes : 0, dtype, host_context_lens,
+                                stream);
 }

@@ -164,6 +164,16 @@ def paged_attention_decode(out, query, k_cache, v_cache, block_tables, context_l
     check(lib.paged_attention_decode(*args, _stream(stream)))
 
 
+def paged_attention_decode_noalloc(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                                   partition_size=0, stream=None, host_context_lens=None) -> None:
+    """paged_attention_decode with the split-K partials in the library's static per-GPU scratch
+    (no workspace argument, nothing allocated).  Calls that overlap on one GPU race."""
+    hl, hp = _host_lens_ptr(host_context_lens)
+    args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                        partition_size, None, hp)
+    check(lib.paged_attention_decode_noalloc(*args[:17], args[19], args[20], _stream(stream)))
+
+
 def _fused_args(args, new_key, new_value):
     """Argument tuple of the fused-append entry points from a _decode_args tuple."""
     _dev(new_key, new_value)

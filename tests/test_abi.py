@@ -126,3 +126,18 @@ def test_pool_sanitizer_build(tmp_path):
     r = subprocess.run([str(exe), "20000"], capture_output=True, text=True, env=env)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "ok" in r.stdout
+
+
+def test_noalloc_decode_rejects_partials_beyond_its_scratch():
+    """paged_attention_decode_noalloc refuses, before touching any device, a call whose split-K
+    partials exceed the static scratch; the limit is the header's."""
+    L = pkv.lib
+    assert _lib.PKV_NOALLOC_SCRATCH_BYTES == 16 * 1024 * 1024
+    text = open(HEADER).read()
+    assert re.search(r"#define PKV_NOALLOC_SCRATCH_BYTES \(16 \* 1024 \* 1024\)", text)
+    p = 1 << 12
+    need = L.paged_attention_decode_workspace_bytes(64, 32, 128, 65536, 512)
+    assert need > _lib.PKV_NOALLOC_SCRATCH_BYTES
+    st = L.paged_attention_decode_noalloc(p, pkv.PKV_F32, p, p, p, p, p, 64, 32, 8, 128, 16, 4096, 100000, 65536,
+                                          0.1, 512, pkv.PKV_BF16, NULL, NULL)
+    assert st == pkv.PKV_EINVAL and "static scratch" in _lib.last_error()
