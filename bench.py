@@ -55,6 +55,8 @@ def parse():
                     help="do not pass the host copy of the context lengths (longest-first work order)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the chunked-prefill and long-context measurements reported beside the main line")
+    ap.add_argument("--extras", default="prefill,long,prefix,fp8,mixed,trace",
+                    help="comma-separated side lines to run beside the main line (default: all of them)")
     mode = ap.add_mutually_exclusive_group()
     mode.add_argument("--overlap", action="store_true",
                     help="time paged_attention_decode_newest with paged_cache_append on a second stream, each "
@@ -542,18 +544,45 @@ def measure_fp8(args, dev, bf16_kernel_us):
     }
 
 
-def measure_mixed(args, dev):
-    """The mixed prefix-sharing step: 16 samples forked from a 2,048-token prefix decode one token
-    each (single pass, longest first) and a 512-row chunk is prefilled after 4,096 cached tokens.
-    Attention as one paged_attention_mixed launch against the two separate launches; the step adds
-    the paged_cache_append of its 16 + 512 tokens."""
+def _spin_cycles_per_ms(torch, stream):
+    """Cycles of torch.cuda._sleep per millisecond on this device (for spins that hide enqueue time)."""
+    probe = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    torch.cuda.synchronize()
+    probe[0].record(stream)
+    torch.cuda._sleep(1 << 20)
+    probe[1].record(stream)
+    torch.cuda.synchronize()
+    return (1 << 20) / max(probe[0].elapsed_time(probe[1]), 1e-3)
+
+
+def _spun_avg_us(torch, stream, fn, n, spin_cycles):
+    """Average device time of fn(i), i < n, run back to back behind a bounded spin kernel: the host
+    enqueues all n calls while the spin runs, so the one event pair after the spin times GPU work
+    only (calls whose enqueue takes longer than their kernels would otherwise time the host)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(spin_cycles)
+    e0.record(stream)
+    for i in range(n):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def _mixed_case(args, dev, prefix_len, n, spin):
+    """One prefix-sharing step: 16 samples forked from a prefix_len-token prefix decode one token
+    each, a 512-row chunk is prefilled after 4,096 cached tokens.  Times (HIP events behind a spin)
+    the decode alone (plain single pass, grouped 2 and 4 samples per workgroup), the prefill alone,
+    both as separate launches and as one mixed launch (plain and grouped), and the step = the
+    copy-on-write block copies (if any) + the append of its 16 + 512 tokens + attention."""
     import numpy as np
     import torch
 
     import workloads as wl
     from paged_kv_cache_404_amd import BlockPool, ops
 
-    mw = wl.mixed_step(5, prefix_len=2048)
+    mw = wl.mixed_step(5, prefix_len=prefix_len)
     pool = BlockPool(mw.num_blocks, 16, mw.free_order)
     s0 = pool.new_seq()
     pool.append(s0, mw.prefix_len)
@@ -561,9 +590,9 @@ def measure_mixed(args, dev):
     pf = pool.new_seq()
     pool.append(pf, mw.ctx_start)
     st, _, step_slots, cow = pool.append_many(samples + [pf], [1] * mw.samples + [mw.chunk])
-    assert st == 0 and len(cow) == 0
-    dtab, dlens = pool.block_tables(samples, -(-(mw.prefix_len + 1) // 16))
-    ptab, _ = pool.block_tables([pf], -(-(mw.ctx_start + mw.chunk) // 16))
+    assert st == 0
+    dtab, dlens = pool.block_tables(samples, wl.blocks_for(mw.prefix_len + 1))
+    ptab, _ = pool.block_tables([pf], wl.blocks_for(mw.ctx_start + mw.chunk))
     cache_bytes = 2 * mw.num_blocks * mw.Hkv * 16 * mw.D * 2
     R = max(1, math.ceil((1 << 30) / cache_bytes))
     g = torch.Generator(device=dev)
@@ -572,7 +601,9 @@ def measure_mixed(args, dev):
     dt_t, dl_t = torch.from_numpy(dtab).to(dev), torch.from_numpy(dlens).to(dev)
     pt_t = torch.from_numpy(ptab).to(dev)
     slots_t = torch.from_numpy(step_slots).to(dev)
+    cow_t = torch.from_numpy(np.ascontiguousarray(cow, dtype=np.int32).reshape(-1, 2)).to(dev)
     T = mw.samples + mw.chunk
+    mcl = int(dlens.max())
     reps = []
     for r in range(R):
         k = torch.randn((mw.num_blocks, mw.Hkv, 16 * mw.D), generator=g, device=dev).to(tdt)
@@ -583,59 +614,141 @@ def measure_mixed(args, dev):
         qp = torch.randn((mw.chunk, mw.Hq, mw.D), generator=g, device=dev).to(tdt)
         od = torch.empty((mw.samples, mw.Hq, mw.D), dtype=torch.float32, device=dev)
         op = torch.empty((mw.chunk, mw.Hq, mw.D), dtype=torch.float32, device=dev)
-        app = ops.PreparedAppend(k, v, sk, sv, slots_t)
-        dec = ops.PreparedDecode(od, qd, k, v, dt_t, dl_t, int(dlens.max()), mw.scale, 0, None,
-                                 host_context_lens=dlens)
-        pre = ops.PreparedPrefill(op, qp, k, v, pt_t[0], mw.ctx_start, mw.scale)
-        mix = ops.PreparedMixed(od, qd, dt_t, dl_t, int(dlens.max()), op, qp, pt_t, [mw.ctx_start], [mw.chunk],
-                                k, v, mw.scale, host_dec_lens=dlens)
-        reps.append((app, dec, pre, mix))
+        ws = ops.decode_workspace(mw.samples, mw.Hq, mw.D, mcl, 512)
+        mix_args = (od, qd, dt_t, dl_t, mcl, op, qp, pt_t, [mw.ctx_start], [mw.chunk], k, v, mw.scale)
+        reps.append({
+            "copy": (lambda k=k, v=v: ops.paged_cache_copy_blocks(k, v, cow_t)) if len(cow) else (lambda: None),
+            "append": ops.PreparedAppend(k, v, sk, sv, slots_t),
+            "dec": ops.PreparedDecode(od, qd, k, v, dt_t, dl_t, mcl, mw.scale, 0, None, host_context_lens=dlens),
+            "dec_p512": ops.PreparedDecode(od, qd, k, v, dt_t, dl_t, mcl, mw.scale, 512, ws, host_context_lens=dlens),
+            "dec_g2": ops.PreparedDecode(od, qd, k, v, dt_t, dl_t, mcl, mw.scale, 0, None, group_size=2),
+            "dec_g4": ops.PreparedDecode(od, qd, k, v, dt_t, dl_t, mcl, mw.scale, 0, None, group_size=4),
+            "dec_g2_p512": ops.PreparedDecode(od, qd, k, v, dt_t, dl_t, mcl, mw.scale, 512, ws, group_size=2),
+            "pre": ops.PreparedPrefill(op, qp, k, v, pt_t[0], mw.ctx_start, mw.scale),
+            "mix": ops.PreparedMixed(*mix_args, host_dec_lens=dlens),
+            "mix_g2_p512": ops.PreparedMixed(*mix_args, dec_group_size=2, dec_partition_size=512, workspace=ws),
+        })
     stream = torch.cuda.current_stream()
 
-    def events(fn, n):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(n):
-            fn(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / n
+    def run(*names):
+        def fn(i):
+            r = reps[i % R]
+            for nm in names:
+                r[nm]()
+        return fn
 
-    def separate(i):
-        app, dec, pre, _ = reps[i % R]
-        dec()
-        pre()
-
-    def unified(i):
-        reps[i % R][3]()
-
-    def step_sep(i):
-        reps[i % R][0]()
-        separate(i)
-
-    def step_uni(i):
-        reps[i % R][0]()
-        unified(i)
-
-    n = max(20, args.steps // 4)
-    for fn in (separate, unified):
-        for i in range(5):
-            fn(i)
-    t_sep = events(separate, n)
-    t_uni = events(unified, n)
-    s_sep = events(step_sep, n)
-    s_uni = events(step_uni, n)
-    t_dec = events(lambda i: reps[i % R][1](), n)
-    t_pre = events(lambda i: reps[i % R][2](), n)
+    for nm in reps[0]:
+        for i in range(3):
+            run(nm)(i)
+    t = {key: _spun_avg_us(torch, stream, run(*names), n, spin) for key, names in (
+        ("decode", ("dec",)), ("decode_split512", ("dec_p512",)), ("decode_grouped_2", ("dec_g2",)),
+        ("decode_grouped_4", ("dec_g4",)), ("decode_grouped_2_split512", ("dec_g2_p512",)),
+        ("prefill", ("pre",)), ("separate", ("dec", "pre")), ("separate_grouped", ("dec_g2_p512", "pre")),
+        ("mixed", ("mix",)), ("mixed_grouped", ("mix_g2_p512",)),
+        ("step_separate", ("copy", "append", "dec", "pre")), ("step_mixed", ("copy", "append", "mix")),
+        ("step_mixed_grouped", ("copy", "append", "mix_g2_p512")), ("copies_and_append", ("copy", "append")))}
+    # Algorithmic decode bytes: every distinct cached token once (the shared prefix's blocks are
+    # the same physical blocks in all 16 tables) plus each sample's own tokens, K and V of the 8 KV
+    # heads, and the queries.  Logical bytes count each sample's whole context.
+    shared_blocks = 0
+    for j in range(dtab.shape[1]):
+        if (dtab[:, j] == dtab[0, j]).all() and dtab[0, j] >= 0:
+            shared_blocks += 1
+        else:
+            break
+    shared_tok = shared_blocks * 16
+    tok_bytes = mw.Hkv * mw.D * 2 * 2
+    q_bytes = mw.samples * mw.Hq * mw.D * 2
+    unique = (shared_tok + int(np.sum(dlens - shared_tok))) * tok_bytes + q_bytes
+    logical = int(np.sum(dlens)) * tok_bytes + q_bytes
+    pairs = sum(mw.ctx_start + i + 1 for i in range(mw.chunk))
+    flops = pairs * mw.Hq * 4 * mw.D
+    best_key = min(("decode_grouped_2", "decode_grouped_4", "decode_grouped_2_split512"), key=lambda x: t[x])
+    best_dec = t[best_key]
+    ach = unique / (best_dec * 1e-6) / 1e9
+    pre_tf = flops / (t["prefill"] * 1e-6) / 1e12
     return {
-        "workload": "mixed_step_16_samples_prefix2048_plus_chunk512_ctx4096_gqa32x8_d128_bf16",
-        "attention_us": {"separate_launches": round(t_sep, 2), "mixed_launch": round(t_uni, 2),
-                         "decode_alone": round(t_dec, 2), "prefill_alone": round(t_pre, 2)},
-        "step_us_with_append": {"separate_launches": round(s_sep, 2), "mixed_launch": round(s_uni, 2)},
-        "mixed_speedup": round(t_sep / t_uni, 3),
+        "workload": f"mixed_step_16_samples_prefix{prefix_len}_plus_chunk512_ctx4096_gqa32x8_d128_bf16",
+        "block_copies": int(len(cow)),
+        "shared_prefix_tokens": shared_tok,
+        "decode_unique_bytes": unique,
+        "decode_logical_bytes": logical,
+        "prefill_flops": flops,
+        "us": {k: round(x, 2) for k, x in t.items()},
+        "decode_grouped_speedup": round(t["decode"] / best_dec, 2),
+        "mixed_grouped_speedup_over_separate": round(t["separate"] / t["mixed_grouped"], 3),
+        "step_speedup": round(t["step_separate"] / min(t["step_mixed"], t["step_mixed_grouped"]), 3),
+        "decode_roofline": {"bound": "hbm", "kernel": f"decode_group_kernel ({best_key})", "achieved": round(ach, 1),
+                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
+                            "traffic": None,
+                            "note": "unique algorithmic bytes (each distinct cached token once + queries)"},
+        "decode_plain_unique_frac": round(unique / (t["decode"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+        "decode_logical_gbs": {"plain": round(logical / (t["decode"] * 1e-6) / 1e9, 1),
+                               "grouped": round(logical / (best_dec * 1e-6) / 1e9, 1)},
+        "prefill_roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": round(pre_tf, 2),
+                             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(pre_tf / PEAK_BF16_TFLOPS, 4),
+                             "traffic": None},
         "replicas": R,
     }
+
+
+def cpu_baseline_mixed(seconds: float):
+    """The oracle on the prefix-sharing step: the 16 samples' decode over their 2,049 tokens, whole,
+    and the prefill of the first R chunk rows (R grown until the prefill sample takes about
+    `seconds`), its time scaled to the chunk's 512 rows by their (row, key) pairs."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import workloads as wl
+    from oracle import CacheModel, PoolModel
+    from oracle import attention as oatt
+
+    mw = wl.mixed_step(5, prefix_len=2048)
+    rng = np.random.default_rng(1055)
+    pool = PoolModel(mw.num_blocks, 16, mw.free_order)
+    cache = CacheModel(mw.num_blocks, mw.Hkv, mw.D, "bf16", fill_nan=True)
+    s0 = pool.new_seq()
+    slots, _ = pool.append(s0, mw.prefix_len)
+    cache.append(wl.normal_bits(rng, (mw.prefix_len, mw.Hkv, mw.D), "bf16"),
+                 wl.normal_bits(rng, (mw.prefix_len, mw.Hkv, mw.D), "bf16"), slots)
+    samples = [s0] + [pool.fork(s0) for _ in range(mw.samples - 1)]
+    for s in samples:
+        sl, cw = pool.append(s, 1)
+        cache.copy_blocks(cw)
+        cache.append(wl.normal_bits(rng, (1, mw.Hkv, mw.D), "bf16"), wl.normal_bits(rng, (1, mw.Hkv, mw.D), "bf16"), sl)
+    q = wl.normal_bits(rng, (mw.samples, mw.Hq, mw.D), "bf16")
+    tables, lens = pool.block_tables(samples, len(pool.tables[s0]))
+    t0 = time.perf_counter()
+    oatt.paged_decode(q, cache, tables, lens, mw.scale)
+    dec_s = time.perf_counter() - t0
+    pre = cpu_baseline_prefill(mw.ctx_start, mw.Hq, mw.Hkv, mw.D, mw.scale, seconds)
+    flops = sum(mw.ctx_start + i + 1 for i in range(mw.chunk)) * mw.Hq * 4 * mw.D
+    pre_s = flops / (pre["value"] * 1e12)
+    step_s = dec_s + pre_s
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": round(1.0 / step_s, 4), "unit": "steps/s", "cores": int(threads), "kind": "oracle",
+            "us_per_step": round(step_s * 1e6, 1),
+            "sample": (f"decode of all 16 samples ({dec_s:.2f} s) + prefill {pre['sample']}, scaled to 512 rows "
+                       f"({pre_s:.2f} s); numpy fp64")}
+
+
+def measure_mixed(args, dev):
+    """The mixed prefix-sharing step (a 2,048-token shared prefix), and its copy-on-write variant
+    (2,040 tokens: the partial last prefix block is copied for 15 of the 16 samples)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    spin = int(_spin_cycles_per_ms(torch, stream) * 50)
+    n = max(20, args.steps // 4)
+    res = _mixed_case(args, dev, 2048, n, spin)
+    res["copy_on_write_variant"] = _mixed_case(args, dev, 2040, n, spin)
+    res["timing"] = (f"{n} back-to-back calls behind a 50 ms spin, one HIP event pair (device time only); "
+                     "grouped = paged_attention_decode_grouped / paged_attention_mixed with dec_group_size "
+                     "(2 samples per workgroup), split512 = 512-token partitions + reduce; every decode variant's "
+                     "outputs are bit for bit the plain decode's with the same partition size")
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_mixed(args.cpu_seconds / 2)
+    return res
 
 
 def measure_long(args, dev):
@@ -1024,17 +1137,24 @@ def main():
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         res["cpu_baseline"]["cpu_model"] = cpu_model()
         res["cpu_baseline"]["single_core"] = cpu_baseline_one_core(args)
+    extras = set(args.extras.split(","))
     if not args.no_extra and args.workload == "llama":
         del reps
         torch.cuda.empty_cache()
-        res["prefill"] = measure_prefill(args, dev)
-        res["long_context"] = measure_long(args, dev)
-        if not args.no_cpu_baseline:
-            res["long_context"]["cpu_baseline"] = cpu_baseline(wl.long_context_decode(4), args.cpu_seconds / 2,
-                                                               max_seqs=1)
-        res["prefix_cache"] = measure_prefix_cache()
-        res["fp8_cache"] = measure_fp8(args, dev, part_us)
-        res["mixed_step"] = measure_mixed(args, dev)
+        if "prefill" in extras:
+            res["prefill"] = measure_prefill(args, dev)
+        if "long" in extras:
+            res["long_context"] = measure_long(args, dev)
+            if not args.no_cpu_baseline:
+                res["long_context"]["cpu_baseline"] = cpu_baseline(wl.long_context_decode(4), args.cpu_seconds / 2,
+                                                                   max_seqs=1)
+        if "prefix" in extras:
+            res["prefix_cache"] = measure_prefix_cache()
+        if "fp8" in extras:
+            res["fp8_cache"] = measure_fp8(args, dev, part_us)
+        if "mixed" in extras:
+            res["mixed_step"] = measure_mixed(args, dev)
+    if not args.no_extra and args.workload == "llama" and "trace" in extras:
         res["trace"] = measure_trace(dev)
         med = res["trace"].pop("_median_step_lens")
         if not args.no_cpu_baseline:

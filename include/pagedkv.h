@@ -214,6 +214,29 @@ int paged_attention_decode(void* out, int32_t out_dtype, const void* query, cons
                            const int32_t* host_context_lens, pkv_stream_t stream);
 
 /*
+ * paged_attention_decode_grouped - paged_attention_decode for batches in which sequences share
+ * cached blocks.  [Chapter] "PagedAttention: KV cache memory": several samples of one answer, or
+ * conversations with a common prefix, point at the same physical blocks (pkv_seq_fork,
+ * pkv_prefix_lookup).  Sequences group_size * k .. group_size * k + group_size - 1 run in one
+ * workgroup per KV head (and partition), their query heads side by side in the matrix columns; a
+ * 32-token step whose two blocks are the same in every member's table is read from memory once
+ * for the whole group, a step whose blocks differ is run once per member.  Order the batch so that
+ * sequences sharing a prefix are adjacent; any batch is correct, sharing only saves reads.
+ *   group_size  1 (exactly paged_attention_decode), or a size with group_size * (num_q_heads /
+ *               num_kv_heads) equal to 8 or 16 (PKV_EUNSUPPORTED otherwise; bf16 / fp16 only).
+ *   Other arguments as paged_attention_decode (no host_context_lens: groups run in batch order).
+ * Output: bit for bit that of paged_attention_decode with the same partition_size, so the batch
+ * invariance stated there holds here too, across group sizes as well.  K/V values must be finite
+ * (a member's zero weights meet the other members' values in the shared products).
+ */
+int paged_attention_decode_grouped(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                   const void* v_cache, const int32_t* block_tables, const int32_t* context_lens,
+                                   int32_t B, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                   int32_t max_context_len, float scale, int32_t partition_size, void* workspace,
+                                   size_t workspace_bytes, int32_t dtype, int32_t group_size, pkv_stream_t stream);
+
+/*
  * paged_attention_decode_noalloc - paged_attention_decode for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the
  * same arguments without workspace / workspace_bytes, the same kernels and results, bit for bit.
@@ -336,28 +359,36 @@ int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const void* quer
  * paged_attention_mixed - one launch for a continuous-batching step's attention: a decode batch
  * and up to 16 prefill chunks ([Chapter] "How the scheduler works" and [Notes] "Prefill gets in the
  * way": a step carries the running sequences' decode tokens and a chunk of a new prompt).  The
- * decode part is paged_attention_decode with partition_size 0 (single pass); chunk i is
- * paged_attention_prefill_chunk over its own table row; outputs are bit for bit theirs.  Decode
- * workgroups are dispatched first, so their cache streaming overlaps the prefill tiles' matrix
- * work.  Either part may be empty (B_dec = 0 or num_chunks = 0).
+ * decode part is paged_attention_decode (dec_group_size 1) or paged_attention_decode_grouped with
+ * dec_partition_size; chunk i is paged_attention_prefill_chunk over its own table row; outputs
+ * are bit for bit theirs.  Decode workgroups are dispatched first, so their cache streaming
+ * overlaps the prefill tiles' matrix work.  With split-K partitions, the decode's log-sum-exp
+ * merge (paged_attention_decode_reduce) is enqueued after the launch.  Either part may be empty
+ * (B_dec = 0 or num_chunks = 0).
  *   decode:  dec_out [B_dec][Hq][D] (out_dtype), dec_query [B_dec][Hq][D], dec_block_tables
- *            [B_dec][dec_max_blocks], dec_context_lens [B_dec] (device); dec_max_context_len and
- *            host_dec_context_lens (NULL or a host copy, for the longest-first order) as in
- *            paged_attention_decode; B_dec <= 512.
+ *            [B_dec][dec_max_blocks], dec_context_lens [B_dec] (device); dec_max_context_len,
+ *            host_dec_context_lens (NULL or a host copy, for the work order; ignored when grouped),
+ *            dec_partition_size and workspace / workspace_bytes
+ *            (paged_attention_decode_workspace_bytes(B_dec, Hq, D, dec_max_context_len,
+ *            dec_partition_size)) as in paged_attention_decode.
+ *            dec_group_size: 1, or the size with 8 matrix columns (8 / (Hq / Hkv) sequences; 2 when
+ *            Hq / Hkv is 8) to run sequences dec_group_size to a workgroup and read the blocks they
+ *            share once (paged_attention_decode_grouped).
  *   prefill: chunk i has host_chunk_lens[i] rows at positions host_ctx_starts[i] + r, packed one
  *            chunk after another in pre_query / pre_out ([sum of lengths][Hq][D]); its block table
  *            is row i of pre_block_tables [num_chunks][pre_max_blocks] (device); the chunks' K/V
  *            are already appended.  Starts and lengths are host arrays (they size the grid).
- *   group size Hq / Hkv must be 4 or 8 (PKV_EUNSUPPORTED otherwise); bf16 or fp16; head_dim 64/128.
+ *   group size Hq / Hkv in {1, 2, 4, 8}; bf16 or fp16; head_dim 64/128.
  */
 int paged_attention_mixed(void* dec_out, const void* dec_query, const int32_t* dec_block_tables,
                           const int32_t* dec_context_lens, int32_t B_dec, int32_t dec_max_blocks,
-                          int32_t dec_max_context_len, const int32_t* host_dec_context_lens, void* pre_out,
-                          const void* pre_query, const int32_t* pre_block_tables, int32_t pre_max_blocks,
-                          const int32_t* host_ctx_starts, const int32_t* host_chunk_lens, int32_t num_chunks,
-                          int32_t out_dtype, const void* k_cache, const void* v_cache, int32_t num_q_heads,
-                          int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks, float scale,
-                          int32_t dtype, pkv_stream_t stream);
+                          int32_t dec_max_context_len, const int32_t* host_dec_context_lens,
+                          int32_t dec_partition_size, int32_t dec_group_size, void* workspace,
+                          size_t workspace_bytes, void* pre_out, const void* pre_query,
+                          const int32_t* pre_block_tables, int32_t pre_max_blocks, const int32_t* host_ctx_starts,
+                          const int32_t* host_chunk_lens, int32_t num_chunks, int32_t out_dtype, const void* k_cache,
+                          const void* v_cache, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t block_size, int32_t num_blocks, float scale, int32_t dtype, pkv_stream_t stream);
 
 /* ============================== FP8 K/V cache ============================== */
 /*

@@ -60,6 +60,8 @@ _SIGS = {
     "paged_attention_decode_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "paged_attention_decode": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp]),
+    "paged_attention_decode_grouped": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                 _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _i32, _vp]),
     "paged_attention_decode_noalloc": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
                                                  _i32, _i32, _i32, _f32, _i32, _i32, _vp, _vp]),
     "paged_attention_decode_partitions": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32,
@@ -77,8 +79,9 @@ _SIGS = {
                                                            _i32, _vp, _vp]),
     "paged_attention_prefill_chunk": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                                 _i32, _f32, _i32, _vp]),
-    "paged_attention_mixed": (C.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
-                                        _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp]),
+    "paged_attention_mixed": (C.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _sz, _vp, _vp, _vp,
+                                        _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
+                                        _vp]),
     "paged_cache_append_fp8": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _vp]),
     "paged_cache_copy_blocks_fp8": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),

@@ -30,6 +30,7 @@
 #include <mutex>
 #include <type_traits>
 
+#include "decode_host.h"
 #include "decode_part.h"
 
 namespace pkv {
@@ -197,83 +198,18 @@ __global__ void __launch_bounds__(128) decode_reduce_loop_kernel(void* __restric
 // ------------------------------------------------------------------------------------------
 // Host side
 // ------------------------------------------------------------------------------------------
-struct Plan {
-  int32_t part_size;
-  int32_t max_parts;
-  size_t ml_bytes;
-  size_t need_bytes;
-};
-
-size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
-
-Plan make_plan(int32_t B, int32_t Hq, int32_t D, int32_t max_ctx, int32_t partition_size) {
-  Plan pl{};
-  if (partition_size <= 0) {
-    pl.part_size = ((max_ctx + kBlock - 1) / kBlock) * kBlock;
-    if (pl.part_size < kBlock) pl.part_size = kBlock;
-    pl.max_parts = 1;
-    pl.ml_bytes = 0;
-    pl.need_bytes = 0;
-  } else {
-    pl.part_size = partition_size;
-    pl.max_parts = (max_ctx + partition_size - 1) / partition_size;
-    pl.ml_bytes = align256(static_cast<size_t>(B) * Hq * pl.max_parts * 2 * sizeof(float));
-    pl.need_bytes = pl.ml_bytes + static_cast<size_t>(B) * Hq * pl.max_parts * D * sizeof(float);
-  }
-  return pl;
-}
-
-int validate(const char* fn, void* out, int32_t out_dtype, const void* query, const void* k_cache,
-             const void* v_cache, const int32_t* block_tables, const int32_t* context_lens, int32_t B, int32_t Hq,
-             int32_t Hkv, int32_t D, int32_t bs, int32_t max_blocks, int32_t num_blocks, int32_t max_ctx,
-             int32_t partition_size, const void* workspace, size_t workspace_bytes, int32_t dtype,
-             bool check_workspace = true) {
-  if (!valid_dtype(dtype)) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
-  if (out_dtype != PKV_F32 && out_dtype != dtype)
-    return fail(PKV_EINVAL, "%s: out_dtype must be PKV_F32 or the input dtype", fn);
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || bs <= 0 || max_blocks < 0 || num_blocks <= 0 || max_ctx < 0)
-    return fail(PKV_EINVAL, "%s: bad sizes", fn);
-  if (Hq % Hkv != 0) return fail(PKV_EINVAL, "%s: num_q_heads %d not a multiple of num_kv_heads %d", fn, Hq, Hkv);
-  if (bs != kBlock) return fail(PKV_EUNSUPPORTED, "%s: block_size %d (kernels implement 16)", fn, bs);
-  if (D != 64 && D != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim %d (64 or 128)", fn, D);
-  const int G = Hq / Hkv;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PKV_EUNSUPPORTED, "%s: group size %d", fn, G);
-  if (B > 65535 || Hq > 65535) return fail(PKV_EUNSUPPORTED, "%s: batch or head count above 65535", fn);
-  if (partition_size != PKV_SINGLE_PASS_ADAPTIVE && (partition_size < 0 || partition_size % bs != 0))
-    return fail(PKV_EINVAL, "%s: partition_size %d must be 0, -1 or a multiple of block_size", fn, partition_size);
-  if (partition_size > 0 && (max_ctx + static_cast<int64_t>(partition_size) - 1) / partition_size > 65535)
-    return fail(PKV_EUNSUPPORTED, "%s: more than 65535 partitions per sequence", fn);
-  if (static_cast<int64_t>(max_ctx) > static_cast<int64_t>(max_blocks) * bs)
-    return fail(PKV_EINVAL, "%s: max_context_len %d exceeds max_blocks_per_seq * block_size", fn, max_ctx);
-  if (B == 0) return PKV_OK;
-  if (!out || !query || !k_cache || !v_cache || !block_tables || !context_lens)
-    return fail(PKV_EINVAL, "%s: NULL pointer", fn);
-  const Plan pl = make_plan(B, Hq, D, max_ctx, partition_size);
-  if (check_workspace && pl.need_bytes > 0 && (!workspace || workspace_bytes < pl.need_bytes))
-    return fail(PKV_EINVAL, "%s: workspace of %zu bytes needed, %zu given", fn, pl.need_bytes, workspace_bytes);
-  const uintptr_t al = reinterpret_cast<uintptr_t>(query) | reinterpret_cast<uintptr_t>(k_cache) |
-                       reinterpret_cast<uintptr_t>(v_cache) | reinterpret_cast<uintptr_t>(workspace);
-  if (al % 16 != 0) return fail(PKV_EINVAL, "%s: query, caches and workspace must be 16-byte aligned", fn);
-  return PKV_OK;
-}
-
 template <int DT, int DT_OUT, int D>
 int launch_valu(const DecodeArgs& a, int B, hipStream_t s) {
   hipLaunchKernelGGL((decode_valu_kernel<DT, DT_OUT, D>), dim3(a.Hq, B, a.max_parts), dim3(64), 0, s, a);
   return PKV_OK;
 }
 
-// Waves per workgroup: 4 for partitions of up to 512 tokens (<= 4 steps per wave), 8 above and
-// for the single pass.  The choice depends only on the caller's partition_size, never on the
-// batch (a single pass spans the batch's longest context, so its wave count is fixed): a
-// sequence's reduction order, and so its output bits, do not depend on the rest of the batch.
-// The batch-adaptive single pass (partition_size -1) applies the 512-token rule to the batch's
-// longest context instead.
+// Waves per workgroup: decode_waves (decode_host.h).
 template <int DT, int DT_OUT, int D, int G>
-int launch_mfma(const DecodeArgs& a, int B, bool single_pass, hipStream_t s) {
+int launch_mfma(const DecodeArgs& a, int B, int nw, hipStream_t s) {
   const dim3 grid(a.Hkv, B, a.max_parts);
   const bool fused = a.new_k != nullptr;
-  if (!single_pass && a.part_size <= 512) {
+  if (nw == 4) {
     if (fused)
       hipLaunchKernelGGL((decode_mfma_kernel<DT, DT_OUT, D, G, 4, true>), grid, dim3(256), 0, s, a);
     else
@@ -288,37 +224,36 @@ int launch_mfma(const DecodeArgs& a, int B, bool single_pass, hipStream_t s) {
 }
 
 template <int DT, int DT_OUT, int D>
-int dispatch_group(const DecodeArgs& a, int B, bool single_pass, hipStream_t s) {
+int dispatch_group(const DecodeArgs& a, int B, int nw, hipStream_t s) {
   switch (a.Hq / a.Hkv) {
-    case 1: return launch_mfma<DT, DT_OUT, D, 1>(a, B, single_pass, s);
-    case 2: return launch_mfma<DT, DT_OUT, D, 2>(a, B, single_pass, s);
-    case 4: return launch_mfma<DT, DT_OUT, D, 4>(a, B, single_pass, s);
-    default: return launch_mfma<DT, DT_OUT, D, 8>(a, B, single_pass, s);
+    case 1: return launch_mfma<DT, DT_OUT, D, 1>(a, B, nw, s);
+    case 2: return launch_mfma<DT, DT_OUT, D, 2>(a, B, nw, s);
+    case 4: return launch_mfma<DT, DT_OUT, D, 4>(a, B, nw, s);
+    default: return launch_mfma<DT, DT_OUT, D, 8>(a, B, nw, s);
   }
 }
 
 template <int DT, int DT_OUT>
-int dispatch_dim(const DecodeArgs& a, int D, int B, bool single_pass, hipStream_t s) {
+int dispatch_dim(const DecodeArgs& a, int D, int B, int nw, hipStream_t s) {
   if constexpr (DT == PKV_F32) {
     return D == 64 ? launch_valu<DT, DT_OUT, 64>(a, B, s) : launch_valu<DT, DT_OUT, 128>(a, B, s);
   } else {
-    return D == 64 ? dispatch_group<DT, DT_OUT, 64>(a, B, single_pass, s)
-                   : dispatch_group<DT, DT_OUT, 128>(a, B, single_pass, s);
+    return D == 64 ? dispatch_group<DT, DT_OUT, 64>(a, B, nw, s)
+                   : dispatch_group<DT, DT_OUT, 128>(a, B, nw, s);
   }
 }
 
-int launch_partitions(const DecodeArgs& a, int32_t dtype, int32_t out_dtype, int D, int B, bool single_pass,
-                      hipStream_t s) {
+int launch_partitions(const DecodeArgs& a, int32_t dtype, int32_t out_dtype, int D, int B, int nw, hipStream_t s) {
   const bool f32out = out_dtype == PKV_F32;
   switch (dtype) {
     case PKV_BF16:
-      return f32out ? dispatch_dim<PKV_BF16, PKV_F32>(a, D, B, single_pass, s)
-                    : dispatch_dim<PKV_BF16, PKV_BF16>(a, D, B, single_pass, s);
+      return f32out ? dispatch_dim<PKV_BF16, PKV_F32>(a, D, B, nw, s)
+                    : dispatch_dim<PKV_BF16, PKV_BF16>(a, D, B, nw, s);
     case PKV_F16:
-      return f32out ? dispatch_dim<PKV_F16, PKV_F32>(a, D, B, single_pass, s)
-                    : dispatch_dim<PKV_F16, PKV_F16>(a, D, B, single_pass, s);
+      return f32out ? dispatch_dim<PKV_F16, PKV_F32>(a, D, B, nw, s)
+                    : dispatch_dim<PKV_F16, PKV_F16>(a, D, B, nw, s);
     default:
-      return dispatch_dim<PKV_F32, PKV_F32>(a, D, B, single_pass, s);
+      return dispatch_dim<PKV_F32, PKV_F32>(a, D, B, nw, s);
   }
 }
 
@@ -407,30 +342,8 @@ int partitions_impl(const char* fn, void* out, int32_t out_dtype, const void* qu
   a.new_v = new_v;
   a.k_out = k_out;
   a.v_out = v_out;
-  if (host_lens != nullptr && B <= kMaxOrder) {
-    // Work order (largest work first, smallest last): rows sorted by the size of their
-    // sequence's last partition (the whole context for a single pass), largest first, ties
-    // longest first; and each sequence's partitions rotated so that its last one falls in the
-    // grid's last slice.  Full partitions are then all dispatched before the ragged last ones,
-    // which go smallest last.  The schedule only: every partition's arithmetic is the same
-    // wherever it runs.
-    int32_t nparts[kMaxOrder], last[kMaxOrder], idx[kMaxOrder];
-    for (int i = 0; i < B; ++i) {
-      const int L = std::max(0, std::min(host_lens[i], max_ctx));
-      nparts[i] = (L + pl.part_size - 1) / pl.part_size;
-      last[i] = L - std::max(0, nparts[i] - 1) * pl.part_size;
-      idx[i] = i;
-    }
-    std::stable_sort(idx, idx + B, [&](int32_t x, int32_t y) {
-      return last[x] != last[y] ? last[x] > last[y] : host_lens[x] > host_lens[y];
-    });
-    for (int i = 0; i < B; ++i) {
-      const uint32_t rot = static_cast<uint32_t>(nparts[idx[i]] % pl.max_parts);
-      a.order[i] = static_cast<uint32_t>(idx[i]) | (rot << 16);
-    }
-    a.num_order = B;
-  }
-  launch_partitions(a, dtype, out_dtype, D, B, partition_size == 0, as_stream(stream));
+  set_work_order(a, host_lens, B, max_ctx, pl);
+  launch_partitions(a, dtype, out_dtype, D, B, decode_waves(partition_size, pl), as_stream(stream));
   return check_launch(fn);
 }
 

@@ -5,16 +5,18 @@
 // "Continuous batching and PagedAttention: serving many users from one GPU", "Prefill gets in the
 // way": a step carries the running sequences' decode tokens and, within the token budget, a chunk
 // of a new prompt; production servers put both into the same batch.  Here they go into the same
-// kernel launch: workgroups [0, n_dec) each run one (KV head, sequence) of the single-pass decode
-// (the body of the decode kernel, 8 waves), the rest each run one (16-row tile, KV head) of a
-// prefill chunk (the body of the prefill kernel, 8 waves).  Decode work is dispatched first: its
-// workgroups stream the cache from HBM while the prefill workgroups, which are bound by the matrix
-// and vector units, fill the other compute units; the step needs one attention launch instead of
-// two.  Every output is bit for bit the one the separate launches produce (same bodies, same order
-// of arithmetic).  LDS is one buffer, used by whichever body the workgroup runs.
+// kernel launch: workgroups [0, n_dec) each run one (KV head, sequence or group of sequences,
+// partition) of the decode (the body of the decode kernel, or of the grouped decode kernel when
+// sequences share blocks), the rest each run one (16-row tile, KV head) of a prefill chunk (the
+// body of the prefill kernel).  Decode work is dispatched first: its workgroups stream the cache
+// from HBM while the prefill workgroups, which are bound by the matrix and vector units, fill the
+// other compute units.  With split-K partitions the decode's log-sum-exp merge follows as a second
+// launch.  Every output is bit for bit the one the separate launches produce (same bodies, same
+// order of arithmetic).  LDS is one buffer, used by whichever body the workgroup runs.
 #include <algorithm>
 
-#include "decode_part.h"
+#include "decode_group.h"
+#include "decode_host.h"
 #include "prefill_tile.h"
 
 namespace pkv {
@@ -33,9 +35,10 @@ struct ChunkDesc {
 };
 
 struct MixedArgs {
-  DecodeArgs dec;  // the decode batch: single pass (max_parts 1)
+  DecodeArgs dec;
   int32_t B_dec;
-  int32_t n_dec_wg;  // Hkv * B_dec rounded up to a multiple of 8
+  int32_t dec_rows;  // decode rows of the grid: B_dec sequences, or ceil(B_dec / NS) groups
+  int32_t n_dec_wg;  // Hkv * dec_rows * max_parts rounded up to a multiple of 8
   int32_t n_chunks;
   ChunkDesc chunks[kMaxChunks];
   const void* k;
@@ -46,18 +49,28 @@ struct MixedArgs {
   float scale_log2;
 };
 
-template <int DT, int DT_OUT, int D, int G>
+constexpr int smax(int a, int b) { return a > b ? a : b; }
+
+// NS: decode sequences per workgroup (1, or a grouped size); NWD: decode waves (4 or 8, the
+// decode kernel's rule for the partition size).  Every workgroup has 8 waves; a 4-wave decode
+// workgroup's other 4 waves leave at once (a barrier then waits for the remaining waves only).
+template <int DT, int DT_OUT, int D, int G, int NS, int NWD>
 __global__ void __launch_bounds__(512) mixed_kernel(MixedArgs m) {
-  static_assert(PrefillShape<G>::NWAVES == 8, "the mixed launch runs 8-wave prefill tiles (group 4 or 8)");
-  constexpr int kDec = decode_smem_floats<D, G, 8>();
+  static_assert(PrefillShape<G>::NWAVES == 8, "the mixed launch runs 8-wave prefill tiles");
+  constexpr int kDec = NS == 1 ? decode_smem_floats<D, G, NWD>() : group_smem_floats<D, G, NS, NWD>();
   constexpr int kPre = prefill_smem_floats<D, G>();
-  __shared__ float smem[kDec > kPre ? kDec : kPre];
+  __shared__ float smem[smax(kDec, kPre)];
   const int id = blockIdx.x;
   if (id < m.n_dec_wg) {
     const int g = id % m.Hkv;
-    const int y = id / m.Hkv;
-    if (y >= m.B_dec) return;  // padding up to a multiple of 8
-    decode_mfma_part<DT, DT_OUT, D, G, 8, false>(m.dec, g, y, 0, smem);
+    const int y = (id / m.Hkv) % m.dec_rows;
+    const int z = id / (m.Hkv * m.dec_rows);
+    if (z >= m.dec.max_parts) return;  // padding up to a multiple of 8
+    if (NWD < 8 && threadIdx.x >= NWD * 64) return;
+    if constexpr (NS == 1)
+      decode_mfma_part<DT, DT_OUT, D, G, NWD, false>(m.dec, g, y, z, smem);
+    else
+      decode_group_part<DT, DT_OUT, D, G, NS, NWD>(m.dec, m.B_dec, g, y, z, smem);
     return;
   }
   int c = 0;
@@ -81,20 +94,42 @@ __global__ void __launch_bounds__(512) mixed_kernel(MixedArgs m) {
   prefill_tile<DT, DT_OUT, D, G>(pa, local, smem);
 }
 
-template <int DT, int DT_OUT, int D>
-void launch_mixed(const MixedArgs& m, int grid, hipStream_t s) {
-  if (m.Hq / m.Hkv == 4)
-    hipLaunchKernelGGL((mixed_kernel<DT, DT_OUT, D, 4>), dim3(grid), dim3(512), 0, s, m);
+template <int DT, int DT_OUT, int D, int G, int NS>
+void launch_nw(const MixedArgs& m, int nwd, int grid, hipStream_t s) {
+  if (nwd == 4)
+    hipLaunchKernelGGL((mixed_kernel<DT, DT_OUT, D, G, NS, 4>), dim3(grid), dim3(512), 0, s, m);
   else
-    hipLaunchKernelGGL((mixed_kernel<DT, DT_OUT, D, 8>), dim3(grid), dim3(512), 0, s, m);
+    hipLaunchKernelGGL((mixed_kernel<DT, DT_OUT, D, G, NS, 8>), dim3(grid), dim3(512), 0, s, m);
+}
+
+// Decode grouping: 1, or mixed_group_size(G) sequences per workgroup.
+constexpr int mixed_group_size(int G) { return G >= 4 ? 2 : 8 / G; }
+
+template <int DT, int DT_OUT, int D, int G>
+void launch_ns(const MixedArgs& m, int ns, int nwd, int grid, hipStream_t s) {
+  constexpr int kGroup = mixed_group_size(G);
+  if (ns == 1)
+    launch_nw<DT, DT_OUT, D, G, 1>(m, nwd, grid, s);
+  else
+    launch_nw<DT, DT_OUT, D, G, kGroup>(m, nwd, grid, s);
+}
+
+template <int DT, int DT_OUT, int D>
+void launch_g(const MixedArgs& m, int ns, int nwd, int grid, hipStream_t s) {
+  switch (m.Hq / m.Hkv) {
+    case 1: launch_ns<DT, DT_OUT, D, 1>(m, ns, nwd, grid, s); break;
+    case 2: launch_ns<DT, DT_OUT, D, 2>(m, ns, nwd, grid, s); break;
+    case 4: launch_ns<DT, DT_OUT, D, 4>(m, ns, nwd, grid, s); break;
+    default: launch_ns<DT, DT_OUT, D, 8>(m, ns, nwd, grid, s); break;
+  }
 }
 
 template <int DT, int DT_OUT>
-void launch_mixed_d(const MixedArgs& m, int D, int grid, hipStream_t s) {
+void launch_d(const MixedArgs& m, int D, int ns, int nwd, int grid, hipStream_t s) {
   if (D == 64)
-    launch_mixed<DT, DT_OUT, 64>(m, grid, s);
+    launch_g<DT, DT_OUT, 64>(m, ns, nwd, grid, s);
   else
-    launch_mixed<DT, DT_OUT, 128>(m, grid, s);
+    launch_g<DT, DT_OUT, 128>(m, ns, nwd, grid, s);
 }
 
 }  // namespace
@@ -105,12 +140,13 @@ using namespace pkv;
 extern "C" int paged_attention_mixed(void* dec_out, const void* dec_query, const int32_t* dec_block_tables,
                                      const int32_t* dec_context_lens, int32_t B_dec, int32_t dec_max_blocks,
                                      int32_t dec_max_context_len, const int32_t* host_dec_context_lens,
-                                     void* pre_out, const void* pre_query, const int32_t* pre_block_tables,
-                                     int32_t pre_max_blocks, const int32_t* host_ctx_starts,
-                                     const int32_t* host_chunk_lens, int32_t num_chunks, int32_t out_dtype,
-                                     const void* k_cache, const void* v_cache, int32_t num_q_heads,
-                                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
-                                     float scale, int32_t dtype, pkv_stream_t stream) {
+                                     int32_t dec_partition_size, int32_t dec_group_size, void* workspace,
+                                     size_t workspace_bytes, void* pre_out, const void* pre_query,
+                                     const int32_t* pre_block_tables, int32_t pre_max_blocks,
+                                     const int32_t* host_ctx_starts, const int32_t* host_chunk_lens,
+                                     int32_t num_chunks, int32_t out_dtype, const void* k_cache, const void* v_cache,
+                                     int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                                     int32_t num_blocks, float scale, int32_t dtype, pkv_stream_t stream) {
   const char* fn = "paged_attention_mixed";
   if (dtype != PKV_BF16 && dtype != PKV_F16) return fail(PKV_EUNSUPPORTED, "%s: dtype %d (bf16 or fp16)", fn, dtype);
   if (out_dtype != PKV_F32 && out_dtype != dtype)
@@ -120,20 +156,26 @@ extern "C" int paged_attention_mixed(void* dec_out, const void* dec_query, const
     return fail(PKV_EINVAL, "%s: bad sizes", fn);
   if (num_q_heads % num_kv_heads != 0) return fail(PKV_EINVAL, "%s: num_q_heads not a multiple of num_kv_heads", fn);
   const int G = num_q_heads / num_kv_heads;
-  if (G != 4 && G != 8) return fail(PKV_EUNSUPPORTED, "%s: group size %d (the mixed launch takes 4 or 8)", fn, G);
+  if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PKV_EUNSUPPORTED, "%s: group size %d", fn, G);
   if (block_size != kBlock) return fail(PKV_EUNSUPPORTED, "%s: block_size %d (kernels implement 16)", fn, block_size);
   if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim %d", fn, head_dim);
   if (num_chunks > kMaxChunks) return fail(PKV_EUNSUPPORTED, "%s: more than %d prefill chunks", fn, kMaxChunks);
-  if (B_dec > kMaxOrder) return fail(PKV_EUNSUPPORTED, "%s: more than %d decode sequences", fn, kMaxOrder);
-  if (static_cast<int64_t>(dec_max_context_len) > static_cast<int64_t>(dec_max_blocks) * kBlock)
-    return fail(PKV_EINVAL, "%s: dec_max_context_len exceeds dec_max_blocks * block_size", fn);
+  if (dec_group_size != 1 && dec_group_size != mixed_group_size(G))
+    return fail(PKV_EUNSUPPORTED, "%s: dec_group_size %d (1, or %d for %d query heads per KV head)", fn,
+                dec_group_size, mixed_group_size(G), G);
   if (!k_cache || !v_cache) return fail(PKV_EINVAL, "%s: NULL cache", fn);
-  if (B_dec > 0 && (!dec_out || !dec_query || !dec_block_tables || !dec_context_lens))
-    return fail(PKV_EINVAL, "%s: NULL decode pointer", fn);
   if (num_chunks > 0 && (!pre_out || !pre_query || !pre_block_tables || !host_ctx_starts || !host_chunk_lens))
     return fail(PKV_EINVAL, "%s: NULL prefill pointer", fn);
-  if ((reinterpret_cast<uintptr_t>(dec_query) | reinterpret_cast<uintptr_t>(pre_query) |
-       reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) % 16 != 0)
+  // The decode part: paged_attention_decode's argument rules (partition size, workspace, sizes).
+  const bool has_dec = B_dec > 0 && dec_max_context_len > 0;
+  if (B_dec > 0) {
+    const int st = validate(fn, dec_out, out_dtype, dec_query, k_cache, v_cache, dec_block_tables, dec_context_lens,
+                            B_dec, num_q_heads, num_kv_heads, head_dim, block_size, dec_max_blocks, num_blocks,
+                            dec_max_context_len, dec_partition_size, workspace, workspace_bytes, dtype);
+    if (st != PKV_OK) return st;
+  }
+  if ((reinterpret_cast<uintptr_t>(pre_query) | reinterpret_cast<uintptr_t>(k_cache) |
+       reinterpret_cast<uintptr_t>(v_cache)) % 16 != 0)
     return fail(PKV_EINVAL, "%s: queries and caches must be 16-byte aligned", fn);
   MixedArgs m{};
   m.k = k_cache;
@@ -142,8 +184,9 @@ extern "C" int paged_attention_mixed(void* dec_out, const void* dec_query, const
   m.Hkv = num_kv_heads;
   m.num_blocks = num_blocks;
   m.scale_log2 = scale * kLog2e;
-  // decode part: the single pass of paged_attention_decode (partition = the longest context)
-  const bool has_dec = B_dec > 0 && dec_max_context_len > 0;
+  const Plan pl = make_plan(has_dec ? B_dec : 1, num_q_heads, head_dim, has_dec ? dec_max_context_len : 1,
+                            dec_partition_size);
+  const int nwd = decode_waves(dec_partition_size, pl);
   m.B_dec = has_dec ? B_dec : 0;
   DecodeArgs& a = m.dec;
   a.out = dec_out;
@@ -152,20 +195,18 @@ extern "C" int paged_attention_mixed(void* dec_out, const void* dec_query, const
   a.v = v_cache;
   a.tables = dec_block_tables;
   a.lens = dec_context_lens;
+  a.part_ml = pl.need_bytes ? static_cast<float*>(workspace) : nullptr;
+  a.part_o = pl.need_bytes ? reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + pl.ml_bytes) : nullptr;
   a.Hq = num_q_heads;
   a.Hkv = num_kv_heads;
   a.max_blocks = dec_max_blocks;
   a.num_blocks = num_blocks;
-  a.max_parts = 1;
-  a.part_size = std::max(kBlock, ((dec_max_context_len + kBlock - 1) / kBlock) * kBlock);
+  a.max_parts = pl.max_parts;
+  a.part_size = pl.part_size;
   a.scale_log2 = scale * kLog2e;
-  if (has_dec && host_dec_context_lens != nullptr) {
-    for (int i = 0; i < B_dec; ++i) a.order[i] = i;
-    std::stable_sort(a.order, a.order + B_dec,
-                     [&](uint32_t x, uint32_t y) { return host_dec_context_lens[x] > host_dec_context_lens[y]; });
-    a.num_order = B_dec;
-  }
-  int64_t wg = has_dec ? (static_cast<int64_t>(num_kv_heads) * B_dec + 7) / 8 * 8 : 0;
+  if (has_dec && dec_group_size == 1) set_work_order(a, host_dec_context_lens, B_dec, dec_max_context_len, pl);
+  m.dec_rows = has_dec ? (dec_group_size == 1 ? B_dec : (B_dec + dec_group_size - 1) / dec_group_size) : 1;
+  int64_t wg = has_dec ? (static_cast<int64_t>(num_kv_heads) * m.dec_rows * pl.max_parts + 7) / 8 * 8 : 0;
   m.n_dec_wg = static_cast<int32_t>(wg);
   // prefill chunks, rows packed one after another in pre_query / pre_out
   const int64_t row_elems = static_cast<int64_t>(num_q_heads) * head_dim;
@@ -196,16 +237,20 @@ extern "C" int paged_attention_mixed(void* dec_out, const void* dec_query, const
   if (wg == 0) return PKV_OK;
   hipStream_t s = as_stream(stream);
   const bool f32out = out_dtype == PKV_F32;
+  const int grid = static_cast<int>(wg);
   if (dtype == PKV_BF16) {
     if (f32out)
-      launch_mixed_d<PKV_BF16, PKV_F32>(m, head_dim, static_cast<int>(wg), s);
+      launch_d<PKV_BF16, PKV_F32>(m, head_dim, dec_group_size, nwd, grid, s);
     else
-      launch_mixed_d<PKV_BF16, PKV_BF16>(m, head_dim, static_cast<int>(wg), s);
+      launch_d<PKV_BF16, PKV_BF16>(m, head_dim, dec_group_size, nwd, grid, s);
   } else {
     if (f32out)
-      launch_mixed_d<PKV_F16, PKV_F32>(m, head_dim, static_cast<int>(wg), s);
+      launch_d<PKV_F16, PKV_F32>(m, head_dim, dec_group_size, nwd, grid, s);
     else
-      launch_mixed_d<PKV_F16, PKV_F16>(m, head_dim, static_cast<int>(wg), s);
+      launch_d<PKV_F16, PKV_F16>(m, head_dim, dec_group_size, nwd, grid, s);
   }
-  return check_launch(fn);
+  const int st = check_launch(fn);
+  if (st != PKV_OK || !has_dec || pl.max_parts <= 1) return st;
+  return paged_attention_decode_reduce(dec_out, out_dtype, dec_context_lens, B_dec, num_q_heads, head_dim,
+                                       dec_max_context_len, dec_partition_size, workspace, workspace_bytes, stream);
 }

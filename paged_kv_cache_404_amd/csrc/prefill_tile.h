@@ -30,7 +30,7 @@ struct PrefillArgs {
 
 // One workgroup = 16 chunk rows x the G query heads of one KV head.  A wave owns HPW = min(G, 2)
 // heads of the group (HSETS = G / HPW head sets) over one key split (KSPLIT splits of the row
-// tile's keys; HSETS x KSPLIT <= 8 waves, two per SIMD): every K/V fragment it loads feeds the
+// tile's keys; HSETS x KSPLIT = 8 waves, two per SIMD): every K/V fragment it loads feeds the
 // Q.K and P.V products of both its heads, halving the vector-memory bytes per matrix
 // instruction (more heads per wave overflow the 256 architectural registers).  Each wave walks its consecutive 32-key steps with one step of
 // K/V in flight (next K once this step's Q.K products have consumed the K registers, next V
@@ -40,7 +40,7 @@ template <int G>
 struct PrefillShape {
   static constexpr int HPW = G < 2 ? G : 2;
   static constexpr int HSETS = G / HPW;
-  static constexpr int KSPLIT = HSETS >= 4 ? 2 : 4;
+  static constexpr int KSPLIT = 8 / HSETS;
   static constexpr int NWAVES = HSETS * KSPLIT;
 };
 

@@ -164,6 +164,15 @@ def paged_attention_decode(out, query, k_cache, v_cache, block_tables, context_l
     check(lib.paged_attention_decode(*args, _stream(stream)))
 
 
+def paged_attention_decode_grouped(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                                   group_size, partition_size=0, workspace=None, stream=None) -> None:
+    """Decode in which batch rows group_size*k .. group_size*k + group_size - 1 share a workgroup and
+    read the blocks common to their tables once; output bit for bit paged_attention_decode's."""
+    args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
+                        partition_size, workspace)
+    check(lib.paged_attention_decode_grouped(*args[:20], int(group_size), _stream(stream)))
+
+
 def paged_attention_decode_noalloc(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                                    partition_size=0, stream=None, host_context_lens=None) -> None:
     """paged_attention_decode with the split-K partials in the library's static per-GPU scratch
@@ -281,9 +290,13 @@ class PreparedDecode:
 
     def __init__(self, out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
                  partition_size=0, workspace=None, stream=None, new_key=None, new_value=None,
-                 host_context_lens=None, write_cache=True):
+                 host_context_lens=None, write_cache=True, group_size=1):
         """With new_key/new_value: the fused append (write_cache) or the newest-token variant that
-        leaves the cache to the caller (write_cache=False)."""
+        leaves the cache to the caller (write_cache=False).  group_size > 1: the grouped decode
+        (paged_attention_decode_grouped; no fused append)."""
+        if group_size > 1 and new_key is not None:
+            raise ValueError("the grouped decode has no fused append")
+        self.group_size = int(group_size)
         hl, hp = _host_lens_ptr(host_context_lens)
         self._keep = (out, query, k_cache, v_cache, block_tables, context_lens, workspace, new_key, new_value, hl)
         self.args = _decode_args(out, query, k_cache, v_cache, block_tables, context_lens, max_context_len, scale,
@@ -299,6 +312,8 @@ class PreparedDecode:
         if self.fused_args is not None:
             fn = lib.paged_attention_decode_append if self.write_cache else lib.paged_attention_decode_newest
             check(fn(*self.fused_args, self.stream))
+        elif self.group_size > 1:
+            check(lib.paged_attention_decode_grouped(*self.args[:20], self.group_size, self.stream))
         else:
             check(lib.paged_attention_decode(*self.args, self.stream))
 
@@ -487,7 +502,8 @@ class PreparedAppendFp8:
 
 
 def _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, pre_out, pre_query, pre_tables,
-                ctx_starts, chunk_lens, k_cache, v_cache, scale, host_dec_lens):
+                ctx_starts, chunk_lens, k_cache, v_cache, scale, host_dec_lens, dec_partition_size=0, dec_group_size=1,
+                workspace=None):
     """Every shape and dtype is checked before the tensors' device (so a mismatch is reported as
     such), and all of it before the launch."""
     N, Hkv, D = cache_dims(k_cache, v_cache)
@@ -536,9 +552,14 @@ def _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, p
          *((pre_out, pre_query, pre_tables) if S else ()))
     hl, hp = _host_lens_ptr(host_dec_lens)
     keep = (starts, lens, hl)
+    if workspace is not None:
+        _dev(workspace)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
+                                                            workspace.numel() * workspace.element_size())
     args = (dec_out.data_ptr() if B else None, dec_query.data_ptr() if B else None,
             dec_tables.data_ptr() if B else None, dec_lens.data_ptr() if B else None, B,
             dec_tables.shape[1] if B else 0, int(dec_max_context_len) if B else 0, hp,
+            int(dec_partition_size), int(dec_group_size), ws_ptr, ws_bytes,
             pre_out.data_ptr() if S else None, pre_query.data_ptr() if S else None,
             pre_tables.data_ptr() if S else None, pre_tables.shape[1] if S else 0,
             starts.ctypes.data if S else None, lens.ctypes.data if S else None, S, dtype_code(out_dtype),
@@ -548,11 +569,13 @@ def _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, p
 
 def paged_attention_mixed(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, pre_out, pre_query,
                           pre_tables, ctx_starts, chunk_lens, k_cache, v_cache, scale, stream=None,
-                          host_dec_lens=None) -> None:
-    """One launch: single-pass decode of a batch + causal attention of prefill chunks (rows packed
-    in pre_query/pre_out; chunk i at positions ctx_starts[i] .., table row i of pre_tables)."""
+                          host_dec_lens=None, dec_partition_size=0, dec_group_size=1, workspace=None) -> None:
+    """One launch (+ the split-K merge when dec_partition_size > 0): decode of a batch (grouped
+    dec_group_size sequences to a workgroup when > 1) + causal attention of prefill chunks (rows
+    packed in pre_query/pre_out; chunk i at positions ctx_starts[i] .., table row i of pre_tables)."""
     r = _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, pre_out, pre_query, pre_tables,
-                    ctx_starts, chunk_lens, k_cache, v_cache, scale, host_dec_lens)
+                    ctx_starts, chunk_lens, k_cache, v_cache, scale, host_dec_lens, dec_partition_size,
+                    dec_group_size, workspace)
     if r is None:
         return
     args, keep = r
@@ -562,9 +585,11 @@ def paged_attention_mixed(dec_out, dec_query, dec_tables, dec_lens, dec_max_cont
 class PreparedMixed:
     """paged_attention_mixed with its arguments marshalled once."""
 
-    def __init__(self, *a, stream=None, host_dec_lens=None):
-        self._tensors = a
-        r = _mixed_args(*a, host_dec_lens=host_dec_lens)
+    def __init__(self, *a, stream=None, host_dec_lens=None, dec_partition_size=0, dec_group_size=1,
+                 workspace=None):
+        self._tensors = (a, workspace)
+        r = _mixed_args(*a, host_dec_lens=host_dec_lens, dec_partition_size=dec_partition_size,
+                        dec_group_size=dec_group_size, workspace=workspace)
         self.args, self._keep = r
         self.stream = _stream(stream)
 
