@@ -345,9 +345,11 @@ int paged_attention_decode_newest_partitions(void* out, int32_t out_dtype, const
  * chunk's own K/V must already be appended (paged_cache_append) before this call.
  *
  *   out         device [C][num_q_heads][head_dim] of out_dtype (PKV_F32 or `dtype`).
- *   query       device [C][num_q_heads][head_dim] of `dtype` (PKV_F16 or PKV_BF16).
+ *   query       device [C][num_q_heads][head_dim] of `dtype` (bf16 and fp16 run on the matrix cores;
+ *               PKV_F32 on the vector ALU, at most 65535 rows).
  *   block_table device int32 [>= ceil((ctx_start + C) / block_size)] of the one sequence.
- * Accumulation is fp32; the products run on the matrix cores.
+ *   scale       positive and finite (PKV_EINVAL otherwise).
+ * Accumulation is fp32.
  */
 int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const void* query, const void* k_cache,
                                   const void* v_cache, const int32_t* block_table, int32_t ctx_start,

@@ -14,6 +14,7 @@
 // launch.  Every output is bit for bit the one the separate launches produce (same bodies, same
 // order of arithmetic).  LDS is one buffer, used by whichever body the workgroup runs.
 #include <algorithm>
+#include <cmath>
 
 #include "decode_group.h"
 #include "decode_host.h"
@@ -155,6 +156,8 @@ extern "C" int paged_attention_mixed(void* dec_out, const void* dec_query, const
       dec_max_blocks < 0 || pre_max_blocks < 0 || dec_max_context_len < 0)
     return fail(PKV_EINVAL, "%s: bad sizes", fn);
   if (num_q_heads % num_kv_heads != 0) return fail(PKV_EINVAL, "%s: num_q_heads not a multiple of num_kv_heads", fn);
+  // The prefill tile compares raw scores against thresholds divided by the scale: positive only.
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale must be positive and finite", fn);
   const int G = num_q_heads / num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return fail(PKV_EUNSUPPORTED, "%s: group size %d", fn, G);
   if (block_size != kBlock) return fail(PKV_EUNSUPPORTED, "%s: block_size %d (kernels implement 16)", fn, block_size);

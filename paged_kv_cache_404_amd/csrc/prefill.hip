@@ -9,7 +9,8 @@
 // softmax, weighted sum of values; [Serving] "Production Serving: Continuous Batching and
 // PagedAttention", The Build, Step 6).
 //
-// MI355X mapping: a workgroup owns 16 consecutive chunk rows of the G query heads of one KV
+// MI355X mapping (bf16 / fp16; fp32 caches take a plain vector-ALU kernel): a workgroup owns 16
+// consecutive chunk rows of the G query heads of one KV
 // head; its waves split the key range and the heads, and each wave serves two heads from every
 // K/V fragment it loads.  Per
 // 32-key step, S^T = K.Q^T (2 x D/32 MFMA 16x16x32) and O += P.V (D/16 MFMA, twice: P split
@@ -27,6 +28,81 @@ template <int DT, int DT_OUT, int D, int G>
 __global__ void __launch_bounds__(PrefillShape<G>::NWAVES * 64) prefill_mfma_kernel(PrefillArgs a) {
   __shared__ float smem[prefill_smem_floats<D, G>()];
   prefill_tile<DT, DT_OUT, D, G>(a, blockIdx.x, smem);
+}
+
+__device__ __forceinline__ float wave_max64(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ __forceinline__ float wave_sum64(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// fp32 caches: one wave per (query head, chunk row) on the vector ALU; grid = (Hq, C).  Lane i
+// scores key c0 + i of each 64-key chunk of the row's visible keys 0 .. ctx_start + row and keeps
+// an online softmax; each lane owns dimensions lane and lane + 64 of the output.
+template <int DT_OUT, int D>
+__global__ void __launch_bounds__(64) prefill_valu_kernel(PrefillArgs a) {
+  constexpr int E = 4;  // fp32 elements per 16-byte chunk of the K tile
+  constexpr int DPL = (D + 63) / 64;
+  const int hq = blockIdx.x;
+  const int row = blockIdx.y;
+  const int g = hq / (a.Hq / a.Hkv);
+  const int L = a.ctx_start + row + 1;  // keys this row sees
+  const int lane = threadIdx.x;
+  const float* __restrict__ kc = static_cast<const float*>(a.k);
+  const float* __restrict__ vc = static_cast<const float*>(a.v);
+
+  __shared__ float qs[D];
+  for (int d = lane; d < D; d += 64)
+    qs[d] = static_cast<const float*>(a.q)[(static_cast<int64_t>(row) * a.Hq + hq) * D + d] * a.scale_log2;
+  __syncthreads();
+
+  float o[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) o[i] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+  for (int c0 = 0; c0 < L; c0 += 64) {
+    const int t = c0 + lane;
+    const bool valid = t < L;
+    int64_t tile = 0;
+    int off = 0;
+    float sc = -INFINITY;
+    if (valid) {
+      const int blk = min(max(a.table[t / kBlock], 0), a.num_blocks - 1);
+      tile = (static_cast<int64_t>(blk) * a.Hkv + g) * kBlock * D;
+      off = t % kBlock;
+      float acc = 0.f;
+      for (int d = 0; d < D; ++d) acc += qs[d] * kc[tile + static_cast<int64_t>(k_chunk_pos(off, d / E)) * E + d % E];
+      sc = acc;
+    }
+    const float m_new = fmaxf(m_run, wave_max64(sc));
+    const float alpha = fast_exp2(m_run - m_new);
+    const float pt = valid ? fast_exp2(sc - m_new) : 0.f;
+    l_run = l_run * alpha + wave_sum64(pt);
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) o[i] *= alpha;
+    const int n = min(64, L - c0);
+    for (int i = 0; i < n; ++i) {
+      const float pi = __shfl(pt, i);
+      const int64_t ti = __shfl(tile, i);
+      const int oi = __shfl(off, i);
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const int d = lane + 64 * k;
+        if (d < D) o[k] += pi * vc[ti + static_cast<int64_t>((oi >> 3) * D + d) * 8 + (oi & 7)];
+      }
+    }
+    m_run = m_new;
+  }
+#pragma unroll
+  for (int k = 0; k < DPL; ++k) {
+    const int d = lane + 64 * k;
+    if (d < D) store_from_float<DT_OUT>(a.out, (static_cast<int64_t>(row) * a.Hq + hq) * D + d, o[k] / l_run);
+  }
 }
 
 template <int DT, int DT_OUT, int D, int G>
@@ -65,12 +141,13 @@ extern "C" int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const
                                              pkv_stream_t stream) {
   const char* fn = "paged_attention_prefill_chunk";
   if (!valid_dtype(dtype)) return fail(PKV_EINVAL, "%s: unknown dtype %d", fn, dtype);
-  if (dtype == PKV_F32) return fail(PKV_EUNSUPPORTED, "%s: fp32 caches are not implemented (bf16 or fp16)", fn);
   if (out_dtype != PKV_F32 && out_dtype != dtype)
     return fail(PKV_EINVAL, "%s: out_dtype must be PKV_F32 or the input dtype", fn);
   if (ctx_start < 0 || C < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || block_size <= 0)
     return fail(PKV_EINVAL, "%s: bad sizes", fn);
   if (num_q_heads % num_kv_heads != 0) return fail(PKV_EINVAL, "%s: num_q_heads not a multiple of num_kv_heads", fn);
+  // The prefill tile compares raw scores against thresholds divided by the scale: positive only.
+  if (!(scale > 0.f) || !std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale must be positive and finite", fn);
   if (block_size != kBlock) return fail(PKV_EUNSUPPORTED, "%s: block_size %d (kernels implement 16)", fn, block_size);
   if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim %d", fn, head_dim);
   const int G = num_q_heads / num_kv_heads;
@@ -84,6 +161,7 @@ extern "C" int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const
     return fail(PKV_EINVAL, "%s: query and caches must be 16-byte aligned", fn);
   const int64_t tiles = (static_cast<int64_t>(C) + 15) / 16;
   if (tiles * num_kv_heads > INT32_MAX) return fail(PKV_EINVAL, "%s: chunk too large", fn);
+  if (dtype == PKV_F32 && C > 65535) return fail(PKV_EUNSUPPORTED, "%s: fp32 chunks of more than 65535 rows", fn);
   PrefillArgs a{};
   a.out = out;
   a.q = query;
@@ -99,7 +177,13 @@ extern "C" int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const
   a.scale_log2 = scale * kLog2e;
   hipStream_t s = as_stream(stream);
   const bool f32out = out_dtype == PKV_F32;
-  if (dtype == PKV_BF16) {
+  if (dtype == PKV_F32) {
+    const dim3 grid(num_q_heads, C);
+    if (head_dim == 64)
+      hipLaunchKernelGGL((prefill_valu_kernel<PKV_F32, 64>), grid, dim3(64), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill_valu_kernel<PKV_F32, 128>), grid, dim3(64), 0, s, a);
+  } else if (dtype == PKV_BF16) {
     if (f32out)
       launch_d<PKV_BF16, PKV_F32>(a, head_dim, s);
     else

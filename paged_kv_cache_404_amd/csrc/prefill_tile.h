@@ -120,6 +120,9 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
     m_run[h] = kNoMax;
     l_run[h] = 0.f;
   }
+  float thr[HPW];  // raw-score rescale threshold per head: (m_run + 2^8) / (scale * log2 e)
+#pragma unroll
+  for (int h = 0; h < HPW; ++h) thr[h] = (kNoMax + kLazyRescaleLog2) / a.scale_log2;
 
   const int last_row = min(i0 + 15, a.C - 1);
   const int nkeys = a.ctx_start + last_row + 1;  // keys any row of the tile can see
@@ -225,14 +228,17 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
       // Lazy rescale: a row's reference maximum moves only when one of its scores exceeds it by
       // more than 2^8.  Each lane tests its own 8 scores per head; the row maximum over the
       // row's four lanes is formed only when some lane of the wave passes that test.
+      // The raw-score threshold thr = (m_run + 2^8) / c saves the scaling of the maxima, and the
+      // NaN-propagating maximum needs no canonicalising of the matrix results (v_maximum3).
+      // Masked scores are -inf, never NaN, so both maxima agree here.
       float lmax[HPW];
       bool big = false;
 #pragma unroll
       for (int h = 0; h < HPW; ++h) {
         lmax[h] = sc[h][0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) lmax[h] = fmaxf(lmax[h], sc[h][i]);
-        big = big || (lmax[h] * c > m_run[h] + kLazyRescaleLog2);
+        for (int i = 1; i < 8; ++i) lmax[h] = __builtin_elementwise_maximum(lmax[h], sc[h][i]);
+        big = big || (lmax[h] > thr[h]);
       }
       if (__any(big)) {
 #pragma unroll
@@ -243,6 +249,7 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
           const float alpha = need ? fast_exp2(m_run[h] - m_new) : 1.0f;
           l_run[h] *= alpha;
           m_run[h] = m_new;
+          thr[h] = (m_new + kLazyRescaleLog2) / c;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             const float f = __shfl(alpha, 4 * q4 + j);

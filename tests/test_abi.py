@@ -103,8 +103,11 @@ def test_append_and_prefill_host_validation():
     assert L.paged_cache_append(p, p, p, p, 0, 0, NULL, 4, 8, 128, 16, 10, pkv.PKV_BF16, NULL) == pkv.PKV_EINVAL
     assert L.paged_cache_append(p, p, p, p, 8, 0, p, 4, 8, 128, 16, 10, pkv.PKV_BF16, NULL) == pkv.PKV_EINVAL
     assert L.paged_cache_append(NULL, NULL, NULL, NULL, 0, 0, NULL, 0, 8, 128, 16, 10, pkv.PKV_BF16, NULL) == pkv.PKV_OK
-    assert L.paged_attention_prefill_chunk(p, pkv.PKV_F32, p, p, p, p, 0, 16, 32, 8, 128, 16, 64, 0.1, pkv.PKV_F32,
+    assert L.paged_attention_prefill_chunk(p, pkv.PKV_F32, p, p, p, p, 0, 16, 32, 8, 96, 16, 64, 0.1, pkv.PKV_F32,
                                            NULL) == pkv.PKV_EUNSUPPORTED
+    for bad_scale in (0.0, -0.1, float("inf"), float("nan")):
+        assert L.paged_attention_prefill_chunk(p, pkv.PKV_F32, p, p, p, p, 0, 16, 32, 8, 128, 16, 64, bad_scale,
+                                               pkv.PKV_BF16, NULL) == pkv.PKV_EINVAL
     assert L.paged_attention_prefill_chunk(p, pkv.PKV_F32, p, p, p, p, 1000, 100, 32, 8, 128, 16, 64, 0.1,
                                            pkv.PKV_BF16, NULL) == pkv.PKV_EINVAL
     assert L.paged_cache_copy_blocks(p, p, NULL, 3, 8, 128, 16, 64, pkv.PKV_BF16, NULL) == pkv.PKV_EINVAL

@@ -1,5 +1,6 @@
-"""GPU parity of the chunked-prefill causal kernel and of the mixed prefix-sharing step against
-the oracle (max-abs 2e-3 in fp32; cache bytes, tables and slots bit-exact)."""
+"""GPU parity of the chunked-prefill causal kernel (bf16 / fp16 on the matrix cores, fp32 on the
+vector ALU) and of the mixed prefix-sharing step against the oracle (max-abs 2e-3 in fp32; cache
+bytes, tables and slots bit-exact)."""
 import numpy as np
 import pytest
 import torch
@@ -41,6 +42,10 @@ def _prefill_case(seed, ctx_start, C, Hq, Hkv, D, dtype, out_dtype=torch.float32
     (0, 64, 64, 8, 128, "bf16"),
     (250, 130, 16, 8, 128, "f16"),
     (17, 50, 8, 4, 64, "f16"),
+    (0, 1, 8, 8, 64, "f32"),
+    (0, 40, 16, 8, 128, "f32"),
+    (37, 70, 32, 8, 64, "f32"),
+    (100, 33, 8, 2, 128, "f32"),
 ])
 def test_prefill_shapes_and_edges(ctx_start, C, Hq, Hkv, D, dtype):
     m, s, q, out, tables, scale = _prefill_case(60 + C, ctx_start, C, Hq, Hkv, D, dtype)
