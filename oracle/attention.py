@@ -89,10 +89,11 @@ def paged_decode(q_bits, cache, tables, lens, scale: float, return_weights: bool
     return (out, weights) if return_weights else out
 
 
-def prefill_chunk(q_bits, cache, table, ctx_start: int, scale: float):
-    """Causal attention of a prompt chunk against the paged cache: q_bits [C][Hq][D], row i
-    sits at position ctx_start + i and sees keys 0 .. ctx_start + i.  Returns fp64 [C][Hq][D]."""
-    q = bits_to_f64(q_bits, cache.dtype)
+def prefill_chunk(q_bits, cache, table, ctx_start: int, scale: float, q_dtype=None):
+    """Causal attention of a prompt chunk against the paged cache: q_bits [C][Hq][D] (of q_dtype,
+    default the cache's type; an fp8 cache needs bf16 or f16 queries), row i sits at position
+    ctx_start + i and sees keys 0 .. ctx_start + i.  Returns fp64 [C][Hq][D]."""
+    q = bits_to_f64(q_bits, q_dtype or cache.dtype)
     C, Hq, D = q.shape
     G = Hq // cache.H
     K, V = gather(cache, table, ctx_start + C)

@@ -147,3 +147,34 @@ def test_fp8_v_tile_order_fixture():
         phys = c.v_physical()
         assert phys[0, 0, off] == 0xFE, case
         assert np.count_nonzero(phys) == 1, case
+
+
+def test_fp8_prefill_is_causal_attention_on_dequantised_values():
+    # Chunked prefill over the quantised cache: row i at position ctx + i attends causally to the
+    # values the codes stand for (code * scale), computed here from the codec alone and checked
+    # with torch's fp64 causal attention, whatever blocks the table names.
+    import torch
+    rng = np.random.default_rng(31)
+    ctx, C, Hq, Hkv, D = 19, 14, 4, 2, 64
+    total = ctx + C
+    c = Fp8CacheModel(5, Hkv, D)
+    table = [4, 0, 2]
+    k = rng.standard_normal((total, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((total, Hkv, D)).astype(np.float32)
+    c.append(k, v, [table[t // 16] * 16 + t % 16 for t in range(total)])
+    q_bits = (rng.standard_normal((C, Hq, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    out = oatt.prefill_chunk(q_bits, c, table, ctx, 0.125, q_dtype="bf16")
+    kc, ks = fp8.quantize_rows(k)
+    vc, vs = fp8.quantize_rows(v)
+    K = fp8.e4m3_decode(kc) * ks[..., None].astype(np.float64)  # [total][Hkv][D]
+    V = fp8.e4m3_decode(vc) * vs[..., None].astype(np.float64)
+    q = oatt.bits_to_f64(q_bits, "bf16")
+    mask = np.arange(total)[None, :] <= (ctx + np.arange(C))[:, None]
+    Qt = torch.from_numpy(q.transpose(1, 0, 2))[None]
+    Kt = torch.from_numpy(np.repeat(K.transpose(1, 0, 2), Hq // Hkv, axis=0))[None]
+    Vt = torch.from_numpy(np.repeat(V.transpose(1, 0, 2), Hq // Hkv, axis=0))[None]
+    ref = torch.nn.functional.scaled_dot_product_attention(Qt, Kt, Vt, attn_mask=torch.from_numpy(mask), scale=0.125)
+    np.testing.assert_allclose(out, ref[0].numpy().transpose(1, 0, 2), rtol=0, atol=1e-12)
+    # a chunk starting an empty context: its first row sees one token and returns that value row
+    first = oatt.prefill_chunk(q_bits[:3], c, table, 0, 0.125, q_dtype="f16")
+    assert np.array_equal(first[0, 0], V[0, 0]) and np.array_equal(first[0, 3], V[0, 1])
