@@ -55,7 +55,7 @@ def parse():
                     help="do not pass the host copy of the context lengths (longest-first work order)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the chunked-prefill and long-context measurements reported beside the main line")
-    ap.add_argument("--extras", default="prefill,long,prefix,fp8,mixed,trace",
+    ap.add_argument("--extras", default="prefill,prefill_fp8,long,prefix,fp8,mixed,trace",
                     help="comma-separated side lines to run beside the main line (default: all of them)")
     mode = ap.add_mutually_exclusive_group()
     mode.add_argument("--overlap", action="store_true",
@@ -149,10 +149,11 @@ def _events_avg_us(torch, stream, fn, n):
     return e0.elapsed_time(e1) * 1e3 / n
 
 
-def measure_prefill(args, dev):
+def measure_prefill(args, dev, fp8=False):
     """paged_attention_prefill_chunk on the mixed step's chunk: 512 rows at positions 4096..4607
-    of one sequence (32 q / 8 kv heads of 128, bf16), causal against the paged cache.  Work:
-    4 * head_dim flops per visible (row, key) pair and query head."""
+    of one sequence (32 q / 8 kv heads of 128, bf16), causal against the paged cache; with fp8,
+    paged_attention_prefill_chunk_fp8 over the same tokens quantised into an fp8 cache (bf16
+    queries).  Work: 4 * head_dim flops per visible (row, key) pair and query head."""
     import numpy as np
     import torch
 
@@ -167,12 +168,22 @@ def measure_prefill(args, dev):
     table, _ = pool.block_tables([s], wl.blocks_for(ctx + C))
     g = torch.Generator(device=dev)
     g.manual_seed(w.seed)
-    k = torch.randn((w.num_blocks, Hkv, 16 * D), generator=g, device=dev).to(torch.bfloat16)
-    v = torch.randn((w.num_blocks, Hkv, 16 * D), generator=g, device=dev).to(torch.bfloat16)
     q = torch.randn((C, Hq, D), generator=g, device=dev).to(torch.bfloat16)
     out = torch.empty((C, Hq, D), dtype=torch.float32, device=dev)
     tb = torch.from_numpy(table[0]).to(dev)
-    fn = lambda i: ops.paged_attention_prefill_chunk(out, q, k, v, tb, ctx, w.scale)  # noqa: E731
+    if fp8:
+        k, v, ks, vs = ops.fp8_cache(w.num_blocks, Hkv, D, device=dev)
+        T = ctx + C
+        slots = torch.from_numpy((table[0][np.arange(T) // 16].astype(np.int64) * 16 + np.arange(T) % 16)
+                                 .astype(np.int32)).to(dev)
+        kr = torch.randn((T, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+        vr = torch.randn((T, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+        ops.paged_cache_append_fp8(k, v, ks, vs, kr, vr, slots)
+        fn = lambda i: ops.paged_attention_prefill_chunk_fp8(out, q, k, v, ks, vs, tb, ctx, w.scale)  # noqa: E731
+    else:
+        k = torch.randn((w.num_blocks, Hkv, 16 * D), generator=g, device=dev).to(torch.bfloat16)
+        v = torch.randn((w.num_blocks, Hkv, 16 * D), generator=g, device=dev).to(torch.bfloat16)
+        fn = lambda i: ops.paged_attention_prefill_chunk(out, q, k, v, tb, ctx, w.scale)  # noqa: E731
     for i in range(5):
         fn(i)
     us = _events_avg_us(torch, torch.cuda.current_stream(), fn, max(20, args.steps // 4))
@@ -180,26 +191,26 @@ def measure_prefill(args, dev):
     flops = pairs * Hq * 4 * D
     tflops = flops / (us * 1e-6) / 1e12
     res = {
-        "workload": f"prefill_chunk_{C}_after_{ctx}_gqa{Hq}x{Hkv}_d{D}_bf16",
+        "workload": f"prefill_chunk_{C}_after_{ctx}_gqa{Hq}x{Hkv}_d{D}_" + ("fp8_cache_bf16_query" if fp8 else "bf16"),
         "us_per_call": round(us, 3),
         "flops_per_call": flops,
-        "roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": round(tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None},
+        "roofline": {"bound": "mfma", "kernel": "prefill_fp8_kernel" if fp8 else "prefill_mfma_kernel",
+                     "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline_prefill(ctx, Hq, Hkv, D, w.scale, args.cpu_seconds / 2)
+        res["cpu_baseline"] = cpu_baseline_prefill(ctx, Hq, Hkv, D, w.scale, args.cpu_seconds / 2, fp8=fp8)
     return res
 
 
-def cpu_baseline_prefill(ctx, Hq, Hkv, D, scale, seconds):
+def cpu_baseline_prefill(ctx, Hq, Hkv, D, scale, seconds, fp8=False):
     """The oracle's prefill (numpy fp64) on the first R rows of the same chunk shape, R grown
-    until the sample takes about `seconds`."""
+    until the sample takes about `seconds` (fp8: over the oracle's quantised cache)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import workloads as wl
-    from oracle import CacheModel, PoolModel
+    from oracle import CacheModel, Fp8CacheModel, PoolModel
     from oracle import attention as oatt
 
     rng = np.random.default_rng(1005)
@@ -209,13 +220,18 @@ def cpu_baseline_prefill(ctx, Hq, Hkv, D, scale, seconds):
         pool = PoolModel(N, 16, rng.permutation(N))
         sq = pool.new_seq()
         slots, _ = pool.append(sq, ctx + R)
-        cache = CacheModel(N, Hkv, D, "bf16", fill_nan=True)
-        cache.append(wl.normal_bits(rng, (ctx + R, Hkv, D), "bf16"), wl.normal_bits(rng, (ctx + R, Hkv, D), "bf16"),
-                     slots)
+        kb, vb = wl.normal_bits(rng, (ctx + R, Hkv, D), "bf16"), wl.normal_bits(rng, (ctx + R, Hkv, D), "bf16")
+        if fp8:
+            cache = Fp8CacheModel(N, Hkv, D)
+            cache.append(oatt.bits_to_f64(kb, "bf16").astype(np.float32),
+                         oatt.bits_to_f64(vb, "bf16").astype(np.float32), slots)
+        else:
+            cache = CacheModel(N, Hkv, D, "bf16", fill_nan=True)
+            cache.append(kb, vb, slots)
         q = wl.normal_bits(rng, (R, Hq, D), "bf16")
         table, _ = pool.block_tables([sq], len(pool.tables[sq]))
         t0 = time.perf_counter()
-        oatt.prefill_chunk(q, cache, table[0], ctx, scale)
+        oatt.prefill_chunk(q, cache, table[0], ctx, scale, q_dtype="bf16")
         el = time.perf_counter() - t0
         if el >= seconds or R >= 512:
             break
@@ -223,7 +239,8 @@ def cpu_baseline_prefill(ctx, Hq, Hkv, D, scale, seconds):
     flops = sum(ctx + i + 1 for i in range(R)) * Hq * 4 * D
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {R} of 512 chunk rows after {ctx} cached tokens, numpy fp64, {el:.1f} s"}
+            "sample": f"first {R} of 512 chunk rows after {ctx} cached tokens" + (" (fp8 cache)" if fp8 else "") +
+                      f", numpy fp64, {el:.1f} s"}
 
 
 def trace_partition_size(B: int, Hkv: int, max_len: int) -> int:
@@ -1143,6 +1160,8 @@ def main():
         torch.cuda.empty_cache()
         if "prefill" in extras:
             res["prefill"] = measure_prefill(args, dev)
+        if "prefill_fp8" in extras:
+            res["prefill_fp8"] = measure_prefill(args, dev, fp8=True)
         if "long" in extras:
             res["long_context"] = measure_long(args, dev)
             if not args.no_cpu_baseline:

@@ -476,6 +476,24 @@ int paged_attention_decode_append_fp8(void* out, int32_t out_dtype, const void* 
                                       void* workspace, size_t workspace_bytes, int32_t q_dtype,
                                       const int32_t* host_context_lens, pkv_stream_t stream);
 
+/*
+ * paged_attention_prefill_chunk_fp8 - paged_attention_prefill_chunk over an fp8 cache: causal
+ * attention of one prompt chunk ([Chapter] "How the scheduler works", [Notes] "Prefill gets in the
+ * way") against the values the quantised cache stands for (code * scale).  The chunk's own K/V must
+ * already be appended (paged_cache_append_fp8).
+ *   out         device [C][num_q_heads][head_dim] of out_dtype (PKV_F32 or q_dtype).
+ *   query       device [C][num_q_heads][head_dim] of q_dtype (PKV_BF16 or PKV_F16).
+ *   k_cache, v_cache, k_scale, v_scale  the fp8 layouts above.
+ *   block_table device int32 [>= ceil((ctx_start + C) / block_size)] of the one sequence.
+ *   scale       positive and finite (PKV_EINVAL otherwise).
+ * Codes are widened exactly to q_dtype for the matrix-core products; accumulation is fp32.
+ */
+int paged_attention_prefill_chunk_fp8(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                      const void* v_cache, const void* k_scale, const void* v_scale,
+                                      const int32_t* block_table, int32_t ctx_start, int32_t C, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
+                                      float scale, int32_t q_dtype, pkv_stream_t stream);
+
 /* ============================== host block pool ============================== */
 /*
  * [Serving] Step 4: a pool of physical block ids with a free list; allocation takes the id at the

@@ -87,6 +87,8 @@ _SIGS = {
     "paged_cache_copy_blocks_fp8": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
     "paged_check_inputs": (C.c_int, [_vp, _vp, _i32, _i32, _i32, _vp, _i32, _i32, _i32, _vp, _vp]),
     "paged_probe_stream_read": (C.c_int, [_vp, _sz, _vp, _i32, _vp]),
+    "paged_attention_prefill_chunk_fp8": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
+                                                    _i32, _i32, _i32, _f32, _i32, _vp]),
     "paged_attention_decode_fp8": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp]),
     "paged_attention_decode_fp8_partitions": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,

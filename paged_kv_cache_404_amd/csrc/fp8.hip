@@ -27,7 +27,7 @@
 #include <algorithm>
 #include <cmath>
 
-#include "device.h"
+#include "fp8_device.h"
 
 namespace pkv {
 namespace {
@@ -164,31 +164,6 @@ __device__ __forceinline__ f32x4 mfma_f8(u32x4 a, u32x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0,
                                                   0, 0);
   }
-}
-
-// Two E4M3 codes (the low or high half of w) -> two 16-bit elements of the product type, exact.
-template <int DT, bool HIGH>
-__device__ __forceinline__ uint32_t widen2(uint32_t w) {
-  if constexpr (DT == PKV_BF16) {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HIGH));
-  } else {
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HIGH));
-  }
-}
-
-// Eight codes (two dwords) -> one 8-element operand fragment.
-template <int DT>
-__device__ __forceinline__ u32x4 widen8(uint32_t w0, uint32_t w1) {
-  return u32x4{widen2<DT, false>(w0), widen2<DT, true>(w0), widen2<DT, false>(w1), widen2<DT, true>(w1)};
-}
-
-__device__ __forceinline__ u32x4 keep_first8(u32x4 v, int n) {
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t m = (2 * w + 1 < n) ? 0xFFFFFFFFu : ((2 * w < n) ? 0x0000FFFFu : 0u);
-    v[w] &= m;
-  }
-  return v;
 }
 
 __device__ __forceinline__ int clamp_len_f8(const Fp8Args& a, int b) {

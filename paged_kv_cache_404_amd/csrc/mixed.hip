@@ -92,6 +92,8 @@ __global__ void __launch_bounds__(512) mixed_kernel(MixedArgs m) {
   pa.num_blocks = m.num_blocks;
   pa.row_tiles = ch.row_tiles;
   pa.scale_log2 = m.scale_log2;
+  pa.ksc = nullptr;
+  pa.vsc = nullptr;
   prefill_tile<DT, DT_OUT, D, G>(pa, local, smem);
 }
 

@@ -4,7 +4,7 @@
 #pragma once
 #include <type_traits>
 
-#include "device.h"
+#include "fp8_device.h"
 
 namespace pkv {
 namespace {
@@ -26,6 +26,8 @@ struct PrefillArgs {
   int32_t num_blocks;
   int32_t row_tiles;  // ceil(C / 16)
   float scale_log2;
+  const float* ksc;  // fp8 cache only: K / V scales, fp32 [num_blocks][Hkv][16]
+  const float* vsc;
 };
 
 // One workgroup = 16 chunk rows x the G query heads of one KV head.  A wave owns HPW = min(G, 2)
@@ -52,11 +54,20 @@ constexpr int prefill_smem_floats() {
 
 // The body of one workgroup; id = its index among the row_tiles * Hkv workgroups of the chunk.
 // smem: prefill_smem_floats<D, G>() floats of LDS.
-template <int DT, int DT_OUT, int D, int G>
+//
+// FP8: the cache holds E4M3 codes with one K and one V scale per (block, head, slot), the query
+// and the products are DT (bf16 / fp16).  A lane's 16-byte K load holds dimensions
+// [64p + 16 q4, +16) of one token (one 512-byte run per block and 64 dimensions), widened exactly
+// into k-steps 2p and 2p + 1; the query fragments take the same dimension order.  A V load is the
+// 8 codes of a dimension for the lane's 8 keys ([D][16] tile).  The scales enter outside the
+// products: a score is multiplied by its key's scale, a weight by its value's scale before P.V
+// (the softmax sum takes the unscaled weight).
+template <int DT, int DT_OUT, int D, int G, bool FP8 = false>
 __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float* smem) {
   constexpr int KS = D / 32;
+  constexpr int KP = D / 64;  // FP8: 16-byte K loads per token set
   constexpr int NB = D / 16;
-  constexpr int TILE = kBlock * D;
+  constexpr int TILE = kBlock * D;  // elements (bytes for FP8) of one (block, head) tile
   constexpr int HPW = PrefillShape<G>::HPW;
   constexpr int HSETS = PrefillShape<G>::HSETS;
   constexpr int KSPLIT = PrefillShape<G>::KSPLIT;
@@ -92,6 +103,8 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
 
   const uint16_t* __restrict__ kc = static_cast<const uint16_t*>(a.k);
   const uint16_t* __restrict__ vc = static_cast<const uint16_t*>(a.v);
+  const uint8_t* __restrict__ k8 = static_cast<const uint8_t*>(a.k);
+  const uint8_t* __restrict__ v8 = static_cast<const uint8_t*>(a.v);
 
   u32x4 qf[HPW][KS];
 #pragma unroll
@@ -99,17 +112,22 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
     const uint16_t* qrow =
         static_cast<const uint16_t*>(a.q) + (static_cast<int64_t>(min(my_row, a.C - 1)) * a.Hq + hq0 + h) * D;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      qf[h][ks] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + ks * 32 + q4 * 8) : u32x4{0, 0, 0, 0};
+    for (int ks = 0; ks < KS; ++ks) {
+      // FP8: k-step 2p + f holds dimensions [64p + 16 q4 + 8f, +8), the K loads' order
+      const int d0 = FP8 ? (ks >> 1) * 64 + q4 * 16 + (ks & 1) * 8 : ks * 32 + q4 * 8;
+      qf[h][ks] = row_ok ? *reinterpret_cast<const u32x4*>(qrow + d0) : u32x4{0, 0, 0, 0};
+    }
   }
 
   // Q.K product #s row m holds token 8*(m/4) + m%4 + 4s of the step's block m/8; in the K tile
   // order those rows of one k-step are one 512-byte run per block (see k_chunk_pos).  Lane
   // (row, q4) then holds the scores of step keys 8*q4 .. 8*q4+7, the k-range of its P row.
   const bool k_from_b = n16 >= 8;
-  const int k_in_tile = (q4 * 8 + (n16 & 7)) * 8;
-  const bool v_from_b = q4 >= 2;
-  const int v_in_tile = (q4 & 1) * D * 8 + n16 * 8;  // V tile [token half][D][8 tokens]
+  const int k_in_tile = FP8 ? (n16 & 7) * 64 + q4 * 16 : (q4 * 8 + (n16 & 7)) * 8;
+  const bool v_from_b = q4 >= 2;  // also the block of the lane's 8 keys' scales
+  // V tile [token half][D][8 tokens]; FP8: [D][16] codes
+  const int v_in_tile = FP8 ? n16 * kBlock + (q4 & 1) * 8 : (q4 & 1) * D * 8 + n16 * 8;
+  const int s_in_head = (q4 & 1) * 8;  // FP8: the lane's 8 keys in their block's scale row
 
   f32x4 o[HPW][NB];
   float m_run[HPW], l_run[HPW];  // per head: reference maximum (log2 domain) and this lane's sum
@@ -142,29 +160,54 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
     const int tab = min(max(a.table[min(cb0 + lane, kblocks - 1)], 0), a.num_blocks - 1);
 
     u32x4 kf[2 * KS], vf[NB];
-    auto tiles = [&](int st, int64_t& tA, int64_t& tB) {
+    u32x4 k8f[2 * KP];  // FP8: raw codes, token set s at [s * KP + p]
+    u32x2 v8f[NB];
+    f32x4 ksf[2], vsf[2];  // FP8: scales of the lane's 8 keys
+    auto heads = [&](int st, int64_t& hA, int64_t& hB) {
       const int j = 2 * (st - c0);
       const int bA = __builtin_amdgcn_readlane(tab, j);
       const int bB = __builtin_amdgcn_readlane(tab, min(j + 1, cnb - 1));  // a lone last block pairs with itself
-      tA = (static_cast<int64_t>(bA) * a.Hkv + g) * TILE;
-      tB = (static_cast<int64_t>(bB) * a.Hkv + g) * TILE;
+      hA = static_cast<int64_t>(bA) * a.Hkv + g;
+      hB = static_cast<int64_t>(bB) * a.Hkv + g;
     };
     auto load_k = [&](int st) {
-      int64_t tA, tB;
-      tiles(st, tA, tB);
-      const uint16_t* kp = kc + (k_from_b ? tB : tA) + k_in_tile;
+      int64_t hA, hB;
+      heads(st, hA, hB);
+      if constexpr (FP8) {
+        const uint8_t* kp = k8 + (k_from_b ? hB : hA) * TILE + k_in_tile;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        kf[ks] = *reinterpret_cast<const u32x4*>(kp + (2 * ks) * 256);
-        kf[KS + ks] = *reinterpret_cast<const u32x4*>(kp + (2 * ks + 1) * 256);
+        for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+          for (int pp = 0; pp < KP; ++pp)
+            k8f[ss * KP + pp] = *reinterpret_cast<const u32x4*>(kp + (pp * 2 + ss) * 512);
+        }
+        const float* sp = a.ksc + (v_from_b ? hB : hA) * kBlock + s_in_head;
+        ksf[0] = *reinterpret_cast<const f32x4*>(sp);
+        ksf[1] = *reinterpret_cast<const f32x4*>(sp + 4);
+      } else {
+        const uint16_t* kp = kc + (k_from_b ? hB : hA) * TILE + k_in_tile;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          kf[ks] = *reinterpret_cast<const u32x4*>(kp + (2 * ks) * 256);
+          kf[KS + ks] = *reinterpret_cast<const u32x4*>(kp + (2 * ks + 1) * 256);
+        }
       }
     };
     auto load_v = [&](int st) {
-      int64_t tA, tB;
-      tiles(st, tA, tB);
-      const uint16_t* vp = vc + (v_from_b ? tB : tA) + v_in_tile;
+      int64_t hA, hB;
+      heads(st, hA, hB);
+      if constexpr (FP8) {
+        const uint8_t* vp = v8 + (v_from_b ? hB : hA) * TILE + v_in_tile;
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) vf[nb] = *reinterpret_cast<const u32x4*>(vp + nb * 16 * 8);
+        for (int nb = 0; nb < NB; ++nb) v8f[nb] = *reinterpret_cast<const u32x2*>(vp + nb * 16 * kBlock);
+        const float* sp = a.vsc + (v_from_b ? hB : hA) * kBlock + s_in_head;
+        vsf[0] = *reinterpret_cast<const f32x4*>(sp);
+        vsf[1] = *reinterpret_cast<const f32x4*>(sp + 4);
+      } else {
+        const uint16_t* vp = vc + (v_from_b ? hB : hA) * TILE + v_in_tile;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) vf[nb] = *reinterpret_cast<const u32x4*>(vp + nb * 16 * 8);
+      }
     };
 
     // One 32-key step for all HPW heads; with `prefetch` the next step's loads are issued as
@@ -173,6 +216,31 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
       const int t0 = st * 32;
       const int nvalid = min(32, nkeys - t0);
       const bool masked = t0 + 32 > full_keys;  // causal limit (and the chunk's end) inside this step
+      // K operands: the loaded fragments, or (FP8) the codes widened, after which the code
+      // registers take the next step's loads.
+      u32x4 kk[2 * KS];
+      f32x4 ks_cur[2];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int ss = 0; ss < 2; ++ss) {
+#pragma unroll
+          for (int pp = 0; pp < KP; ++pp) {
+            const u32x4 r = k8f[ss * KP + pp];
+            kk[ss * KS + 2 * pp] = widen8<DT>(r[0], r[1]);
+            kk[ss * KS + 2 * pp + 1] = widen8<DT>(r[2], r[3]);
+          }
+        }
+        ks_cur[0] = ksf[0];
+        ks_cur[1] = ksf[1];
+        if (prefetch) {
+          asm volatile("" ::: "memory");
+          load_k(st + 1);
+          asm volatile("" ::: "memory");
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2 * KS; ++i) kk[i] = kf[i];
+      }
       f32x4 s1[HPW], s2[HPW];
 #pragma unroll
       for (int h = 0; h < HPW; ++h) {
@@ -180,24 +248,39 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
         s2[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          s1[h] = mfma16x16x32<DT>(kf[ks], qf[h][ks], s1[h]);
-          s2[h] = mfma16x16x32<DT>(kf[KS + ks], qf[h][ks], s2[h]);
+          s1[h] = mfma16x16x32<DT>(kk[ks], qf[h][ks], s1[h]);
+          s2[h] = mfma16x16x32<DT>(kk[KS + ks], qf[h][ks], s2[h]);
         }
       }
-      if (prefetch) {
+      if (!FP8 && prefetch) {
         asm volatile("" ::: "memory");
         load_k(st + 1);
         asm volatile("" ::: "memory");
       }
       if (nvalid < 32) {
-        // Keys past the last visible one may be stale (or NaN): zero them in V.
+        // Keys past the last visible one may be stale (or NaN): zero them in V (FP8: their
+        // codes and value scales).
         const int keep = min(8, max(0, nvalid - 8 * q4));
+        if constexpr (FP8) {
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
+          for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-          for (int wd = 0; wd < 4; ++wd) {
-            const uint32_t m = (2 * wd + 1 < keep) ? 0xFFFFFFFFu : ((2 * wd < keep) ? 0x0000FFFFu : 0u);
-            vf[nb][wd] &= m;
+            for (int wd = 0; wd < 2; ++wd) {
+              const int kb = keep - 4 * wd;  // bytes of this dword to keep
+              const uint32_t m = kb >= 4 ? 0xFFFFFFFFu : (kb <= 0 ? 0u : (1u << (8 * kb)) - 1u);
+              v8f[nb][wd] &= m;
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i) vsf[i >> 2][i & 3] = i < keep ? vsf[i >> 2][i & 3] : 0.f;
+        } else {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+            for (int wd = 0; wd < 4; ++wd) {
+              const uint32_t m = (2 * wd + 1 < keep) ? 0xFFFFFFFFu : ((2 * wd < keep) ? 0x0000FFFFu : 0u);
+              vf[nb][wd] &= m;
+            }
           }
         }
       }
@@ -205,13 +288,14 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
       // give the maxima of scaled ones.  Both heads go through each phase before the next one, so
       // that the common path (no mask, no rescale) is one basic block in which the compiler can
       // issue one head's softmax arithmetic between the other head's matrix instructions.
+      // FP8: the key's scale (>= 0) is part of the raw score.
       float sc[HPW][8];
 #pragma unroll
       for (int h = 0; h < HPW; ++h) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          sc[h][j] = s1[h][j];
-          sc[h][4 + j] = s2[h][j];
+          sc[h][j] = FP8 ? s1[h][j] * ks_cur[0][j] : s1[h][j];
+          sc[h][4 + j] = FP8 ? s2[h][j] * ks_cur[1][j] : s2[h][j];
         }
       }
       if (masked) {
@@ -258,6 +342,24 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
           }
         }
       }
+      // V operands: the loaded fragments, or (FP8) the codes widened and the value scales kept,
+      // after which their registers take the next step's loads.
+      u32x4 vv[NB];
+      float vs_cur[8];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) vv[nb] = widen8<DT>(v8f[nb][0], v8f[nb][1]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vs_cur[i] = vsf[i >> 2][i & 3];
+        if (prefetch) {
+          asm volatile("" ::: "memory");
+          load_v(st + 1);
+          asm volatile("" ::: "memory");
+        }
+      } else {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) vv[nb] = vf[nb];
+      }
 #pragma unroll
       for (int h = 0; h < HPW; ++h) {
         // Before a row's first visible key m_run is the finite kNoMax: masked scores (-inf) get
@@ -269,6 +371,10 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
 #pragma unroll
         for (int i = 1; i < 8; ++i) psum += pv[i];
         l_run[h] += psum;
+        if constexpr (FP8) {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pv[i] *= vs_cur[i];
+        }
         // hi = the weights rounded to 16 bits, lo = the rounding residuals rounded to 16 bits.
         u32x4 hi, lo;
 #pragma unroll
@@ -278,11 +384,11 @@ __device__ __forceinline__ void prefill_tile(const PrefillArgs& a, int id, float
         }
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
-          o[h][nb] = mfma16x16x32<DT>(hi, vf[nb], o[h][nb]);
-          o[h][nb] = mfma16x16x32<DT>(lo, vf[nb], o[h][nb]);
+          o[h][nb] = mfma16x16x32<DT>(hi, vv[nb], o[h][nb]);
+          o[h][nb] = mfma16x16x32<DT>(lo, vv[nb], o[h][nb]);
         }
       }
-      if (prefetch) {
+      if (!FP8 && prefetch) {
         asm volatile("" ::: "memory");
         load_v(st + 1);
         asm volatile("" ::: "memory");

@@ -429,6 +429,40 @@ def paged_attention_decode_fp8(out, query, k_cache, v_cache, k_scale, v_scale, b
     check(lib.paged_attention_decode_fp8(*args, _stream(stream)))
 
 
+def _fp8_prefill_args(out, query, k_cache, v_cache, k_scale, v_scale, block_table, ctx_start, scale):
+    N, Hkv, bs, D = _fp8_shapes(k_cache, v_cache, k_scale, v_scale)
+    _dev(out, query, block_table)
+    if query.dim() != 3 or out.shape != query.shape or query.shape[2] != D:
+        raise ValueError("query and out must be [C][Hq][head_dim]")
+    C, Hq, _ = query.shape
+    if block_table.dtype != torch.int32:
+        raise TypeError("block_table must be int32")
+    if block_table.numel() * bs < ctx_start + C:
+        raise ValueError("block_table too short for ctx_start + C")
+    return (out.data_ptr(), dtype_code(out.dtype), query.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+            k_scale.data_ptr(), v_scale.data_ptr(), block_table.data_ptr(), int(ctx_start), C, Hq, Hkv, D, bs, N,
+            float(scale), dtype_code(query.dtype))
+
+
+def paged_attention_prefill_chunk_fp8(out, query, k_cache, v_cache, k_scale, v_scale, block_table, ctx_start, scale,
+                                      stream=None) -> None:
+    """Prefill chunk over an fp8 cache; query bf16/fp16 [C][Hq][D]; out fp32 or the query dtype."""
+    check(lib.paged_attention_prefill_chunk_fp8(*_fp8_prefill_args(out, query, k_cache, v_cache, k_scale, v_scale,
+                                                                   block_table, ctx_start, scale), _stream(stream)))
+
+
+class PreparedPrefillFp8:
+    """paged_attention_prefill_chunk_fp8 with its arguments marshalled once."""
+
+    def __init__(self, out, query, k_cache, v_cache, k_scale, v_scale, block_table, ctx_start, scale, stream=None):
+        self._keep = (out, query, k_cache, v_cache, k_scale, v_scale, block_table)
+        self.args = _fp8_prefill_args(out, query, k_cache, v_cache, k_scale, v_scale, block_table, ctx_start, scale)
+        self.stream = _stream(stream)
+
+    def __call__(self) -> None:
+        check(lib.paged_attention_prefill_chunk_fp8(*self.args, self.stream))
+
+
 def _fp8_fused_args(args, new_key, new_value):
     """Argument tuple of paged_attention_decode_append_fp8 from a _fp8_decode_args tuple."""
     _dev(new_key, new_value)

@@ -280,3 +280,75 @@ def test_fused_append_fp8_llama_shaped_as_benched():
     got = out.cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all()
     assert float(np.abs(got - ref).max()) <= ATOL
+
+
+def _prefill_fp8(seed, ctx_start, C, Hq, Hkv, D, q_dtype, out_dtype=torch.float32):
+    total = ctx_start + C
+    m, seqs, rng = _build([total], Hkv, D, seed, in_dtype=q_dtype)
+    q = wl.normal_bits(rng, (C, Hq, D), q_dtype)
+    tables, _ = m.tables(seqs)
+    out = torch.full((C, Hq, D), float("nan"), dtype=out_dtype, device="cuda")
+    scale = 1.0 / np.sqrt(D)
+    ops.paged_attention_prefill_chunk_fp8(out, to_dev(q, q_dtype), m.k, m.v, m.ks, m.vs, i32(tables[0]), ctx_start,
+                                          scale)
+    torch.cuda.synchronize()
+    return m, seqs, q, out, tables, scale
+
+
+PREFILL = [
+    # ctx_start, C, Hq, Hkv, D, query dtype
+    (0, 1, 32, 8, 128, "bf16"),
+    (0, 37, 32, 8, 128, "bf16"),
+    (5, 16, 8, 8, 64, "bf16"),
+    (100, 300, 32, 8, 128, "bf16"),
+    (33, 17, 16, 16, 64, "bf16"),
+    (0, 64, 64, 8, 128, "bf16"),
+    (1500, 530, 32, 8, 128, "bf16"),
+    (250, 130, 16, 8, 128, "f16"),
+    (17, 50, 8, 4, 64, "f16"),
+    (0, 33, 8, 1, 64, "f16"),
+]
+
+
+@pytest.mark.parametrize("ctx_start,C,Hq,Hkv,D,q_dtype", PREFILL)
+def test_prefill_fp8_parity(ctx_start, C, Hq, Hkv, D, q_dtype):
+    """Chunked prefill over the quantised cache: every output row against the oracle's causal
+    attention over the dequantised values, within 2e-3 (ragged chunks, empty and long contexts,
+    group sizes 1 to 8, both head sizes and query types)."""
+    m, seqs, q, out, tables, scale = _prefill_fp8(40 + C + ctx_start, ctx_start, C, Hq, Hkv, D, q_dtype)
+    ref = oatt.prefill_chunk(q, m.cache, tables[0], ctx_start, scale, q_dtype=q_dtype)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    err = float(np.abs(got - ref).max())
+    assert err <= ATOL, err
+
+
+def test_prefill_fp8_rows_match_fp8_decode_and_out_dtype():
+    """Row i of a chunk is the fp8 decode of a context of ctx_start + i + 1 tokens (two kernels,
+    same attention: within 2e-3); a bf16 output is the fp32 one rounded (within its half-ulp)."""
+    m, seqs, q, out, tables, scale = _prefill_fp8(45, 200, 48, 32, 8, 128, "bf16")
+    lens = np.array([201 + i for i in range(48)], dtype=np.int32)
+    dec = torch.empty((48, 32, 128), dtype=torch.float32, device="cuda")
+    tt = np.repeat(tables, 48, axis=0)
+    ops.paged_attention_decode_fp8(dec, to_dev(q, "bf16"), m.k, m.v, m.ks, m.vs, i32(tt), i32(lens), int(lens.max()),
+                                   scale, 0, None)
+    out_bf = torch.empty((48, 32, 128), dtype=torch.bfloat16, device="cuda")
+    ops.paged_attention_prefill_chunk_fp8(out_bf, to_dev(q, "bf16"), m.k, m.v, m.ks, m.vs, i32(tables[0]), 200, scale)
+    torch.cuda.synchronize()
+    assert (dec - out).abs().max().item() <= ATOL
+    ref = oatt.prefill_chunk(q, m.cache, tables[0], 200, scale, q_dtype="bf16")
+    got = out_bf.float().cpu().numpy()
+    assert (np.abs(got - ref) <= ATOL + 2.0 ** -9 * np.abs(ref)).all()
+
+
+def test_prefill_fp8_rejects():
+    k, v, ks, vs = ops.fp8_cache(4, 2, 64)
+    q = torch.zeros((3, 4, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((3, 4, 64), dtype=torch.float32, device="cuda")
+    tab = torch.zeros(4, dtype=torch.int32, device="cuda")
+    with pytest.raises(Exception):
+        ops.paged_attention_prefill_chunk_fp8(out, q.float(), k, v, ks, vs, tab, 0, 0.1)  # fp32 query
+    with pytest.raises(Exception):
+        ops.paged_attention_prefill_chunk_fp8(out, q, k, v, ks, vs, tab, 0, -0.1)  # scale
+    with pytest.raises(Exception):
+        ops.paged_attention_prefill_chunk_fp8(out, q, k, v, ks, vs, tab, 62, 0.1)  # past the pool
