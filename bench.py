@@ -37,7 +37,7 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attn: effective KV HBM GB/s (% of peak); seqs*steps/s"
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E, published
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partitions_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
 def parse():
@@ -55,7 +55,7 @@ def parse():
                     help="do not pass the host copy of the context lengths (longest-first work order)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the chunked-prefill and long-context measurements reported beside the main line")
-    ap.add_argument("--extras", default="prefill,prefill_fp8,long,prefix,fp8,mixed,trace",
+    ap.add_argument("--extras", default="tiny,prefill,prefill_fp8,long,prefix,fp8,mixed,trace",
                     help="comma-separated side lines to run beside the main line (default: all of them)")
     mode = ap.add_mutually_exclusive_group()
     mode.add_argument("--overlap", action="store_true",
@@ -67,75 +67,133 @@ def parse():
     ap.add_argument("--cpu-baseline-only", action="store_true",
                     help="print the oracle CPU baseline of the workload as one JSON line and exit (no GPU use); "
                          "the bench runs it in a child process pinned to one BLAS/OpenMP thread")
-    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="write the HBM traffic record from two rocprofv3 --pmc counter_collection.csv files "
-                         "(FETCH_SIZE run, WRITE_SIZE run) of this script, then exit")
+    ap.add_argument("--only", choices=sorted(TRAFFIC_LINES),
+                    help="counter run: measure this one line alone (llama = the main line without side lines), "
+                         "end with a 1 GiB device copy for calibration, print its JSON")
+    ap.add_argument("--traffic-from", nargs=3, metavar=("LINE", "FETCH_CSV", "WRITE_CSV"),
+                    help="write the line's HBM traffic record from the counter_collection.csv files of two "
+                         "rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of --only LINE, then exit")
     return ap.parse_args()
 
 
-def source_digest() -> str:
-    """sha256 over the sources the decode kernel is compiled from."""
+# HBM traffic records (rocprofv3 FETCH_SIZE / WRITE_SIZE) per reported line: the dispatches counted
+# (kernel-name pattern), the sources that kernel is compiled from (a record counts only while their
+# sha256 matches), and whether the figure is per launch (mean over the dispatches) or per replay of
+# the trace (sum over them).
+_DEC_SRC = ("decode.hip", "decode_part.h", "decode_host.h", "device.h")
+_PRE_SRC = ("prefill_tile.h", "device.h", "fp8_device.h")
+TRAFFIC_LINES = {
+    "llama": (r"decode_mfma_kernel<.*, true>", _DEC_SRC, "launch"),
+    "long": (r"decode_mfma_kernel<.*, true>", _DEC_SRC, "launch"),
+    "tiny": (r"decode_valu_kernel<", _DEC_SRC, "launch"),
+    "prefill": (r"prefill_mfma_kernel<", ("prefill.hip",) + _PRE_SRC, "launch"),
+    "prefill_fp8": (r"prefill_fp8_kernel<", ("prefill_fp8.hip",) + _PRE_SRC, "launch"),
+    "fp8": (r"decode_fp8_kernel<.*, false>", ("fp8.hip", "fp8_device.h", "device.h"), "launch"),
+    "mixed": (r"decode_group_kernel<", ("decode_group.hip", "decode_group.h") + _DEC_SRC, "launch"),
+    "trace": (r"decode_(mfma|reduce)_kernel<", _DEC_SRC, "replay"),
+}
+# The mixed step's counter run times this one decode variant (the fastest one on record).
+MIXED_COUNTED_VARIANT = "decode_grouped_2_split512"
+
+
+def source_digest(line: str) -> str:
+    """sha256 over the sources the counted kernel of `line` is compiled from."""
     h = hashlib.sha256()
-    for name in ("decode.hip", "decode_part.h", "device.h"):
+    for name in TRAFFIC_LINES[line][1]:
         h.update(open(os.path.join(ROOT, "paged_kv_cache_404_amd", "csrc", name), "rb").read())
     return h.hexdigest()
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per launch of the partition kernel from rocprofv3 counters, when they were taken
-    on the current kernel source; else None."""
+def measured_traffic(line: str):
+    """HBM bytes per launch (per trace replay) of the line's kernel from the committed counter
+    record, when it was taken on the current kernel sources; else None."""
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    entry = rec.get(workload)
-    if not entry or entry.get("decode_sources_sha256") != source_digest():
+    entry = rec.get(line)
+    if not entry or entry.get("sources_sha256") != source_digest(line):
         return None
-    return entry.get("hbm_bytes_per_launch")
+    return entry.get("hbm_bytes_per_launch", entry.get("hbm_bytes_per_replay"))
 
 
-def write_traffic(workload: str, fetch_csv: str, write_csv: str) -> dict:
-    """HBM bytes per decode partition launch from two counter runs of this script.
+def write_traffic(line: str, fetch_csv: str, write_csv: str) -> dict:
+    """HBM bytes of the line's kernel from two counter runs of `bench.py --only LINE`.
 
     FETCH_SIZE and WRITE_SIZE are KiB per dispatch.  Each is scaled by what the same counter
-    reads for the 1 GiB device-to-device copy this script runs (known bytes: 1 GiB read and
-    1 GiB written), so the figure is in true bytes whatever the counter's granularity."""
+    reads for the 1 GiB device-to-device copy every such run ends with (known bytes: 1 GiB read
+    and 1 GiB written), so the figure is in true bytes whatever the counter's granularity."""
     import csv
+    import re
+
+    pattern, _, per = TRAFFIC_LINES[line]
 
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         copy = max(float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"])
-        dec_rows = [r for r in rows if "decode_mfma_kernel" in r["Kernel_Name"]]
-        if not dec_rows or len({r["Kernel_Name"] for r in dec_rows}) != 1:
-            raise SystemExit(f"{path}: need dispatches of exactly one decode_mfma_kernel instantiation "
-                             "(run the counter passes with --no-extra)")
-        dec = [float(r["Counter_Value"]) for r in dec_rows]
-        return copy, sum(dec) / len(dec), len(dec)
+        sel = [r for r in rows if re.search(pattern, r["Kernel_Name"])]
+        names = {r["Kernel_Name"] for r in sel}
+        if not sel or (per == "launch" and len(names) != 1):
+            raise SystemExit(f"{path}: need dispatches of exactly one kernel matching {pattern!r}, found {names}")
+        vals = [float(r["Counter_Value"]) for r in sel]
+        return copy, (sum(vals) / len(vals) if per == "launch" else sum(vals)), len(vals), sorted(names)
 
-    f_copy, f_dec, n_f = per_kernel(fetch_csv, "FETCH_SIZE")
-    w_copy, w_dec, n_w = per_kernel(write_csv, "WRITE_SIZE")
+    f_copy, f_k, n_f, names = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_copy, w_k, n_w, _ = per_kernel(write_csv, "WRITE_SIZE")
     known = float(1 << 30)
     f_scale, w_scale = known / (f_copy * 1024), known / (w_copy * 1024)
-    hbm = f_dec * 1024 * f_scale + w_dec * 1024 * w_scale
+    hbm = f_k * 1024 * f_scale + w_k * 1024 * w_scale
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         rec = {}
-    rec[workload] = {
-        "decode_sources_sha256": source_digest(),
-        "hbm_bytes_per_launch": round(hbm),
-        "fetch_kib_per_dispatch": round(f_dec, 1),
-        "write_kib_per_dispatch": round(w_dec, 1),
+    unit = "per_dispatch" if per == "launch" else "per_replay"
+    rec[line] = {
+        "kernels": names,
+        "sources_sha256": source_digest(line),
+        f"hbm_bytes_per_{per}": round(hbm),
+        f"fetch_kib_{unit}": round(f_k, 1),
+        f"write_kib_{unit}": round(w_k, 1),
         "dispatches": [n_f, n_w],
         "fetch_scale": round(f_scale, 4),
         "write_scale": round(w_scale, 4),
         "calibration": "1 GiB device-to-device copy (__amd_rocclr_copyBuffer) in the same run: "
                        f"FETCH_SIZE {f_copy:.1f} KiB, WRITE_SIZE {w_copy:.1f} KiB",
+        "counter_runs": f"rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE -- python3 bench.py --only {line} --steps 5 "
+                        "--warmup 2",
     }
+    if line == "mixed":
+        rec[line]["variant"] = MIXED_COUNTED_VARIANT
     with open(TRAFFIC_FILE, "w") as f:
-        json.dump(rec, f, indent=1)
+        json.dump(rec, f, indent=1, sort_keys=True)
         f.write("\n")
-    return rec[workload]
+    return rec[line]
+
+
+def _traffic_fields(line: str, algorithmic_bytes: int) -> dict:
+    """`traffic` (HBM bytes per launch from the line's counter record, None when the kernel changed
+    since) and its ratio to the launch's algorithmic bytes."""
+    t = measured_traffic(line)
+    return {"traffic": t, "algorithmic_bytes": algorithmic_bytes,
+            "traffic_over_algorithmic": round(t / algorithmic_bytes, 4) if t else None}
+
+
+def _prefill_bytes(ctx: int, C: int, Hq: int, Hkv: int, D: int, fp8: bool) -> int:
+    """Bytes a prefill chunk must move at least: the K/V of its ctx + C visible tokens once (fp8:
+    codes + fp32 K and V scales per slot), the queries in, the fp32 outputs out."""
+    T = ctx + C
+    kv = T * Hkv * (2 * D + 8) if fp8 else T * Hkv * D * 2 * 2
+    return kv + C * Hq * D * 2 + C * Hq * D * 4
+
+
+def calibration_copy(dev) -> None:
+    """One 1 GiB device-to-device copy: the known-size kernel the counter records are scaled by."""
+    import torch
+
+    src = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def _events_avg_us(torch, stream, fn, n):
@@ -196,7 +254,8 @@ def measure_prefill(args, dev, fp8=False):
         "flops_per_call": flops,
         "roofline": {"bound": "mfma", "kernel": "prefill_fp8_kernel" if fp8 else "prefill_mfma_kernel",
                      "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     **_traffic_fields("prefill_fp8" if fp8 else "prefill", _prefill_bytes(ctx, C, Hq, Hkv, D, fp8))},
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_prefill(ctx, Hq, Hkv, D, w.scale, args.cpu_seconds / 2, fp8=fp8)
@@ -250,7 +309,7 @@ def trace_partition_size(B: int, Hkv: int, max_len: int) -> int:
     return 512
 
 
-def measure_trace(dev, choose_ps=trace_partition_size):
+def measure_trace(dev, choose_ps=trace_partition_size, counters=False):
     """The continuous-batching trace: 512 seeded requests (Poisson arrivals, lognormal prompts
     around 512 tokens, geometric outputs around 200), at most 128 running, a 12,288-block pool,
     32 q / 8 kv heads of 128, bf16.
@@ -262,7 +321,10 @@ def measure_trace(dev, choose_ps=trace_partition_size):
     steps replay back to back: the admitted prompts' K/V (paged_cache_append), then the fused
     append + decode over the live batch.  Behind a bounded spin the host enqueues the whole replay
     ahead of the GPU, so one event pair around it times device work only; the decode calls alone
-    and the prompt appends alone are replayed the same way for their own times."""
+    and the prompt appends alone are replayed the same way for their own times.
+
+    counters: a counter run; the decode calls of one replay run once (nothing else of the trace
+    on the GPU), so the counter record sums the HBM traffic of exactly one replay's decode."""
     import collections
 
     import numpy as np
@@ -357,6 +419,11 @@ def measure_trace(dev, choose_ps=trace_partition_size):
         kv_bytes += int(lens.sum()) * Hkv * 2 * D * 2 + B * Hq * D * 2
         calls.append((app, dec))
     stream = torch.cuda.current_stream()
+    if counters:
+        for _, dec in calls:
+            dec()
+        torch.cuda.synchronize()
+        return {"counted": "the decode calls of one replay", "steps": len(steps), "decode_kv_plus_q_bytes": kv_bytes}
     for app, dec in calls[:20]:  # warm-up (loads the kernels)
         if app is not None:
             app()
@@ -409,6 +476,10 @@ def measure_trace(dev, choose_ps=trace_partition_size):
         "decode_kv_plus_q_bytes": kv_bytes,
         "decode_gbs": round(gbs, 1),
         "decode_pct_of_peak_hbm": round(100 * gbs / PEAK_HBM_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel + decode_reduce_kernel, every decode call of "
+                     "one replay (traffic and algorithmic bytes per replay)", "achieved": round(gbs, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     **_traffic_fields("trace", kv_bytes)},
         "seqs_steps_per_s_gpu": round(seq_steps / (total_ms * 1e-3), 1),
         "timing": "three back-to-back replays behind a bounded spin, one event pair each: the whole "
                   "interleaved replay (seqs_steps_per_s_gpu, replay_gpu_ms), its decode calls alone "
@@ -453,7 +524,35 @@ def measure_prefix_cache():
     insert_us = (time.perf_counter() - t0) / n_iter * 1e6
     return {"workload": "prefix_cache_lookup_2048_tokens_pool_18023", "lookup_and_free_us": round(lookup_us, 2),
             "reinsert_us": round(insert_us, 2), "matched_tokens": int(n), "blocks_per_lookup": 128,
-            "note": "host time per call through the Python binding (ctypes call overhead included)"}
+            "note": "host time per call through the Python binding (ctypes call overhead included)",
+            "roofline": None,
+            "roofline_note": "host code only (a trie walk over 128 block hashes): no device kernel, no HBM roofline",
+            "cpu_baseline": cpu_baseline_prefix(prompt, req)}
+
+
+def cpu_baseline_prefix(prompt, req):
+    """The oracle pool's prefix cache on the same request: register the 2,048-token prompt, then
+    time lookups of the prompt plus 64 new tokens, each followed by freeing the new sequence."""
+    import numpy as np
+
+    from oracle import PoolModel
+
+    N = 18023
+    pool = PoolModel(N, 16, np.random.default_rng(9).permutation(N))
+    s = pool.new_seq()
+    pool.append(s, 2048)
+    pool.prefix_insert(s, [int(t) for t in prompt])
+    toks = [int(t) for t in req]
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        q, n = pool.prefix_lookup(toks)
+        pool.free_seq(q)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= 1.0 and reps >= 10:
+            break
+    return {"value": round(el / reps * 1e6, 2), "unit": "us per lookup and free", "cores": 1, "kind": "oracle",
+            "matched_tokens": int(n), "sample": f"{reps} lookups of the same request, pure Python, {el:.1f} s"}
 
 
 def measure_fp8(args, dev, bf16_kernel_us):
@@ -552,13 +651,56 @@ def measure_fp8(args, dev, bf16_kernel_us):
         "separate_launches_us_per_step": round(sep_us, 3),
         "kernel_us": {"append_fp8": round(app_us, 3), "decode_fp8": round(kern_us, 3),
                       "decode_fp8_fused_append": round(step_us, 3)},
-        "decode_speedup_over_bf16_cache": round(bf16_kernel_us / kern_us, 3),
+        "decode_speedup_over_bf16_cache": round(bf16_kernel_us / kern_us, 3) if bf16_kernel_us else None,
         "roofline": {"bound": "hbm", "kernel": "decode_fp8_kernel (decode alone, no append)", "achieved": round(achieved, 2),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None},
+                     **_traffic_fields("fp8", nbytes)},
         "format_error_vs_bf16_cache": err,
         "replicas": R,
+        **({} if args.no_cpu_baseline else {"cpu_baseline": cpu_baseline_fp8(w, args.cpu_seconds / 2)}),
     }
+
+
+def cpu_baseline_fp8(w, seconds: float, max_seqs: int = 8):
+    """The oracle over its FP8 cache model (codes times per-slot scales, fp64 attention) on the first
+    S = min(B, max_seqs) sequences of the batch, bf16 queries; bytes counted as on the GPU line."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import workloads as wl
+    from oracle import Fp8CacheModel, PoolModel
+    from oracle import attention as oatt
+
+    S = min(w.B, max_seqs)
+    lens = w.lens[:S]
+    rng = np.random.default_rng(1002)
+    N = sum(wl.blocks_for(int(L)) for L in lens) + 1
+    pool = PoolModel(N, 16, rng.permutation(N))
+    cache = Fp8CacheModel(N, w.Hkv, w.D)
+    seqs = []
+    for L in lens:
+        s = pool.new_seq()
+        slots, _ = pool.append(s, int(L))
+        cache.append(rng.standard_normal((int(L), w.Hkv, w.D)).astype(np.float32),
+                     rng.standard_normal((int(L), w.Hkv, w.D)).astype(np.float32), slots)
+        seqs.append(s)
+    q = wl.normal_bits(rng, (S, w.Hq, w.D), "bf16")
+    tables, tl = pool.block_tables(seqs, max(len(pool.tables[s]) for s in seqs))
+    tok = int(np.sum(lens.astype(np.int64)))
+    sample_bytes = tok * w.Hkv * w.D * 2 + tok * w.Hkv * 2 * 4 + S * w.Hq * w.D * 2
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oatt.paged_decode(q, cache, tables, tl, w.scale, q_dtype="bf16")
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and reps >= 3:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    per = el / reps
+    return {"value": round(sample_bytes / per / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "seqs_steps_per_s": round(S / per, 3),
+            "sample": f"{S} of {w.B} sequences ({tok} cached tokens, {sample_bytes} B of codes, scales and Q), "
+                      f"numpy fp64 over dequantised codes, {reps} calls in {el:.1f} s"}
 
 
 def _spin_cycles_per_ms(torch, stream):
@@ -587,12 +729,13 @@ def _spun_avg_us(torch, stream, fn, n, spin_cycles):
     return e0.elapsed_time(e1) * 1e3 / n
 
 
-def _mixed_case(args, dev, prefix_len, n, spin):
+def _mixed_case(args, dev, prefix_len, n, spin, counted=False):
     """One prefix-sharing step: 16 samples forked from a prefix_len-token prefix decode one token
     each, a 512-row chunk is prefilled after 4,096 cached tokens.  Times (HIP events behind a spin)
     the decode alone (plain single pass, grouped 2 and 4 samples per workgroup), the prefill alone,
     both as separate launches and as one mixed launch (plain and grouped), and the step = the
-    copy-on-write block copies (if any) + the append of its 16 + 512 tokens + attention."""
+    copy-on-write block copies (if any) + the append of its 16 + 512 tokens + attention.  counted:
+    only n calls of the decode variant the counter record covers (a counter run)."""
     import numpy as np
     import torch
 
@@ -654,16 +797,22 @@ def _mixed_case(args, dev, prefix_len, n, spin):
                 r[nm]()
         return fn
 
+    variants = {
+        "decode": ("dec",), "decode_split512": ("dec_p512",), "decode_grouped_2": ("dec_g2",),
+        "decode_grouped_4": ("dec_g4",), "decode_grouped_2_split512": ("dec_g2_p512",),
+        "prefill": ("pre",), "separate": ("dec", "pre"), "separate_grouped": ("dec_g2_p512", "pre"),
+        "mixed": ("mix",), "mixed_grouped": ("mix_g2_p512",),
+        "step_separate": ("copy", "append", "dec", "pre"), "step_mixed": ("copy", "append", "mix"),
+        "step_mixed_grouped": ("copy", "append", "mix_g2_p512"), "copies_and_append": ("copy", "append")}
+    if counted:
+        for i in range(n):
+            run(*variants[MIXED_COUNTED_VARIANT])(i)
+        torch.cuda.synchronize()
+        return {"counted_variant": MIXED_COUNTED_VARIANT, "calls": n}
     for nm in reps[0]:
         for i in range(3):
             run(nm)(i)
-    t = {key: _spun_avg_us(torch, stream, run(*names), n, spin) for key, names in (
-        ("decode", ("dec",)), ("decode_split512", ("dec_p512",)), ("decode_grouped_2", ("dec_g2",)),
-        ("decode_grouped_4", ("dec_g4",)), ("decode_grouped_2_split512", ("dec_g2_p512",)),
-        ("prefill", ("pre",)), ("separate", ("dec", "pre")), ("separate_grouped", ("dec_g2_p512", "pre")),
-        ("mixed", ("mix",)), ("mixed_grouped", ("mix_g2_p512",)),
-        ("step_separate", ("copy", "append", "dec", "pre")), ("step_mixed", ("copy", "append", "mix")),
-        ("step_mixed_grouped", ("copy", "append", "mix_g2_p512")), ("copies_and_append", ("copy", "append")))}
+    t = {key: _spun_avg_us(torch, stream, run(*names), n, spin) for key, names in variants.items()}
     # Algorithmic decode bytes: every distinct cached token once (the shared prefix's blocks are
     # the same physical blocks in all 16 tables) plus each sample's own tokens, K and V of the 8 KV
     # heads, and the queries.  Logical bytes count each sample's whole context.
@@ -697,14 +846,17 @@ def _mixed_case(args, dev, prefix_len, n, spin):
         "step_speedup": round(t["step_separate"] / min(t["step_mixed"], t["step_mixed_grouped"]), 3),
         "decode_roofline": {"bound": "hbm", "kernel": f"decode_group_kernel ({best_key})", "achieved": round(ach, 1),
                             "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4),
-                            "traffic": None,
-                            "note": "unique algorithmic bytes (each distinct cached token once + queries)"},
+                            **(_traffic_fields("mixed", unique) if best_key == MIXED_COUNTED_VARIANT and
+                               prefix_len == 2048 else {"traffic": None}),
+                            "note": "unique algorithmic bytes (each distinct cached token once + queries); "
+                                    "traffic: the grouped kernel's launch, its reduce not counted"},
         "decode_plain_unique_frac": round(unique / (t["decode"] * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
         "decode_logical_gbs": {"plain": round(logical / (t["decode"] * 1e-6) / 1e9, 1),
                                "grouped": round(logical / (best_dec * 1e-6) / 1e9, 1)},
         "prefill_roofline": {"bound": "mfma", "kernel": "prefill_mfma_kernel", "achieved": round(pre_tf, 2),
                              "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(pre_tf / PEAK_BF16_TFLOPS, 4),
-                             "traffic": None},
+                             **_traffic_fields("prefill", _prefill_bytes(mw.ctx_start, mw.chunk, mw.Hq, mw.Hkv,
+                                                                         mw.D, False))},
         "replicas": R,
     }
 
@@ -749,12 +901,15 @@ def cpu_baseline_mixed(seconds: float):
                        f"({pre_s:.2f} s); numpy fp64")}
 
 
-def measure_mixed(args, dev):
+def measure_mixed(args, dev, counted=False):
     """The mixed prefix-sharing step (a 2,048-token shared prefix), and its copy-on-write variant
-    (2,040 tokens: the partial last prefix block is copied for 15 of the 16 samples)."""
+    (2,040 tokens: the partial last prefix block is copied for 15 of the 16 samples).  counted:
+    the counter run of the decode variant the traffic record covers."""
     import torch
 
     stream = torch.cuda.current_stream()
+    if counted:
+        return _mixed_case(args, dev, 2048, max(5, args.steps), 0, counted=True)
     spin = int(_spin_cycles_per_ms(torch, stream) * 50)
     n = max(20, args.steps // 4)
     res = _mixed_case(args, dev, 2048, n, spin)
@@ -766,6 +921,103 @@ def measure_mixed(args, dev):
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_mixed(args.cpu_seconds / 2)
     return res
+
+
+def measure_tiny(args, dev):
+    """The tiny fp32 step: batch 4, 8 q = 8 kv heads of 64, a 32-block pool handed out from a seeded
+    permutation, lengths {5, 17, 32, 40}; one paged_cache_append of the step's 4 tokens plus one
+    paged_attention_decode (fp32 caches have no fused append).  Device time of n back-to-back steps
+    behind a spin; the step moves 0.4 MB, so launch latency, not HBM, sets its time."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_404_amd import BlockPool, ops
+
+    w = wl.tiny_decode(1)
+    pool = BlockPool(w.num_blocks, 16, w.free_order)
+    seqs = [pool.new_seq() for _ in range(w.B)]
+    st, _, _, _ = pool.append_many(seqs, [int(L) - 1 for L in w.lens])
+    st2, _, step_slots, _ = pool.append_many(seqs, [1] * w.B)
+    assert st == 0 and st2 == 0
+    tables, lens = pool.block_tables(seqs, w.max_blocks_per_seq)
+    g = torch.Generator(device=dev)
+    g.manual_seed(w.seed)
+    f32 = torch.float32
+    k = torch.randn((w.num_blocks, w.Hkv, 16 * w.D), generator=g, device=dev, dtype=f32)
+    v = torch.randn((w.num_blocks, w.Hkv, 16 * w.D), generator=g, device=dev, dtype=f32)
+    q = torch.randn((w.B, w.Hq, w.D), generator=g, device=dev, dtype=f32)
+    sk = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev, dtype=f32)
+    sv = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev, dtype=f32)
+    out = torch.empty((w.B, w.Hq, w.D), dtype=f32, device=dev)
+    app = ops.PreparedAppend(k, v, sk, sv, torch.from_numpy(step_slots).to(dev))
+    dec = ops.PreparedDecode(out, q, k, v, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev),
+                             int(lens.max()), w.scale, 0, None, host_context_lens=lens)
+    for _ in range(5):
+        app()
+        dec()
+    stream = torch.cuda.current_stream()
+    n = max(50, args.steps)
+    spin = int(_spin_cycles_per_ms(torch, stream) * 20)
+    step_us = _spun_avg_us(torch, stream, lambda i: (app(), dec()), n, spin)
+    dec_us = _spun_avg_us(torch, stream, lambda i: dec(), n, spin)
+    nbytes = w.kv_bytes() + w.q_bytes()
+    gbs = nbytes / (dec_us * 1e-6) / 1e9
+    res = {
+        "workload": w.name,
+        "kv_plus_q_bytes_per_step": nbytes,
+        "us_per_step": round(step_us, 3),
+        "seqs_steps_per_s": round(w.B / (step_us * 1e-6), 1),
+        "kernel_us": {"decode": round(dec_us, 3), "append": round(step_us - dec_us, 3)},
+        "step": "paged_cache_append + paged_attention_decode (fp32, single pass, vector-ALU decode)",
+        "roofline": {"bound": "hbm", "kernel": "decode_valu_kernel", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 6), **_traffic_fields("tiny", nbytes),
+                     "note": "latency-bound: 32 workgroups move 0.4 MB"},
+        "timing": f"{n} back-to-back steps behind a 20 ms spin, one HIP event pair (device time only)",
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_tiny(w, args.cpu_seconds / 4)
+    return res
+
+
+def cpu_baseline_tiny(w, seconds):
+    """The oracle on the whole tiny step: the 4 new tokens written into its cache model, then the
+    fp64 decode of the 4 sequences, repeated for about `seconds`."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import workloads as wl
+    from oracle import CacheModel, PoolModel
+    from oracle import attention as oatt
+
+    rng = np.random.default_rng(1001)
+    pool = PoolModel(w.num_blocks, 16, w.free_order)
+    seqs = [pool.new_seq() for _ in range(w.B)]
+    cache = CacheModel(w.num_blocks, w.Hkv, w.D, w.dtype, fill_nan=True)
+    for s, L in zip(seqs, w.lens):
+        slots, _ = pool.append(s, int(L) - 1)
+        cache.append(wl.normal_bits(rng, (int(L) - 1, w.Hkv, w.D), "f32"),
+                     wl.normal_bits(rng, (int(L) - 1, w.Hkv, w.D), "f32"), slots)
+    step_slots = []
+    for s in seqs:
+        sl, _ = pool.append(s, 1)
+        step_slots += sl
+    tables, lens = pool.block_tables(seqs, w.max_blocks_per_seq)
+    q = wl.normal_bits(rng, (w.B, w.Hq, w.D), "f32")
+    nk, nv = wl.normal_bits(rng, (w.B, w.Hkv, w.D), "f32"), wl.normal_bits(rng, (w.B, w.Hkv, w.D), "f32")
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        cache.append(nk, nv, step_slots)
+        oatt.paged_decode(q, cache, tables, lens, w.scale)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds and reps >= 3:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    per = el / reps
+    return {"value": round((w.kv_bytes() + w.q_bytes()) / per / 1e9, 5), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle", "us_per_step": round(per * 1e6, 1), "seqs_steps_per_s": round(w.B / per, 1),
+            "sample": f"the whole step (append + decode of all 4 sequences), {reps} steps in {el:.1f} s"}
 
 
 def measure_long(args, dev):
@@ -813,7 +1065,7 @@ def measure_long(args, dev):
         "kernel_us": {"decode_partitions": round(part_us, 3), "decode_reduce": round(step_us - part_us, 3)},
         "roofline": {"bound": "hbm", "kernel": "decode_mfma_kernel (partition pass, fused append)",
                      "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), **_traffic_fields("long", nbytes)},
     }
 
 
@@ -929,7 +1181,7 @@ def measure_read_probe(dev, step_bytes: int) -> dict:
 def main():
     args = parse()
     if args.traffic_from:
-        print(json.dumps(write_traffic(args.workload, *args.traffic_from)))
+        print(json.dumps(write_traffic(*args.traffic_from)))
         return
     if args.cpu_baseline_only:
         import workloads as wl
@@ -951,6 +1203,19 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.only:
+        args.no_cpu_baseline = True
+        if args.only == "llama":
+            args.no_extra = True
+            args.workload = "llama"
+        else:
+            res = {"long": lambda: measure_long(args, dev), "tiny": lambda: measure_tiny(args, dev),
+                   "prefill": lambda: measure_prefill(args, dev), "prefill_fp8": lambda: measure_prefill(args, dev, True),
+                   "fp8": lambda: measure_fp8(args, dev, None), "mixed": lambda: measure_mixed(args, dev, counted=True),
+                   "trace": lambda: measure_trace(dev, counters=True)}[args.only]()
+            calibration_copy(dev)
+            print(json.dumps(res), flush=True)
+            return
     if args.workload == "llama":
         w = wl.llama_decode(2, partition_size=0 if args.partition_size is None else args.partition_size)
     else:
@@ -1158,6 +1423,8 @@ def main():
     if not args.no_extra and args.workload == "llama":
         del reps
         torch.cuda.empty_cache()
+        if "tiny" in extras:
+            res["tiny"] = measure_tiny(args, dev)
         if "prefill" in extras:
             res["prefill"] = measure_prefill(args, dev)
         if "prefill_fp8" in extras:
