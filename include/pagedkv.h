@@ -292,8 +292,8 @@ int paged_attention_decode_reduce(void* out, int32_t out_dtype, const int32_t* c
  *   new_key, new_value device [B][num_kv_heads][head_dim] of `dtype`, 16-byte aligned.
  *   k_cache, v_cache   device, written at the B new slots only.
  *   Other arguments as paged_attention_decode.  The slots must be private to their sequences
- *   (copy-on-write copies done first) and distinct.  bf16 / fp16 only: PKV_EUNSUPPORTED for
- *   PKV_F32.
+ *   (copy-on-write copies done first) and distinct.  Every dtype: bf16 / fp16 in the matrix-core
+ *   kernel, fp32 in the vector-ALU kernel (which also copies the rows into the slots).
  */
 int paged_attention_decode_append(void* out, int32_t out_dtype, const void* query, const void* new_key,
                                   const void* new_value, void* k_cache, void* v_cache, const int32_t* block_tables,
@@ -318,7 +318,7 @@ int paged_attention_decode_append_partitions(void* out, int32_t out_dtype, const
  * cache is not written.  The caller stores those tokens with paged_cache_append, before, after,
  * or concurrently on another stream: this call never depends on the bytes of those slots, so the
  * append can overlap the attention.  Output bit for bit that of paged_attention_decode_append.
- * Arguments as paged_attention_decode_append (k_cache, v_cache read only).  bf16 / fp16 only.
+ * Arguments as paged_attention_decode_append (k_cache, v_cache read only).  Every dtype.
  */
 int paged_attention_decode_newest(void* out, int32_t out_dtype, const void* query, const void* new_key,
                                   const void* new_value, const void* k_cache, const void* v_cache,

@@ -56,6 +56,11 @@ __device__ __forceinline__ float wave_sum(float x) {
 // ------------------------------------------------------------------------------------------
 // Vector-ALU kernel (any element type; used for fp32).  grid = (Hq, B, max_parts), one wave.
 // Lane i scores token c0 + i of each 64-token chunk; each lane owns dims lane and lane + 64.
+//
+// Fused append (new_k set): token L - 1 takes its K/V from the input rows new_k / new_v in every
+// workgroup that sees it, so no workgroup reads its cache slot; the workgroup of the KV head's
+// first query head that owns the token's partition also copies the rows into the slot (when
+// k_out is set), element for element, so the cache ends as an append would leave it.
 // ------------------------------------------------------------------------------------------
 template <int DT, int DT_OUT, int D>
 __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
@@ -78,6 +83,18 @@ __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
     qs[d] = elem_to_float<DT>(a.q, (static_cast<int64_t>(b) * a.Hq + hq) * D + d) * a.scale_log2;
   __syncthreads();
 
+  const bool fused = a.new_k != nullptr;
+  const int tn = L - 1;                                    // the new token (fused append)
+  const int64_t nrow = (static_cast<int64_t>(b) * a.Hkv + g) * D;  // its input rows
+  if (fused && a.k_out != nullptr && hq % G == 0 && tn >= pstart && tn < pend) {
+    const int64_t tile = (static_cast<int64_t>(clamp_blk(a, table[tn / kBlock])) * a.Hkv + g) * kBlock * D;
+    const int off = tn % kBlock;
+    for (int d = lane; d < D; d += 64) {
+      copy_elem<DT>(a.k_out, tile + static_cast<int64_t>(k_chunk_pos(off, d / E)) * E + d % E, a.new_k, nrow + d);
+      copy_elem<DT>(a.v_out, tile + static_cast<int64_t>((off >> 3) * D + d) * 8 + (off & 7), a.new_v, nrow + d);
+    }
+  }
+
   constexpr int DPL = (D + 63) / 64;  // dims per lane
   float o[DPL];
 #pragma unroll
@@ -94,8 +111,12 @@ __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
       tile = (static_cast<int64_t>(clamp_blk(a, table[t / kBlock])) * a.Hkv + g) * kBlock * D;
       off = t % kBlock;
       float acc = 0.f;
-      for (int d = 0; d < D; ++d)
-        acc += qs[d] * elem_to_float<DT>(a.k, tile + static_cast<int64_t>(k_chunk_pos(off, d / E)) * E + d % E);
+      if (fused && t == tn) {
+        for (int d = 0; d < D; ++d) acc += qs[d] * elem_to_float<DT>(a.new_k, nrow + d);
+      } else {
+        for (int d = 0; d < D; ++d)
+          acc += qs[d] * elem_to_float<DT>(a.k, tile + static_cast<int64_t>(k_chunk_pos(off, d / E)) * E + d % E);
+      }
       s = acc;
     }
     const float m_new = fmaxf(m_run, wave_max(s));
@@ -109,10 +130,13 @@ __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
       const float pi = __shfl(pt, i);
       const int64_t ti = __shfl(tile, i);
       const int oi = __shfl(off, i);
+      const bool inew = fused && c0 + i == tn;
 #pragma unroll
       for (int k = 0; k < DPL; ++k) {
         const int d = lane + 64 * k;
-        if (d < D) o[k] += pi * elem_to_float<DT>(a.v, ti + static_cast<int64_t>((oi >> 3) * D + d) * 8 + (oi & 7));
+        if (d < D)
+          o[k] += pi * (inew ? elem_to_float<DT>(a.new_v, nrow + d)
+                             : elem_to_float<DT>(a.v, ti + static_cast<int64_t>((oi >> 3) * D + d) * 8 + (oi & 7)));
       }
     }
     m_run = m_new;
@@ -316,7 +340,6 @@ int partitions_impl(const char* fn, void* out, int32_t out_dtype, const void* qu
                     max_blocks, num_blocks, max_ctx, partition_size, workspace, workspace_bytes, dtype);
   if (st != PKV_OK || B == 0 || max_ctx == 0) return st;
   if (new_k != nullptr || new_v != nullptr) {
-    if (dtype == PKV_F32) return fail(PKV_EUNSUPPORTED, "%s: fused append needs bf16 or fp16 caches", fn);
     if (!new_k || !new_v) return fail(PKV_EINVAL, "%s: NULL new_key or new_value", fn);
     if ((reinterpret_cast<uintptr_t>(new_k) | reinterpret_cast<uintptr_t>(new_v)) % 16 != 0)
       return fail(PKV_EINVAL, "%s: new_key and new_value must be 16-byte aligned", fn);

@@ -42,6 +42,16 @@ __device__ __forceinline__ float f16_bits_to_float(uint32_t bits16) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
 
+// Copy one element of type DT, bit for bit: dst[di] = src[si].
+template <int DT>
+__device__ __forceinline__ void copy_elem(void* dst, int64_t di, const void* src, int64_t si) {
+  if constexpr (DT == PKV_F32) {
+    static_cast<uint32_t*>(dst)[di] = static_cast<const uint32_t*>(src)[si];
+  } else {
+    static_cast<uint16_t*>(dst)[di] = static_cast<const uint16_t*>(src)[si];
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ float elem_to_float(const void* base, int64_t i) {
   if constexpr (DT == PKV_F32) {
