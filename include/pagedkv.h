@@ -494,6 +494,30 @@ int paged_attention_prefill_chunk_fp8(void* out, int32_t out_dtype, const void* 
                                       int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t num_blocks,
                                       float scale, int32_t q_dtype, pkv_stream_t stream);
 
+/*
+ * paged_attention_mixed_fp8 - paged_attention_mixed over an fp8 cache: one launch for a step's
+ * decode rows (paged_attention_decode_fp8) and up to 16 prefill chunks
+ * (paged_attention_prefill_chunk_fp8); outputs are bit for bit theirs.  [Chapter] "How the
+ * scheduler works" and [Notes] "Prefill gets in the way" (decodes and a prompt chunk in one step),
+ * over the quantised cache of [Notes] "Memory, not compute, caps the batch".  Arguments as
+ * paged_attention_mixed, except: no grouped decode (one sequence per decode workgroup); the
+ * caches and k_scale / v_scale are the fp8 layouts above; q_dtype (PKV_BF16 or PKV_F16) is the type
+ * of both queries, out_dtype PKV_F32 or q_dtype; the decode part follows paged_attention_decode_fp8's
+ * rules (partition_size 0, -1 or a multiple of 16, workspace from
+ * paged_attention_decode_workspace_bytes, longest-first order from host_dec_context_lens).  With
+ * split-K partitions the log-sum-exp merge is enqueued after the launch.
+ */
+int paged_attention_mixed_fp8(void* dec_out, const void* dec_query, const int32_t* dec_block_tables,
+                              const int32_t* dec_context_lens, int32_t B_dec, int32_t dec_max_blocks,
+                              int32_t dec_max_context_len, const int32_t* host_dec_context_lens,
+                              int32_t dec_partition_size, void* workspace, size_t workspace_bytes, void* pre_out,
+                              const void* pre_query, const int32_t* pre_block_tables, int32_t pre_max_blocks,
+                              const int32_t* host_ctx_starts, const int32_t* host_chunk_lens, int32_t num_chunks,
+                              int32_t out_dtype, const void* k_cache, const void* v_cache, const void* k_scale,
+                              const void* v_scale, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t block_size, int32_t num_blocks, float scale, int32_t q_dtype,
+                              pkv_stream_t stream);
+
 /* ============================== host block pool ============================== */
 /*
  * [Serving] Step 4: a pool of physical block ids with a free list; allocation takes the id at the

@@ -82,6 +82,9 @@ _SIGS = {
     "paged_attention_mixed": (C.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _i32, _vp, _sz, _vp, _vp, _vp,
                                         _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _i32,
                                         _vp]),
+    "paged_attention_mixed_fp8": (C.c_int, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _i32, _vp, _sz, _vp, _vp,
+                                            _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                            _i32, _i32, _f32, _i32, _vp]),
     "paged_cache_append_fp8": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _i32, _i32, _i32, _i32,
                                          _i32, _i32, _vp]),
     "paged_cache_copy_blocks_fp8": (C.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),

@@ -17,8 +17,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpagedkv.so")
 
-HIP_SOURCES = ["append.hip", "check.hip", "decode.hip", "decode_group.hip", "fp8.hip", "mixed.hip", "prefill.hip",
-               "prefill_fp8.hip", "probe.hip"]
+HIP_SOURCES = ["append.hip", "check.hip", "decode.hip", "decode_group.hip", "fp8.hip", "mixed.hip", "mixed_fp8.hip",
+               "prefill.hip", "prefill_fp8.hip", "probe.hip"]
 HOST_SOURCES = ["pool.cpp", "status.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

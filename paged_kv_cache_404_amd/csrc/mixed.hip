@@ -18,39 +18,18 @@
 
 #include "decode_group.h"
 #include "decode_host.h"
-#include "prefill_tile.h"
+#include "mixed_host.h"
 
 namespace pkv {
 namespace {
-
-constexpr int kMaxChunks = 16;
-
-struct ChunkDesc {
-  void* out;
-  const void* q;
-  const int32_t* table;
-  int32_t ctx_start;
-  int32_t C;
-  int32_t row_tiles;
-  int32_t wg_base;  // first workgroup of this chunk (a multiple of 8)
-};
 
 struct MixedArgs {
   DecodeArgs dec;
   int32_t B_dec;
   int32_t dec_rows;  // decode rows of the grid: B_dec sequences, or ceil(B_dec / NS) groups
   int32_t n_dec_wg;  // Hkv * dec_rows * max_parts rounded up to a multiple of 8
-  int32_t n_chunks;
-  ChunkDesc chunks[kMaxChunks];
-  const void* k;
-  const void* v;
-  int32_t Hq;
-  int32_t Hkv;
-  int32_t num_blocks;
-  float scale_log2;
+  ChunkSet pre;
 };
-
-constexpr int smax(int a, int b) { return a > b ? a : b; }
 
 // NS: decode sequences per workgroup (1, or a grouped size); NWD: decode waves (4 or 8, the
 // decode kernel's rule for the partition size).  Every workgroup has 8 waves; a 4-wave decode
@@ -63,9 +42,9 @@ __global__ void __launch_bounds__(512) mixed_kernel(MixedArgs m) {
   __shared__ float smem[smax(kDec, kPre)];
   const int id = blockIdx.x;
   if (id < m.n_dec_wg) {
-    const int g = id % m.Hkv;
-    const int y = (id / m.Hkv) % m.dec_rows;
-    const int z = id / (m.Hkv * m.dec_rows);
+    const int g = id % m.pre.Hkv;
+    const int y = (id / m.pre.Hkv) % m.dec_rows;
+    const int z = id / (m.pre.Hkv * m.dec_rows);
     if (z >= m.dec.max_parts) return;  // padding up to a multiple of 8
     if (NWD < 8 && threadIdx.x >= NWD * 64) return;
     if constexpr (NS == 1)
@@ -74,27 +53,7 @@ __global__ void __launch_bounds__(512) mixed_kernel(MixedArgs m) {
       decode_group_part<DT, DT_OUT, D, G, NS, NWD>(m.dec, m.B_dec, g, y, z, smem);
     return;
   }
-  int c = 0;
-  while (c + 1 < m.n_chunks && id >= m.chunks[c + 1].wg_base) ++c;
-  const ChunkDesc& ch = m.chunks[c];
-  const int local = id - ch.wg_base;
-  if (local >= ch.row_tiles * m.Hkv) return;  // padding up to a multiple of 8
-  PrefillArgs pa;
-  pa.out = ch.out;
-  pa.q = ch.q;
-  pa.k = m.k;
-  pa.v = m.v;
-  pa.table = ch.table;
-  pa.ctx_start = ch.ctx_start;
-  pa.C = ch.C;
-  pa.Hq = m.Hq;
-  pa.Hkv = m.Hkv;
-  pa.num_blocks = m.num_blocks;
-  pa.row_tiles = ch.row_tiles;
-  pa.scale_log2 = m.scale_log2;
-  pa.ksc = nullptr;
-  pa.vsc = nullptr;
-  prefill_tile<DT, DT_OUT, D, G>(pa, local, smem);
+  mixed_prefill_role<DT, DT_OUT, D, G, false>(m.pre, id, smem);
 }
 
 template <int DT, int DT_OUT, int D, int G, int NS>
@@ -119,7 +78,7 @@ void launch_ns(const MixedArgs& m, int ns, int nwd, int grid, hipStream_t s) {
 
 template <int DT, int DT_OUT, int D>
 void launch_g(const MixedArgs& m, int ns, int nwd, int grid, hipStream_t s) {
-  switch (m.Hq / m.Hkv) {
+  switch (m.pre.Hq / m.pre.Hkv) {
     case 1: launch_ns<DT, DT_OUT, D, 1>(m, ns, nwd, grid, s); break;
     case 2: launch_ns<DT, DT_OUT, D, 2>(m, ns, nwd, grid, s); break;
     case 4: launch_ns<DT, DT_OUT, D, 4>(m, ns, nwd, grid, s); break;
@@ -183,12 +142,12 @@ extern "C" int paged_attention_mixed(void* dec_out, const void* dec_query, const
        reinterpret_cast<uintptr_t>(v_cache)) % 16 != 0)
     return fail(PKV_EINVAL, "%s: queries and caches must be 16-byte aligned", fn);
   MixedArgs m{};
-  m.k = k_cache;
-  m.v = v_cache;
-  m.Hq = num_q_heads;
-  m.Hkv = num_kv_heads;
-  m.num_blocks = num_blocks;
-  m.scale_log2 = scale * kLog2e;
+  m.pre.k = k_cache;
+  m.pre.v = v_cache;
+  m.pre.Hq = num_q_heads;
+  m.pre.Hkv = num_kv_heads;
+  m.pre.num_blocks = num_blocks;
+  m.pre.scale_log2 = scale * kLog2e;
   const Plan pl = make_plan(has_dec ? B_dec : 1, num_q_heads, head_dim, has_dec ? dec_max_context_len : 1,
                             dec_partition_size);
   const int nwd = decode_waves(dec_partition_size, pl);
@@ -214,31 +173,9 @@ extern "C" int paged_attention_mixed(void* dec_out, const void* dec_query, const
   int64_t wg = has_dec ? (static_cast<int64_t>(num_kv_heads) * m.dec_rows * pl.max_parts + 7) / 8 * 8 : 0;
   m.n_dec_wg = static_cast<int32_t>(wg);
   // prefill chunks, rows packed one after another in pre_query / pre_out
-  const int64_t row_elems = static_cast<int64_t>(num_q_heads) * head_dim;
-  const int es = elem_size(dtype);
-  const int oes = elem_size(out_dtype);
-  int64_t row0 = 0;
-  int n = 0;
-  for (int i = 0; i < num_chunks; ++i) {
-    const int32_t cs = host_ctx_starts[i], C = host_chunk_lens[i];
-    if (cs < 0 || C < 0) return fail(PKV_EINVAL, "%s: chunk %d has a negative start or length", fn, i);
-    if (static_cast<int64_t>(cs) + C > static_cast<int64_t>(pre_max_blocks) * kBlock)
-      return fail(PKV_EINVAL, "%s: chunk %d extends past pre_max_blocks * block_size", fn, i);
-    if (C > 0) {
-      ChunkDesc& d = m.chunks[n++];
-      d.out = static_cast<uint8_t*>(pre_out) + row0 * row_elems * oes;
-      d.q = static_cast<const uint8_t*>(pre_query) + row0 * row_elems * es;
-      d.table = pre_block_tables + static_cast<int64_t>(i) * pre_max_blocks;
-      d.ctx_start = cs;
-      d.C = C;
-      d.row_tiles = (C + 15) / 16;
-      d.wg_base = static_cast<int32_t>(wg);
-      wg += (static_cast<int64_t>(d.row_tiles) * num_kv_heads + 7) / 8 * 8;
-    }
-    row0 += C;
-  }
-  m.n_chunks = n;
-  if (wg > INT32_MAX) return fail(PKV_EINVAL, "%s: too much work for one launch", fn);
+  const int pst = pack_chunks(fn, m.pre, wg, pre_out, pre_query, pre_block_tables, pre_max_blocks, host_ctx_starts,
+                              host_chunk_lens, num_chunks, head_dim, elem_size(dtype), elem_size(out_dtype));
+  if (pst != PKV_OK) return pst;
   if (wg == 0) return PKV_OK;
   hipStream_t s = as_stream(stream);
   const bool f32out = out_dtype == PKV_F32;

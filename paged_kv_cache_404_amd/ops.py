@@ -537,14 +537,30 @@ class PreparedAppendFp8:
 
 def _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, pre_out, pre_query, pre_tables,
                 ctx_starts, chunk_lens, k_cache, v_cache, scale, host_dec_lens, dec_partition_size=0, dec_group_size=1,
-                workspace=None):
+                workspace=None, k_scale=None, v_scale=None):
     """Every shape and dtype is checked before the tensors' device (so a mismatch is reported as
-    such), and all of it before the launch."""
-    N, Hkv, D = cache_dims(k_cache, v_cache)
-    bs = 16
-    if v_cache.dtype != k_cache.dtype:
-        raise TypeError("k_cache and v_cache must share one dtype")
-    dtype = dtype_code(k_cache.dtype)
+    such), and all of it before the launch.  With k_scale / v_scale: the fp8 cache and the argument
+    order of paged_attention_mixed_fp8 (queries bf16 or fp16)."""
+    fp8 = k_scale is not None or v_scale is not None
+    if fp8:
+        if k_scale is None or v_scale is None:
+            raise ValueError("an fp8 cache needs both k_scale and v_scale")
+        if dec_group_size != 1:
+            raise ValueError("the fp8 mixed launch has no grouped decode")
+        N, Hkv, bs, D = _fp8_shapes(k_cache, v_cache, k_scale, v_scale)
+        qs = [t for t in (dec_query, pre_query) if t is not None and t.numel()]
+        qdt = qs[0].dtype if qs else torch.bfloat16
+        if qdt not in (torch.bfloat16, torch.float16) or any(t.dtype != qdt for t in qs):
+            raise TypeError("fp8 mixed queries must share one dtype, bf16 or fp16")
+        dtype = dtype_code(qdt)
+        cache_dt = qdt  # the dtype the query checks below compare against
+    else:
+        N, Hkv, D = cache_dims(k_cache, v_cache)
+        bs = 16
+        if v_cache.dtype != k_cache.dtype:
+            raise TypeError("k_cache and v_cache must share one dtype")
+        dtype = dtype_code(k_cache.dtype)
+        cache_dt = k_cache.dtype
     B = 0 if dec_query is None else dec_query.shape[0]
     S = len(chunk_lens)
     Hq = out_dtype = None
@@ -553,7 +569,7 @@ def _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, p
             raise ValueError("dec_query must be [B][Hq][head_dim]")
         if tuple(dec_out.shape) != tuple(dec_query.shape):
             raise ValueError("dec_out must have dec_query's shape [B][Hq][D]")
-        if dec_query.dtype != k_cache.dtype:
+        if dec_query.dtype != cache_dt:
             raise TypeError("dec_query must have the cache dtype")
         if dec_tables.dtype != torch.int32 or dec_lens.dtype != torch.int32:
             raise TypeError("decode tables and lens must be int32")
@@ -564,7 +580,7 @@ def _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, p
     if S:
         if pre_query.dim() != 3 or pre_query.shape[2] != D:
             raise ValueError("pre_query must be [rows][Hq][head_dim]")
-        if pre_query.dtype != k_cache.dtype:
+        if pre_query.dtype != cache_dt:
             raise TypeError("pre_query must have the cache dtype")
         if pre_tables.dtype != torch.int32 or pre_tables.dim() != 2 or pre_tables.shape[0] != S:
             raise ValueError("prefill tables must be int32 [num_chunks][max_blocks]")
@@ -582,7 +598,7 @@ def _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, p
     lens = np.ascontiguousarray(np.asarray(chunk_lens, dtype=np.int32))
     if len(starts) != S:
         raise ValueError("ctx_starts and chunk_lens must have one entry per chunk")
-    _dev(k_cache, v_cache, *((dec_out, dec_query, dec_tables, dec_lens) if B else ()),
+    _dev(k_cache, v_cache, *((k_scale, v_scale) if fp8 else ()), *((dec_out, dec_query, dec_tables, dec_lens) if B else ()),
          *((pre_out, pre_query, pre_tables) if S else ()))
     hl, hp = _host_lens_ptr(host_dec_lens)
     keep = (starts, lens, hl)
@@ -590,14 +606,18 @@ def _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, p
         _dev(workspace)
     ws_ptr, ws_bytes = (None, 0) if workspace is None else (workspace.data_ptr(),
                                                             workspace.numel() * workspace.element_size())
-    args = (dec_out.data_ptr() if B else None, dec_query.data_ptr() if B else None,
-            dec_tables.data_ptr() if B else None, dec_lens.data_ptr() if B else None, B,
-            dec_tables.shape[1] if B else 0, int(dec_max_context_len) if B else 0, hp,
-            int(dec_partition_size), int(dec_group_size), ws_ptr, ws_bytes,
-            pre_out.data_ptr() if S else None, pre_query.data_ptr() if S else None,
-            pre_tables.data_ptr() if S else None, pre_tables.shape[1] if S else 0,
-            starts.ctypes.data if S else None, lens.ctypes.data if S else None, S, dtype_code(out_dtype),
-            k_cache.data_ptr(), v_cache.data_ptr(), Hq, Hkv, D, bs, N, float(scale), dtype)
+    dec = (dec_out.data_ptr() if B else None, dec_query.data_ptr() if B else None,
+           dec_tables.data_ptr() if B else None, dec_lens.data_ptr() if B else None, B,
+           dec_tables.shape[1] if B else 0, int(dec_max_context_len) if B else 0, hp, int(dec_partition_size))
+    pre = (pre_out.data_ptr() if S else None, pre_query.data_ptr() if S else None,
+           pre_tables.data_ptr() if S else None, pre_tables.shape[1] if S else 0,
+           starts.ctypes.data if S else None, lens.ctypes.data if S else None, S, dtype_code(out_dtype))
+    if fp8:
+        args = dec + (ws_ptr, ws_bytes) + pre + (k_cache.data_ptr(), v_cache.data_ptr(), k_scale.data_ptr(),
+                                                 v_scale.data_ptr(), Hq, Hkv, D, bs, N, float(scale), dtype)
+    else:
+        args = dec + (int(dec_group_size), ws_ptr, ws_bytes) + pre + (k_cache.data_ptr(), v_cache.data_ptr(), Hq, Hkv,
+                                                                      D, bs, N, float(scale), dtype)
     return args, keep
 
 
@@ -614,6 +634,19 @@ def paged_attention_mixed(dec_out, dec_query, dec_tables, dec_lens, dec_max_cont
         return
     args, keep = r
     check(lib.paged_attention_mixed(*args, _stream(stream)))
+
+
+def paged_attention_mixed_fp8(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, pre_out, pre_query,
+                              pre_tables, ctx_starts, chunk_lens, k_cache, v_cache, k_scale, v_scale, scale,
+                              stream=None, host_dec_lens=None, dec_partition_size=0, workspace=None) -> None:
+    """paged_attention_mixed over an fp8 cache (codes + per-slot scales); bf16/fp16 queries."""
+    r = _mixed_args(dec_out, dec_query, dec_tables, dec_lens, dec_max_context_len, pre_out, pre_query, pre_tables,
+                    ctx_starts, chunk_lens, k_cache, v_cache, scale, host_dec_lens, dec_partition_size, 1,
+                    workspace, k_scale, v_scale)
+    if r is None:
+        return
+    args, keep = r
+    check(lib.paged_attention_mixed_fp8(*args, _stream(stream)))
 
 
 class PreparedMixed:

@@ -352,3 +352,77 @@ def test_prefill_fp8_rejects():
         ops.paged_attention_prefill_chunk_fp8(out, q, k, v, ks, vs, tab, 0, -0.1)  # scale
     with pytest.raises(Exception):
         ops.paged_attention_prefill_chunk_fp8(out, q, k, v, ks, vs, tab, 62, 0.1)  # past the pool
+
+
+MIXED = [
+    # seed, decode lengths, chunks (ctx_start, length), Hq, Hkv, D, query dtype, partition size
+    (1, [1, 17, 300, 2048, 513, 64], [(0, 37), (100, 16), (640, 130)], 32, 8, 128, "bf16", 0),
+    (2, [5, 900, 1200], [(33, 1)], 32, 8, 128, "bf16", 512),
+    (3, [], [(0, 20), (48, 64)], 32, 8, 128, "bf16", 0),
+    (4, [1000, 2, 700], [], 32, 8, 128, "bf16", 256),
+    (5, [40, 129, 1500], [(16, 48), (0, 5)], 64, 8, 64, "f16", 0),
+    (6, [77, 31], [(250, 130)], 16, 4, 64, "bf16", 64),
+    (7, [30, 600, 1, 250], [(0, 16), (300, 70)], 16, 8, 128, "bf16", 1024),
+    (8, [130, 7, 1025], [(17, 40), (0, 33)], 8, 8, 128, "f16", 0),
+]
+
+
+@pytest.mark.parametrize("seed,dec_lens,chunks,Hq,Hkv,D,qd,ps", MIXED)
+def test_mixed_fp8_equals_separate_launches(seed, dec_lens, chunks, Hq, Hkv, D, qd, ps):
+    """paged_attention_mixed_fp8: decode rows and prefill chunks over the fp8 cache in one launch
+    (+ the split-K merge), bit for bit paged_attention_decode_fp8 and
+    paged_attention_prefill_chunk_fp8, and within 2e-3 of the oracle over code * scale."""
+    counts = list(dec_lens) + [c + n for c, n in chunks]
+    m, seqs, rng = _build(counts, Hkv, D, 900 + seed, in_dtype=qd)
+    dseqs, pseqs = seqs[:len(dec_lens)], seqs[len(dec_lens):]
+    B, S = len(dseqs), len(pseqs)
+    q_dec = wl.normal_bits(rng, (B, Hq, D), qd)
+    q_pre = wl.normal_bits(rng, (sum(n for _, n in chunks), Hq, D), qd)
+    R = q_pre.shape[0]
+    scale = 1 / np.sqrt(D)
+    dtab, dlens = m.tables(dseqs) if B else (None, None)
+    ptab, _ = m.tables(pseqs) if S else (None, None)
+    mcl = int(dlens.max()) if B else 0
+    ws = ops.decode_workspace(B, Hq, D, mcl, ps) if (B and ps > 0) else None
+    dec_sep = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    pre_sep = torch.full((R, Hq, D), float("nan"), dtype=torch.float32, device="cuda")
+    if B:
+        ops.paged_attention_decode_fp8(dec_sep, to_dev(q_dec, qd), m.k, m.v, m.ks, m.vs, i32(dtab), i32(dlens), mcl,
+                                       scale, ps, ws, host_context_lens=dlens)
+    r0 = 0
+    for i, (c, n) in enumerate(chunks):
+        ops.paged_attention_prefill_chunk_fp8(pre_sep[r0:r0 + n], to_dev(q_pre[r0:r0 + n], qd), m.k, m.v, m.ks, m.vs,
+                                              i32(ptab[i]), c, scale)
+        r0 += n
+    dec_mix = torch.full_like(dec_sep, float("nan"))
+    pre_mix = torch.full_like(pre_sep, float("nan"))
+    ws2 = torch.full_like(ws, 0xFF) if ws is not None else None  # NaN partials until written
+    ops.paged_attention_mixed_fp8(dec_mix if B else None, to_dev(q_dec, qd) if B else None, i32(dtab) if B else None,
+                                  i32(dlens) if B else None, mcl, pre_mix if S else None,
+                                  to_dev(q_pre, qd) if S else None, i32(ptab) if S else None,
+                                  [c for c, _ in chunks], [n for _, n in chunks], m.k, m.v, m.ks, m.vs, scale,
+                                  host_dec_lens=dlens if (B and seed % 2) else None, dec_partition_size=ps,
+                                  workspace=ws2)
+    torch.cuda.synchronize()
+    assert torch.equal(dec_mix.view(torch.int32), dec_sep.view(torch.int32))
+    assert torch.equal(pre_mix.view(torch.int32), pre_sep.view(torch.int32))
+    if B:
+        ref = oatt.paged_decode(q_dec, m.cache, dtab, dlens, scale, q_dtype=qd)
+        assert float(np.abs(dec_mix.cpu().numpy().astype(np.float64) - ref).max()) <= ATOL
+    r0 = 0
+    for i, (c, n) in enumerate(chunks):
+        ref = oatt.prefill_chunk(q_pre[r0:r0 + n], m.cache, ptab[i], c, scale, q_dtype=qd)
+        assert float(np.abs(pre_mix[r0:r0 + n].cpu().numpy().astype(np.float64) - ref).max()) <= ATOL
+        r0 += n
+
+
+def test_mixed_fp8_binding_rejects():
+    k, v, ks, vs = ops.fp8_cache(8, 2, 64)
+    q = torch.zeros((2, 4, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros((2, 4, 64), dtype=torch.float32, device="cuda")
+    tab = torch.zeros((2, 4), dtype=torch.int32, device="cuda")
+    lens = torch.ones(2, dtype=torch.int32, device="cuda")
+    with pytest.raises(TypeError):  # queries of two types
+        ops.paged_attention_mixed_fp8(out, q, tab, lens, 1, out, q.half(), tab, [0, 0], [1, 1], k, v, ks, vs, 0.1)
+    with pytest.raises(Exception):  # non-positive scale, refused by the library
+        ops.paged_attention_mixed_fp8(out, q, tab, lens, 1, None, None, None, [], [], k, v, ks, vs, 0.0)
