@@ -901,6 +901,82 @@ def cpu_baseline_mixed(seconds: float):
                        f"({pre_s:.2f} s); numpy fp64")}
 
 
+def _mixed_fp8_case(args, dev, n, spin):
+    """The prefix-sharing step's attention over an FP8 cache (the same scene: 16 samples on a
+    2,048-token prefix, a 512-row chunk after 4,096 tokens, every slot of the pool filled by the
+    quantising append, bf16 queries): the FP8 decode and FP8 prefill as separate launches against
+    one paged_attention_mixed_fp8 launch, single pass and with 512-token partitions."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    from paged_kv_cache_404_amd import BlockPool, ops
+
+    mw = wl.mixed_step(5, prefix_len=2048)
+    pool = BlockPool(mw.num_blocks, 16, mw.free_order)
+    s0 = pool.new_seq()
+    pool.append(s0, mw.prefix_len)
+    samples = [s0] + [pool.fork(s0) for _ in range(mw.samples - 1)]
+    pf = pool.new_seq()
+    pool.append(pf, mw.ctx_start)
+    st, _, _, _ = pool.append_many(samples + [pf], [1] * mw.samples + [mw.chunk])
+    assert st == 0
+    dtab, dlens = pool.block_tables(samples, wl.blocks_for(mw.prefix_len + 1))
+    ptab, _ = pool.block_tables([pf], wl.blocks_for(mw.ctx_start + mw.chunk))
+    dt_t, dl_t, pt_t = (torch.from_numpy(x).to(dev) for x in (dtab, dlens, ptab))
+    mcl = int(dlens.max())
+    T = mw.num_blocks * 16
+    all_slots = torch.arange(T, dtype=torch.int32, device=dev)
+    per_rep = 2 * mw.num_blocks * mw.Hkv * 16 * (mw.D + 4)
+    R = max(1, math.ceil((1 << 30) / per_rep))
+    g = torch.Generator(device=dev)
+    g.manual_seed(56)
+    reps = []
+    for r in range(R):
+        k, v, ks, vs = ops.fp8_cache(mw.num_blocks, mw.Hkv, mw.D, device=dev)
+        kb = torch.randn((T, mw.Hkv, mw.D), generator=g, device=dev).to(torch.bfloat16)
+        vb = torch.randn((T, mw.Hkv, mw.D), generator=g, device=dev).to(torch.bfloat16)
+        ops.paged_cache_append_fp8(k, v, ks, vs, kb, vb, all_slots)
+        del kb, vb
+        qd = torch.randn((mw.samples, mw.Hq, mw.D), generator=g, device=dev).to(torch.bfloat16)
+        qp = torch.randn((mw.chunk, mw.Hq, mw.D), generator=g, device=dev).to(torch.bfloat16)
+        od = torch.empty((mw.samples, mw.Hq, mw.D), dtype=torch.float32, device=dev)
+        op = torch.empty((mw.chunk, mw.Hq, mw.D), dtype=torch.float32, device=dev)
+        ws = ops.decode_workspace(mw.samples, mw.Hq, mw.D, mcl, 512)
+        mix = (od, qd, dt_t, dl_t, mcl, op, qp, pt_t, [mw.ctx_start], [mw.chunk], k, v, ks, vs, mw.scale)
+        reps.append({
+            "dec": ops.PreparedDecodeFp8(od, qd, k, v, ks, vs, dt_t, dl_t, mcl, mw.scale, 0, None,
+                                         host_context_lens=dlens),
+            "dec_p512": ops.PreparedDecodeFp8(od, qd, k, v, ks, vs, dt_t, dl_t, mcl, mw.scale, 512, ws,
+                                              host_context_lens=dlens),
+            "pre": ops.PreparedPrefillFp8(op, qp, k, v, ks, vs, pt_t[0], mw.ctx_start, mw.scale),
+            "mix": lambda mix=mix: ops.paged_attention_mixed_fp8(*mix, host_dec_lens=dlens),
+            "mix_p512": lambda mix=mix, ws=ws: ops.paged_attention_mixed_fp8(*mix, host_dec_lens=dlens,
+                                                                              dec_partition_size=512, workspace=ws),
+        })
+    stream = torch.cuda.current_stream()
+
+    def run(*names):
+        def fn(i):
+            r = reps[i % R]
+            for nm in names:
+                r[nm]()
+        return fn
+
+    for nm in reps[0]:
+        for i in range(3):
+            run(nm)(i)
+    variants = {"decode": ("dec",), "decode_split512": ("dec_p512",), "prefill": ("pre",),
+                "separate": ("dec", "pre"), "separate_split512": ("dec_p512", "pre"), "mixed": ("mix",),
+                "mixed_split512": ("mix_p512",)}
+    t = {key: _spun_avg_us(torch, stream, run(*names), n, spin) for key, names in variants.items()}
+    best_sep = min(t["separate"], t["separate_split512"])
+    best_mix = min(t["mixed"], t["mixed_split512"])
+    return {"workload": "mixed_step_16_samples_prefix2048_plus_chunk512_ctx4096_gqa32x8_d128_fp8_cache_bf16_query",
+            "us": {k: round(x, 2) for k, x in t.items()}, "mixed_speedup_over_separate": round(best_sep / best_mix, 3),
+            "replicas": R}
+
+
 def measure_mixed(args, dev, counted=False):
     """The mixed prefix-sharing step (a 2,048-token shared prefix), and its copy-on-write variant
     (2,040 tokens: the partial last prefix block is copied for 15 of the 16 samples).  counted:
@@ -914,6 +990,7 @@ def measure_mixed(args, dev, counted=False):
     n = max(20, args.steps // 4)
     res = _mixed_case(args, dev, 2048, n, spin)
     res["copy_on_write_variant"] = _mixed_case(args, dev, 2040, n, spin)
+    res["fp8_cache"] = _mixed_fp8_case(args, dev, n, spin)
     res["timing"] = (f"{n} back-to-back calls behind a 50 ms spin, one HIP event pair (device time only); "
                      "grouped = paged_attention_decode_grouped / paged_attention_mixed with dec_group_size "
                      "(2 samples per workgroup), split512 = 512-token partitions + reduce; every decode variant's "
