@@ -144,3 +144,40 @@ def test_noalloc_decode_rejects_partials_beyond_its_scratch():
     st = L.paged_attention_decode_noalloc(p, pkv.PKV_F32, p, p, p, p, p, 64, 32, 8, 128, 16, 4096, 100000, 65536,
                                           0.1, 512, pkv.PKV_BF16, NULL, NULL)
     assert st == pkv.PKV_EINVAL and "static scratch" in _lib.last_error()
+
+
+def test_fp8_prefill_and_mixed_host_validation():
+    """paged_attention_prefill_chunk_fp8 and paged_attention_mixed_fp8 refuse bad arguments on the
+    host (query type, output type, head size, scale, alignment, pool bounds, chunk count) and
+    treat empty work as a no-op, all before any launch."""
+    L = pkv.lib
+    p = 1 << 12
+    bf, f32 = pkv.PKV_BF16, pkv.PKV_F32
+
+    def pre(q_dtype=bf, out_dtype=f32, ctx=0, C=16, D=128, scale=0.1, ks=p):
+        return L.paged_attention_prefill_chunk_fp8(p, out_dtype, p, p, p, ks, p, p, ctx, C, 32, 8, D, 16, 64, scale,
+                                                   q_dtype, NULL)
+    assert pre(q_dtype=f32) == pkv.PKV_EUNSUPPORTED
+    assert pre(out_dtype=pkv.PKV_F16) == pkv.PKV_EINVAL
+    assert pre(D=96) == pkv.PKV_EUNSUPPORTED
+    for bad in (0.0, -1.0, float("inf"), float("nan")):
+        assert pre(scale=bad) == pkv.PKV_EINVAL
+    assert pre(ctx=1000, C=100) == pkv.PKV_EINVAL       # past the 64-block pool
+    assert pre(ks=p + 4) == pkv.PKV_EINVAL              # scales not 16-byte aligned
+    assert pre(C=0) == pkv.PKV_OK
+
+    starts = (C.c_int32 * 17)(*([0] * 17))
+    lens = (C.c_int32 * 17)(*([16] * 17))
+
+    def mix(q_dtype=bf, out_dtype=f32, n_chunks=1, scale=0.1, ks=p, B=0):
+        return L.paged_attention_mixed_fp8(p, p, p, p, B, 4, 64 if B else 0, NULL, 0, NULL, 0, p, p, p, 8, starts,
+                                           lens, n_chunks, out_dtype, p, p, ks, p, 32, 8, 128, 16, 64, scale, q_dtype,
+                                           NULL)
+    assert mix(q_dtype=f32) == pkv.PKV_EUNSUPPORTED
+    assert mix(out_dtype=pkv.PKV_F16) == pkv.PKV_EINVAL
+    assert mix(n_chunks=17) == pkv.PKV_EUNSUPPORTED
+    assert mix(scale=0.0) == pkv.PKV_EINVAL
+    assert mix(ks=NULL) == pkv.PKV_EINVAL
+    assert mix(ks=p + 4) == pkv.PKV_EINVAL
+    assert mix(B=2, n_chunks=0, out_dtype=pkv.PKV_F16) == pkv.PKV_EINVAL
+    assert mix(n_chunks=0) == pkv.PKV_OK                # nothing to do
