@@ -1000,11 +1000,13 @@ def measure_mixed(args, dev, counted=False):
     return res
 
 
-def measure_tiny(args, dev):
+def measure_tiny(args, dev, counted=False):
     """The tiny fp32 step: batch 4, 8 q = 8 kv heads of 64, a 32-block pool handed out from a seeded
-    permutation, lengths {5, 17, 32, 40}; one paged_cache_append of the step's 4 tokens plus one
-    paged_attention_decode (fp32 caches have no fused append).  Device time of n back-to-back steps
-    behind a spin; the step moves 0.4 MB, so launch latency, not HBM, sets its time."""
+    permutation, lengths {5, 17, 32, 40}.  A step = paged_attention_decode_append: the step's 4
+    tokens written into their slots inside the decode launch (the vector-ALU kernel's fused append);
+    the append + decode as two launches is reported beside it.  Device time of n back-to-back steps
+    behind a spin; the step moves 0.4 MB, so launch latency, not HBM, sets its time.  counted: the
+    counter run, which launches the fused step only."""
     import numpy as np
     import torch
 
@@ -1027,29 +1029,39 @@ def measure_tiny(args, dev):
     sk = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev, dtype=f32)
     sv = torch.randn((w.B, w.Hkv, w.D), generator=g, device=dev, dtype=f32)
     out = torch.empty((w.B, w.Hq, w.D), dtype=f32, device=dev)
+    tables_t, lens_t = torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev)
     app = ops.PreparedAppend(k, v, sk, sv, torch.from_numpy(step_slots).to(dev))
-    dec = ops.PreparedDecode(out, q, k, v, torch.from_numpy(tables).to(dev), torch.from_numpy(lens).to(dev),
-                             int(lens.max()), w.scale, 0, None, host_context_lens=lens)
+    dec = ops.PreparedDecode(out, q, k, v, tables_t, lens_t, int(lens.max()), w.scale, 0, None,
+                             host_context_lens=lens)
+    fused = ops.PreparedDecode(out, q, k, v, tables_t, lens_t, int(lens.max()), w.scale, 0, None,
+                               host_context_lens=lens, new_key=sk, new_value=sv)
     for _ in range(5):
-        app()
-        dec()
+        fused()
+        if not counted:
+            app()
+            dec()
     stream = torch.cuda.current_stream()
     n = max(50, args.steps)
     spin = int(_spin_cycles_per_ms(torch, stream) * 20)
-    step_us = _spun_avg_us(torch, stream, lambda i: (app(), dec()), n, spin)
-    dec_us = _spun_avg_us(torch, stream, lambda i: dec(), n, spin)
+    step_us = _spun_avg_us(torch, stream, lambda i: fused(), n, spin)
+    sep_us = dec_us = None
+    if not counted:
+        sep_us = _spun_avg_us(torch, stream, lambda i: (app(), dec()), n, spin)
+        dec_us = _spun_avg_us(torch, stream, lambda i: dec(), n, spin)
     nbytes = w.kv_bytes() + w.q_bytes()
-    gbs = nbytes / (dec_us * 1e-6) / 1e9
+    gbs = nbytes / (step_us * 1e-6) / 1e9
     res = {
         "workload": w.name,
         "kv_plus_q_bytes_per_step": nbytes,
         "us_per_step": round(step_us, 3),
         "seqs_steps_per_s": round(w.B / (step_us * 1e-6), 1),
-        "kernel_us": {"decode": round(dec_us, 3), "append": round(step_us - dec_us, 3)},
-        "step": "paged_cache_append + paged_attention_decode (fp32, single pass, vector-ALU decode)",
-        "roofline": {"bound": "hbm", "kernel": "decode_valu_kernel", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 6), **_traffic_fields("tiny", nbytes),
-                     "note": "latency-bound: 32 workgroups move 0.4 MB"},
+        "separate_launches_us_per_step": None if sep_us is None else round(sep_us, 3),
+        "kernel_us": {"decode_fused_append": round(step_us, 3),
+                      "decode_alone": None if dec_us is None else round(dec_us, 3)},
+        "step": "paged_attention_decode_append (fp32: the new tokens written inside the vector-ALU decode), single pass",
+        "roofline": {"bound": "hbm", "kernel": "decode_valu_kernel (append fused)", "achieved": round(gbs, 2),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 6),
+                     **_traffic_fields("tiny", nbytes), "note": "latency-bound: 32 workgroups move 0.4 MB"},
         "timing": f"{n} back-to-back steps behind a 20 ms spin, one HIP event pair (device time only)",
     }
     if not args.no_cpu_baseline:
@@ -1286,7 +1298,7 @@ def main():
             args.no_extra = True
             args.workload = "llama"
         else:
-            res = {"long": lambda: measure_long(args, dev), "tiny": lambda: measure_tiny(args, dev),
+            res = {"long": lambda: measure_long(args, dev), "tiny": lambda: measure_tiny(args, dev, counted=True),
                    "prefill": lambda: measure_prefill(args, dev), "prefill_fp8": lambda: measure_prefill(args, dev, True),
                    "fp8": lambda: measure_fp8(args, dev, None), "mixed": lambda: measure_mixed(args, dev, counted=True),
                    "trace": lambda: measure_trace(dev, counters=True)}[args.only]()
