@@ -120,6 +120,43 @@ def test_fused_batch_beyond_the_order_table(ps):
     _fused_vs_all(m, seqs, w, t, slots, ps)
 
 
+@pytest.mark.parametrize("ps", [64, 512])
+def test_fused_with_wrong_host_lengths(ps):
+    """The host copy of the lengths only schedules the work.  With partitions, the slices past a
+    sequence's host partition count leave at once and the slice of its last host partition runs
+    whatever partitions the device lengths add, the new token's included.  A host copy that
+    understates, overstates or scrambles the lengths must leave output and caches bit for bit as
+    without one."""
+    lens = [1, 2, 16, 17, 33, 100, 511, 513, 1000, 1500, 64, 2049]
+    w = wl.custom_decode(77 + ps, lens, 32, 8, 128, "bf16", partition_size=ps)
+    t = wl.decode_tensors(w)
+    m, seqs = _prefix(w, t)
+    slots, _ = _reserve(m, seqs)
+    tables, dlens = m.tables(seqs)
+    B, mcl = len(seqs), int(dlens.max())
+    q = to_dev(t.q, w.dtype)
+    sk, sv = to_dev(t.step_k, w.dtype), to_dev(t.step_v, w.dtype)
+    k0, v0 = m.k.clone(), m.v.clone()
+    results = []
+    for hl in (None, dlens, np.ones_like(dlens), np.full_like(dlens, mcl), dlens[::-1].copy(),
+               (dlens * 7) % (mcl + 1)):
+        k, v = k0.clone(), v0.clone()
+        out = torch.full((B, w.Hq, w.D), float("nan"), dtype=torch.float32, device="cuda")
+        ops.paged_attention_decode_append(out, q, sk, sv, k, v, i32(tables), i32(dlens), mcl, w.scale, ps,
+                                          ops.decode_workspace(B, w.Hq, w.D, mcl, ps), host_context_lens=hl)
+        torch.cuda.synchronize()
+        results.append((out, k, v))
+    out0, k0_, v0_ = results[0]
+    assert torch.isfinite(out0).all()
+    for out, k, v in results[1:]:
+        assert torch.equal(out0.view(torch.int32), out.view(torch.int32))
+        assert torch.equal(k0_.view(torch.int16), k.view(torch.int16))
+        assert torch.equal(v0_.view(torch.int16), v.view(torch.int16))
+    m.cache.append(t.step_k, t.step_v, slots)
+    ref = oatt.paged_decode(t.q, m.cache, tables, dlens, w.scale)
+    assert float(np.abs(out0.cpu().numpy().astype(np.float64) - ref).max()) <= ATOL
+
+
 @pytest.mark.parametrize("ps", [512, 0])
 def test_fused_llama_shaped_full_size(ps):
     w = wl.llama_decode(2)
