@@ -30,10 +30,11 @@ Modules:
   brute      pure-Python per-page / per-token loops for tiny inputs (pins the numpy path)
 
 Pins: every function here is checked in ``tests/test_oracle_*.py`` against values the pages
-fix, closed forms, invariants and brute force.  Parity unpinned:
-none of the pages prints an attention value or a worked attention example, so no attention
-output is pinned to a printed number; attention is pinned to closed forms, invariants,
-brute force and an independent library routine instead.
+fix, closed forms, invariants and brute force.  None of the pages prints an attention value
+or a worked attention example, so attention is pinned by the other kinds: closed forms
+(one-token context = V, constant V, zero query = mean of V), invariants (physical-block
+permutation, softmax weights summing to 1, GQA = MHA on repeated K/V), brute force on tiny
+inputs, and torch's scaled-dot-product attention as an independent library routine.
 """
 
 from .pool import PoolModel, OutOfBlocks, InvalidOp  # noqa: F401
