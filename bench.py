@@ -85,7 +85,7 @@ _PRE_SRC = ("prefill_tile.h", "device.h", "fp8_device.h")
 TRAFFIC_LINES = {
     "llama": (r"decode_mfma_kernel<.*, true>", _DEC_SRC, "launch"),
     "long": (r"decode_mfma_kernel<.*, true>", _DEC_SRC, "launch"),
-    "tiny": (r"decode_valu_kernel<", _DEC_SRC, "launch"),
+    "tiny": (r"decode_valu_kernel<", _DEC_SRC + ("decode_valu.h",), "launch"),
     "prefill": (r"prefill_mfma_kernel<", ("prefill.hip",) + _PRE_SRC, "launch"),
     "prefill_fp8": (r"prefill_fp8_kernel<", ("prefill_fp8.hip",) + _PRE_SRC, "launch"),
     "fp8": (r"decode_fp8_kernel<.*, false>", ("fp8.hip", "fp8_device.h", "device.h"), "launch"),

@@ -380,7 +380,9 @@ int paged_attention_prefill_chunk(void* out, int32_t out_dtype, const void* quer
  *            chunk after another in pre_query / pre_out ([sum of lengths][Hq][D]); its block table
  *            is row i of pre_block_tables [num_chunks][pre_max_blocks] (device); the chunks' K/V
  *            are already appended.  Starts and lengths are host arrays (they size the grid).
- *   group size Hq / Hkv in {1, 2, 4, 8}; bf16 or fp16; head_dim 64/128.
+ *   group size Hq / Hkv in {1, 2, 4, 8}; bf16, fp16 or fp32; head_dim 64/128.  fp32 caches run
+ *   the fp32 decode and prefill kernels' vector-ALU bodies (one wave per query head and sequence
+ *   or chunk row; dec_group_size must be 1, else PKV_EUNSUPPORTED), bit for bit theirs.
  */
 int paged_attention_mixed(void* dec_out, const void* dec_query, const int32_t* dec_block_tables,
                           const int32_t* dec_context_lens, int32_t B_dec, int32_t dec_max_blocks,

@@ -18,7 +18,9 @@
 
 #include "decode_group.h"
 #include "decode_host.h"
+#include "decode_valu.h"
 #include "mixed_host.h"
+#include "prefill_valu.h"
 
 namespace pkv {
 namespace {
@@ -94,6 +96,75 @@ void launch_d(const MixedArgs& m, int D, int ns, int nwd, int grid, hipStream_t 
     launch_g<DT, DT_OUT, 128>(m, ns, nwd, grid, s);
 }
 
+// fp32 caches: the vector-ALU bodies, one wave per workgroup.  Workgroups [0, n_dec_wg) run a
+// (query head, sequence, partition) of the decode (decode_valu_part, the fp32 decode kernel's
+// body), the rest a (query head, row) of a chunk (prefill_valu_part, the fp32 prefill kernel's).
+struct MixedValuArgs {
+  DecodeArgs dec;
+  int32_t B_dec;
+  int32_t n_dec_wg;  // Hq * B_dec * max_parts
+  ChunkSet pre;      // chunk i runs Hq * C workgroups from chunks[i].wg_base on
+};
+
+template <int DT_OUT, int D>
+__global__ void __launch_bounds__(64) mixed_valu_kernel(MixedValuArgs m) {
+  const int id = blockIdx.x;
+  if (id < m.n_dec_wg) {
+    const int hq = id % m.dec.Hq;
+    const int y = (id / m.dec.Hq) % m.B_dec;
+    const int z = id / (m.dec.Hq * m.B_dec);
+    decode_valu_part<PKV_F32, DT_OUT, D>(m.dec, hq, y, z);
+    return;
+  }
+  int c = 0;
+  while (c + 1 < m.pre.n_chunks && id >= m.pre.chunks[c + 1].wg_base) ++c;
+  const ChunkDesc& ch = m.pre.chunks[c];
+  const int local = id - ch.wg_base;
+  PrefillArgs pa{};
+  pa.out = ch.out;
+  pa.q = ch.q;
+  pa.k = m.pre.k;
+  pa.v = m.pre.v;
+  pa.table = ch.table;
+  pa.ctx_start = ch.ctx_start;
+  pa.C = ch.C;
+  pa.Hq = m.pre.Hq;
+  pa.Hkv = m.pre.Hkv;
+  pa.num_blocks = m.pre.num_blocks;
+  pa.scale_log2 = m.pre.scale_log2;
+  prefill_valu_part<DT_OUT, D>(pa, local % m.pre.Hq, local / m.pre.Hq);
+}
+
+// Chunks of the fp32 launch: Hq * C workgroups each, one after another from wg on.
+inline int pack_valu_chunks(const char* fn, ChunkSet& cs, int64_t& wg, void* pre_out, const void* pre_query,
+                            const int32_t* pre_block_tables, int32_t pre_max_blocks, const int32_t* host_ctx_starts,
+                            const int32_t* host_chunk_lens, int32_t num_chunks, int32_t head_dim) {
+  const int64_t row_bytes = static_cast<int64_t>(cs.Hq) * head_dim * 4;
+  int64_t row0 = 0;
+  int n = 0;
+  for (int i = 0; i < num_chunks; ++i) {
+    const int32_t start = host_ctx_starts[i], C = host_chunk_lens[i];
+    if (start < 0 || C < 0) return fail(PKV_EINVAL, "%s: chunk %d has a negative start or length", fn, i);
+    if (static_cast<int64_t>(start) + C > static_cast<int64_t>(pre_max_blocks) * kBlock)
+      return fail(PKV_EINVAL, "%s: chunk %d extends past pre_max_blocks * block_size", fn, i);
+    if (C > 0) {
+      ChunkDesc& d = cs.chunks[n++];
+      d.out = static_cast<uint8_t*>(pre_out) + row0 * row_bytes;
+      d.q = static_cast<const uint8_t*>(pre_query) + row0 * row_bytes;
+      d.table = pre_block_tables + static_cast<int64_t>(i) * pre_max_blocks;
+      d.ctx_start = start;
+      d.C = C;
+      d.row_tiles = 0;
+      d.wg_base = static_cast<int32_t>(std::min<int64_t>(wg, INT32_MAX));
+      wg += static_cast<int64_t>(cs.Hq) * C;
+    }
+    row0 += C;
+  }
+  cs.n_chunks = n;
+  if (wg > INT32_MAX / 64) return fail(PKV_EINVAL, "%s: too much work for one launch", fn);
+  return PKV_OK;
+}
+
 }  // namespace
 }  // namespace pkv
 
@@ -110,7 +181,8 @@ extern "C" int paged_attention_mixed(void* dec_out, const void* dec_query, const
                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                                      int32_t num_blocks, float scale, int32_t dtype, pkv_stream_t stream) {
   const char* fn = "paged_attention_mixed";
-  if (dtype != PKV_BF16 && dtype != PKV_F16) return fail(PKV_EUNSUPPORTED, "%s: dtype %d (bf16 or fp16)", fn, dtype);
+  if (dtype != PKV_BF16 && dtype != PKV_F16 && dtype != PKV_F32)
+    return fail(PKV_EUNSUPPORTED, "%s: dtype %d (bf16, fp16 or fp32)", fn, dtype);
   if (out_dtype != PKV_F32 && out_dtype != dtype)
     return fail(PKV_EINVAL, "%s: out_dtype must be PKV_F32 or the input dtype", fn);
   if (B_dec < 0 || num_chunks < 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_blocks <= 0 || block_size <= 0 ||
@@ -124,6 +196,8 @@ extern "C" int paged_attention_mixed(void* dec_out, const void* dec_query, const
   if (block_size != kBlock) return fail(PKV_EUNSUPPORTED, "%s: block_size %d (kernels implement 16)", fn, block_size);
   if (head_dim != 64 && head_dim != 128) return fail(PKV_EUNSUPPORTED, "%s: head_dim %d", fn, head_dim);
   if (num_chunks > kMaxChunks) return fail(PKV_EUNSUPPORTED, "%s: more than %d prefill chunks", fn, kMaxChunks);
+  if (dtype == PKV_F32 && dec_group_size != 1)
+    return fail(PKV_EUNSUPPORTED, "%s: fp32 caches take dec_group_size 1", fn);
   if (dec_group_size != 1 && dec_group_size != mixed_group_size(G))
     return fail(PKV_EUNSUPPORTED, "%s: dec_group_size %d (1, or %d for %d query heads per KV head)", fn,
                 dec_group_size, mixed_group_size(G), G);
@@ -169,6 +243,28 @@ extern "C" int paged_attention_mixed(void* dec_out, const void* dec_query, const
   a.part_size = pl.part_size;
   a.scale_log2 = scale * kLog2e;
   if (has_dec && dec_group_size == 1) set_work_order(a, host_dec_context_lens, B_dec, dec_max_context_len, pl);
+  if (dtype == PKV_F32) {
+    MixedValuArgs mv{};
+    mv.dec = a;
+    mv.pre = m.pre;
+    mv.B_dec = has_dec ? B_dec : 1;
+    int64_t wv = has_dec ? static_cast<int64_t>(num_q_heads) * B_dec * pl.max_parts : 0;
+    if (wv > INT32_MAX / 64) return fail(PKV_EINVAL, "%s: too much decode work for one launch", fn);
+    mv.n_dec_wg = static_cast<int32_t>(wv);
+    const int vst = pack_valu_chunks(fn, mv.pre, wv, pre_out, pre_query, pre_block_tables, pre_max_blocks,
+                                     host_ctx_starts, host_chunk_lens, num_chunks, head_dim);
+    if (vst != PKV_OK) return vst;
+    if (wv == 0) return PKV_OK;
+    hipStream_t s = as_stream(stream);
+    if (head_dim == 64)
+      hipLaunchKernelGGL((mixed_valu_kernel<PKV_F32, 64>), dim3(static_cast<uint32_t>(wv)), dim3(64), 0, s, mv);
+    else
+      hipLaunchKernelGGL((mixed_valu_kernel<PKV_F32, 128>), dim3(static_cast<uint32_t>(wv)), dim3(64), 0, s, mv);
+    const int st = check_launch(fn);
+    if (st != PKV_OK || !has_dec || pl.max_parts <= 1) return st;
+    return paged_attention_decode_reduce(dec_out, out_dtype, dec_context_lens, B_dec, num_q_heads, head_dim,
+                                         dec_max_context_len, dec_partition_size, workspace, workspace_bytes, stream);
+  }
   m.dec_rows = has_dec ? (dec_group_size == 1 ? B_dec : (B_dec + dec_group_size - 1) / dec_group_size) : 1;
   int64_t wg = has_dec ? (static_cast<int64_t>(num_kv_heads) * m.dec_rows * pl.max_parts + 7) / 8 * 8 : 0;
   m.n_dec_wg = static_cast<int32_t>(wg);

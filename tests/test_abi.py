@@ -181,3 +181,21 @@ def test_fp8_prefill_and_mixed_host_validation():
     assert mix(ks=p + 4) == pkv.PKV_EINVAL
     assert mix(B=2, n_chunks=0, out_dtype=pkv.PKV_F16) == pkv.PKV_EINVAL
     assert mix(n_chunks=0) == pkv.PKV_OK                # nothing to do
+
+
+def test_mixed_host_validation():
+    """paged_attention_mixed: fp32 caches are accepted but not grouped; an unknown dtype and a
+    group size other than 1 or the 8-column size are refused; nothing to do is a no-op."""
+    L = pkv.lib
+    p = 1 << 12
+    starts = (C.c_int32 * 1)(0)
+    lens = (C.c_int32 * 1)(16)
+
+    def mix(dtype=pkv.PKV_BF16, out_dtype=pkv.PKV_F32, group=1, n_chunks=1, B=0):
+        return L.paged_attention_mixed(p, p, p, p, B, 4, 64 if B else 0, NULL, 0, group, NULL, 0, p, p, p, 8, starts,
+                                       lens, n_chunks, out_dtype, p, p, 32, 8, 128, 16, 64, 0.1, dtype, NULL)
+    assert mix(dtype=7) == pkv.PKV_EUNSUPPORTED
+    assert mix(dtype=pkv.PKV_F32, group=2, B=2) == pkv.PKV_EUNSUPPORTED
+    assert mix(group=3, B=2) == pkv.PKV_EUNSUPPORTED
+    assert mix(dtype=pkv.PKV_F32, n_chunks=0) == pkv.PKV_OK
+    assert mix(n_chunks=0) == pkv.PKV_OK

@@ -122,6 +122,35 @@ def test_mixed_split_k_and_grouped_decode(seed, ps, ns):
     _check_oracle(m, dec, pre, dtab, dlens, ptab, q_dec, q_pre, chunks, scale)
 
 
+F32_CASES = [
+    # seed, decode lengths, chunks, Hq, Hkv, D, partition size
+    (11, [5, 17, 32, 40], [(0, 8), (24, 9)], 8, 8, 64, 0),          # the tiny step's shape
+    (12, [1, 300, 64, 1000], [(0, 37), (100, 16), (640, 130)], 16, 4, 128, 0),
+    (13, [129, 700, 2], [(33, 70)], 32, 8, 64, 256),
+    (14, [], [(0, 20), (48, 64)], 8, 2, 128, 0),
+    (15, [900, 3], [], 16, 8, 64, 64),
+]
+
+
+@pytest.mark.parametrize("seed,dec_lens,chunks,Hq,Hkv,D,ps", F32_CASES)
+def test_mixed_fp32_equals_separate_launches(seed, dec_lens, chunks, Hq, Hkv, D, ps):
+    """fp32 caches: the mixed launch runs the vector-ALU decode and prefill bodies, bit for bit the
+    fp32 decode (split-K included) and fp32 prefill launches, and within 2e-3 of the oracle."""
+    m, dseqs, pseqs, q_dec, q_pre = _scene(seed, dec_lens, chunks, Hq, Hkv, D, "f32")
+    scale = 1 / np.sqrt(D)
+    dec, pre, dtab, dlens, ptab = _run(m, dseqs, pseqs, chunks, q_dec, q_pre, Hq, D, "f32", scale,
+                                       host_lens=seed % 2 == 1, ps=ps)
+    _check_oracle(m, dec, pre, dtab, dlens, ptab, q_dec, q_pre, chunks, scale)
+
+
+def test_mixed_fp32_rejects_grouping():
+    chunks = [(0, 16)]
+    m, dseqs, pseqs, q_dec, q_pre = _scene(16, [40, 50], chunks, 8, 8, 64, "f32")
+    with pytest.raises(PagedKVError) as e:
+        _run(m, dseqs, pseqs, chunks, q_dec, q_pre, 8, 64, "f32", 0.125, ns=8)
+    assert e.value.status == PKV_EUNSUPPORTED
+
+
 def test_mixed_output_in_bf16():
     chunks = [(64, 64)]
     m, dseqs, pseqs, q_dec, q_pre = _scene(9, [300, 45], chunks, 32, 8, 128, "bf16")
