@@ -88,7 +88,7 @@ TRAFFIC_LINES = {
     "tiny": (r"decode_valu_kernel<", _DEC_SRC + ("decode_valu.h",), "launch"),
     "prefill": (r"prefill_mfma_kernel<", ("prefill.hip",) + _PRE_SRC, "launch"),
     "prefill_fp8": (r"prefill_fp8_kernel<", ("prefill_fp8.hip",) + _PRE_SRC, "launch"),
-    "fp8": (r"decode_fp8_kernel<.*, false>", ("fp8.hip", "fp8_device.h", "device.h"), "launch"),
+    "fp8": (r"decode_fp8_kernel<.*, false>", ("fp8.hip", "decode_fp8_part.h", "fp8_device.h", "device.h"), "launch"),
     "mixed": (r"decode_group_kernel<", ("decode_group.hip", "decode_group.h") + _DEC_SRC, "launch"),
     "trace": (r"decode_(mfma|reduce)_kernel<", _DEC_SRC, "replay"),
 }
@@ -957,6 +957,8 @@ def _mixed_fp8_case(args, dev, n, spin):
                                          host_context_lens=dlens),
             "dec_p512": ops.PreparedDecodeFp8(od, qd, k, v, ks, vs, dt_t, dl_t, mcl, mw.scale, 512, ws,
                                               host_context_lens=dlens),
+            "dec_g2_p512": lambda od=od, qd=qd, k=k, v=v, ks=ks, vs=vs, ws=ws: ops.paged_attention_decode_grouped_fp8(
+                od, qd, k, v, ks, vs, dt_t, dl_t, mcl, mw.scale, 2, 512, ws),
             "pre": ops.PreparedPrefillFp8(op, qp, k, v, ks, vs, pt_t[0], mw.ctx_start, mw.scale),
             "mix": lambda mix=mix: ops.paged_attention_mixed_fp8(*mix, host_dec_lens=dlens),
             "mix_p512": lambda mix=mix, ws=ws: ops.paged_attention_mixed_fp8(*mix, host_dec_lens=dlens,
@@ -974,14 +976,16 @@ def _mixed_fp8_case(args, dev, n, spin):
     for nm in reps[0]:
         for i in range(3):
             run(nm)(i)
-    variants = {"decode": ("dec",), "decode_split512": ("dec_p512",), "prefill": ("pre",),
-                "separate": ("dec", "pre"), "separate_split512": ("dec_p512", "pre"), "mixed": ("mix",),
-                "mixed_split512": ("mix_p512",)}
+    variants = {"decode": ("dec",), "decode_split512": ("dec_p512",), "decode_grouped_2_split512": ("dec_g2_p512",),
+                "prefill": ("pre",), "separate": ("dec", "pre"), "separate_split512": ("dec_p512", "pre"),
+                "separate_grouped": ("dec_g2_p512", "pre"), "mixed": ("mix",), "mixed_split512": ("mix_p512",)}
     t = {key: _spun_avg_us(torch, stream, run(*names), n, spin) for key, names in variants.items()}
     best_sep = min(t["separate"], t["separate_split512"])
     best_mix = min(t["mixed"], t["mixed_split512"])
     return {"workload": "mixed_step_16_samples_prefix2048_plus_chunk512_ctx4096_gqa32x8_d128_fp8_cache_bf16_query",
             "us": {k: round(x, 2) for k, x in t.items()}, "mixed_speedup_over_separate": round(best_sep / best_mix, 3),
+            "decode_grouped_speedup": round(min(t["decode"], t["decode_split512"]) / t["decode_grouped_2_split512"], 2),
+            "grouped": "paged_attention_decode_grouped_fp8, 2 samples per workgroup, 512-token partitions",
             "replicas": R}
 
 

@@ -454,6 +454,30 @@ int paged_attention_decode_fp8_partitions(void* out, int32_t out_dtype, const vo
                                           const int32_t* host_context_lens, pkv_stream_t stream);
 
 /*
+ * paged_attention_decode_grouped_fp8 - paged_attention_decode_grouped over an fp8 cache.
+ * [Chapter] "PagedAttention: KV cache memory" (samples and conversations sharing a prefix point at
+ * the same physical blocks) over the quantised cache of [Notes] "Memory, not compute, caps the
+ * batch".  Sequences group_size * k .. group_size * k + group_size - 1 run in one workgroup per KV
+ * head (and partition), their query heads side by side in the matrix columns; a 32-token step
+ * whose two blocks are the same in every member's table has its codes and scales read once for
+ * the whole group.
+ *   group_size  1 (exactly paged_attention_decode_fp8 without a work order), or a size with
+ *               group_size * (num_q_heads / num_kv_heads) equal to 8 or 16 (PKV_EUNSUPPORTED
+ *               otherwise).
+ *   Other arguments as paged_attention_decode_fp8 (no host_context_lens: groups run in batch order).
+ * Output: bit for bit that of paged_attention_decode_fp8 with the same partition_size.  Codes and
+ * scales of every token some member of a group sees must be finite.
+ */
+int paged_attention_decode_grouped_fp8(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                       const void* v_cache, const void* k_scale, const void* v_scale,
+                                       const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                                       int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                       int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                       int32_t max_context_len, float scale, int32_t partition_size,
+                                       void* workspace, size_t workspace_bytes, int32_t q_dtype,
+                                       int32_t group_size, pkv_stream_t stream);
+
+/*
  * paged_attention_decode_append_fp8 - paged_attention_decode_append over an fp8 cache: one decode
  * step with the step's quantising append fused in.  [Serving] Steps 4 and 6 in one launch, over
  * the quantised cache the [Notes] section "Memory, not compute, caps the batch" asks for: every

@@ -94,6 +94,9 @@ _SIGS = {
                                                     _i32, _i32, _i32, _f32, _i32, _vp]),
     "paged_attention_decode_fp8": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32,
                                              _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32, _vp, _vp]),
+    "paged_attention_decode_grouped_fp8": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                                     _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz, _i32,
+                                                     _i32, _vp]),
     "paged_attention_decode_fp8_partitions": (C.c_int, [_vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                         _i32, _i32, _i32, _i32, _i32, _i32, _f32, _i32, _vp, _sz,
                                                         _i32, _vp, _vp]),

@@ -27,6 +27,7 @@
 #include <algorithm>
 #include <cmath>
 
+#include "decode_fp8_group.h"
 #include "decode_fp8_part.h"
 
 namespace pkv {
@@ -162,6 +163,44 @@ void dispatch_fp8_dim(const Fp8Args& a, int D, int B, bool wide, hipStream_t s) 
     dispatch_fp8_group<DT, DT_OUT, 128>(a, B, wide, s);
 }
 
+// Grouped FP8 decode: grid = (Hkv, groups, max_parts); at least two waves per SIMD whatever NW.
+template <int DT, int DT_OUT, int D, int G, int NS, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2)))
+decode_fp8_group_kernel(Fp8Args a, int32_t B) {
+  __shared__ float smem[fp8_group_smem_floats<D, G, NS, NW>()];
+  decode_fp8_group_part<DT, DT_OUT, D, G, NS, NW>(a, B, blockIdx.x, blockIdx.y, blockIdx.z, smem);
+}
+
+template <int DT, int DT_OUT, int D, int G, int NS>
+void launch_fp8_group_ns(const Fp8Args& a, int B, int ngroups, bool wide, hipStream_t s) {
+  const dim3 grid(a.Hkv, ngroups, a.max_parts);
+  if (wide)
+    hipLaunchKernelGGL((decode_fp8_group_kernel<DT, DT_OUT, D, G, NS, 8>), grid, dim3(512), 0, s, a, B);
+  else
+    hipLaunchKernelGGL((decode_fp8_group_kernel<DT, DT_OUT, D, G, NS, 4>), grid, dim3(256), 0, s, a, B);
+}
+
+// Group sizes whose columns (group_size x query heads per KV head) fill 8 or 16 matrix columns.
+template <int DT, int DT_OUT, int D>
+bool launch_fp8_group_gs(const Fp8Args& a, int B, int G, int NS, int ngroups, bool wide, hipStream_t s) {
+  switch (G * 100 + NS) {
+    case 108: launch_fp8_group_ns<DT, DT_OUT, D, 1, 8>(a, B, ngroups, wide, s); return true;
+    case 116: launch_fp8_group_ns<DT, DT_OUT, D, 1, 16>(a, B, ngroups, wide, s); return true;
+    case 204: launch_fp8_group_ns<DT, DT_OUT, D, 2, 4>(a, B, ngroups, wide, s); return true;
+    case 208: launch_fp8_group_ns<DT, DT_OUT, D, 2, 8>(a, B, ngroups, wide, s); return true;
+    case 402: launch_fp8_group_ns<DT, DT_OUT, D, 4, 2>(a, B, ngroups, wide, s); return true;
+    case 404: launch_fp8_group_ns<DT, DT_OUT, D, 4, 4>(a, B, ngroups, wide, s); return true;
+    case 802: launch_fp8_group_ns<DT, DT_OUT, D, 8, 2>(a, B, ngroups, wide, s); return true;
+    default: return false;
+  }
+}
+
+template <int DT, int DT_OUT>
+bool launch_fp8_group_dim(const Fp8Args& a, int B, int D, int G, int NS, int ngroups, bool wide, hipStream_t s) {
+  return D == 64 ? launch_fp8_group_gs<DT, DT_OUT, 64>(a, B, G, NS, ngroups, wide, s)
+                 : launch_fp8_group_gs<DT, DT_OUT, 128>(a, B, G, NS, ngroups, wide, s);
+}
+
 int fp8_partitions(const char* fn, void* out, int32_t out_dtype, const void* query, const void* k_cache,
                    const void* v_cache, const void* k_scale, const void* v_scale, const int32_t* block_tables,
                    const int32_t* context_lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t bs,
@@ -294,6 +333,50 @@ extern "C" int paged_attention_decode_append_fp8(void* out, int32_t out_dtype, c
                           v_scale, block_tables, context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size,
                           max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size, workspace,
                           workspace_bytes, q_dtype, host_context_lens, stream, new_key, new_value);
+  if (st != PKV_OK) return st;
+  return paged_attention_decode_reduce(out, out_dtype, context_lens, B, num_q_heads, head_dim, max_context_len,
+                                       partition_size, workspace, workspace_bytes, stream);
+}
+
+extern "C" int paged_attention_decode_grouped_fp8(void* out, int32_t out_dtype, const void* query, const void* k_cache,
+                                                  const void* v_cache, const void* k_scale, const void* v_scale,
+                                                  const int32_t* block_tables, const int32_t* context_lens, int32_t B,
+                                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                                  int32_t block_size, int32_t max_blocks_per_seq, int32_t num_blocks,
+                                                  int32_t max_context_len, float scale, int32_t partition_size,
+                                                  void* workspace, size_t workspace_bytes, int32_t q_dtype,
+                                                  int32_t group_size, pkv_stream_t stream) {
+  const char* fn = "paged_attention_decode_grouped_fp8";
+  if (group_size < 1) return fail(PKV_EINVAL, "%s: group_size %d", fn, group_size);
+  if (group_size == 1)
+    return paged_attention_decode_fp8(out, out_dtype, query, k_cache, v_cache, k_scale, v_scale, block_tables,
+                                      context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size,
+                                      max_blocks_per_seq, num_blocks, max_context_len, scale, partition_size,
+                                      workspace, workspace_bytes, q_dtype, nullptr, stream);
+  Fp8Args a;
+  bool wide = false, empty = true;
+  int st = fp8_setup(fn, a, wide, empty, out, out_dtype, query, k_cache, v_cache, k_scale, v_scale, block_tables,
+                     context_lens, B, num_q_heads, num_kv_heads, head_dim, block_size, max_blocks_per_seq, num_blocks,
+                     max_context_len, scale, partition_size, workspace, workspace_bytes, q_dtype, nullptr, nullptr,
+                     nullptr);
+  if (st != PKV_OK) return st;
+  const int G = num_q_heads / num_kv_heads;
+  const int cols = group_size * G;
+  if (cols != 8 && cols != 16)
+    return fail(PKV_EUNSUPPORTED, "%s: group_size x (num_q_heads / num_kv_heads) = %d, must be 8 or 16", fn, cols);
+  if (empty) return PKV_OK;
+  const int ngroups = (B + group_size - 1) / group_size;
+  hipStream_t s = as_stream(stream);
+  const bool f32out = out_dtype == PKV_F32;
+  bool ok;
+  if (q_dtype == PKV_BF16)
+    ok = f32out ? launch_fp8_group_dim<PKV_BF16, PKV_F32>(a, B, head_dim, G, group_size, ngroups, wide, s)
+                : launch_fp8_group_dim<PKV_BF16, PKV_BF16>(a, B, head_dim, G, group_size, ngroups, wide, s);
+  else
+    ok = f32out ? launch_fp8_group_dim<PKV_F16, PKV_F32>(a, B, head_dim, G, group_size, ngroups, wide, s)
+                : launch_fp8_group_dim<PKV_F16, PKV_F16>(a, B, head_dim, G, group_size, ngroups, wide, s);
+  if (!ok) return fail(PKV_EUNSUPPORTED, "%s: group_size %d with group %d", fn, group_size, G);
+  st = check_launch(fn);
   if (st != PKV_OK) return st;
   return paged_attention_decode_reduce(out, out_dtype, context_lens, B, num_q_heads, head_dim, max_context_len,
                                        partition_size, workspace, workspace_bytes, stream);

@@ -429,6 +429,16 @@ def paged_attention_decode_fp8(out, query, k_cache, v_cache, k_scale, v_scale, b
     check(lib.paged_attention_decode_fp8(*args, _stream(stream)))
 
 
+def paged_attention_decode_grouped_fp8(out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                                       max_context_len, scale, group_size, partition_size=0, workspace=None,
+                                       stream=None) -> None:
+    """paged_attention_decode_fp8 with sequences group_size to a workgroup, so that blocks their
+    tables share are read once; bit for bit paged_attention_decode_fp8's output."""
+    args = _fp8_decode_args(out, query, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens,
+                            max_context_len, scale, partition_size, workspace, None)
+    check(lib.paged_attention_decode_grouped_fp8(*args[:22], int(group_size), _stream(stream)))
+
+
 def _fp8_prefill_args(out, query, k_cache, v_cache, k_scale, v_scale, block_table, ctx_start, scale):
     N, Hkv, bs, D = _fp8_shapes(k_cache, v_cache, k_scale, v_scale)
     _dev(out, query, block_table)
