@@ -47,10 +47,18 @@ __device__ __forceinline__ void decode_fp8_group_part(const Fp8Args& a, int B, i
   const int pstart = p * a.part_size;
 
   int seq[NS], pend[NS], nparts[NS];
-  int nsteps = 0;
+  // Each member's first table chunk is loaded before its length is known (its index is bounded
+  // by the table row, not by the length), so the first K/V loads wait for one load, not two.
+  int tab_first[NS];
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     seq[s] = grp * NS + s;
+    const int32_t* row = a.tables + static_cast<int64_t>(seq[s] < B ? seq[s] : 0) * a.max_blocks;
+    tab_first[s] = row[min((pstart >> 4) + lane, a.max_blocks - 1)];
+  }
+  int nsteps = 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
     const int L = seq[s] < B ? clamp_len_f8(a, seq[s]) : 0;
     pend[s] = L > pstart ? min(pstart + a.part_size, L) : pstart;
     nparts[s] = (L + a.part_size - 1) / a.part_size;
@@ -107,7 +115,7 @@ __device__ __forceinline__ void decode_fp8_group_part(const Fp8Args& a, int B, i
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int32_t* row = a.tables + static_cast<int64_t>(seq[s] < B ? seq[s] : 0) * a.max_blocks;
-      tab[s] = clamp_blk_f8(a, row[min(cb0 + lane, a.max_blocks - 1)]);
+      tab[s] = clamp_blk_f8(a, c0 == 0 ? tab_first[s] : row[min(cb0 + lane, a.max_blocks - 1)]);
       cnb[s] = min(2 * kTableSteps, ((pend[s] + 15) >> 4) - cb0);
     }
     auto blocks_of = [&](int s_tab, int s_cnb, int t, int& bA, int& bB) {
