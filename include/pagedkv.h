@@ -174,6 +174,8 @@ size_t paged_attention_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_he
  *   block_tables   device int32 [B][max_blocks_per_seq]; row b lists sequence b's physical blocks
  *                  in logical order; entries past ceil(context_lens[b] / block_size) are not read.
  *   context_lens   device int32 [B]; tokens of sequence b, counting this step's appended token.
+ *                  A sequence with no token (0, or a negative value) has nothing to attend to:
+ *                  its rows of `out` are not written, and the other rows do not change.
  *   max_context_len host-known upper bound of context_lens (sizes the grid without a sync);
  *                  must not exceed max_blocks_per_seq * block_size.
  *   scale          score multiplier (1 / sqrt(head_dim) in the usual case).
