@@ -226,22 +226,32 @@ def measure_prefill(args, dev, fp8=False):
     table, _ = pool.block_tables([s], wl.blocks_for(ctx + C))
     g = torch.Generator(device=dev)
     g.manual_seed(w.seed)
-    q = torch.randn((C, Hq, D), generator=g, device=dev).to(torch.bfloat16)
-    out = torch.empty((C, Hq, D), dtype=torch.float32, device=dev)
     tb = torch.from_numpy(table[0]).to(dev)
-    if fp8:
-        k, v, ks, vs = ops.fp8_cache(w.num_blocks, Hkv, D, device=dev)
-        T = ctx + C
-        slots = torch.from_numpy((table[0][np.arange(T) // 16].astype(np.int64) * 16 + np.arange(T) % 16)
-                                 .astype(np.int32)).to(dev)
-        kr = torch.randn((T, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
-        vr = torch.randn((T, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
-        ops.paged_cache_append_fp8(k, v, ks, vs, kr, vr, slots)
-        fn = lambda i: ops.paged_attention_prefill_chunk_fp8(out, q, k, v, ks, vs, tb, ctx, w.scale)  # noqa: E731
-    else:
-        k = torch.randn((w.num_blocks, Hkv, 16 * D), generator=g, device=dev).to(torch.bfloat16)
-        v = torch.randn((w.num_blocks, Hkv, 16 * D), generator=g, device=dev).to(torch.bfloat16)
-        fn = lambda i: ops.paged_attention_prefill_chunk(out, q, k, v, tb, ctx, w.scale)  # noqa: E731
+    # Replicas of the whole input (caches, queries, output) rotated call by call, at least 1 GiB
+    # in all, so that no call finds the previous one's K/V in the last-level cache.
+    per_rep = 2 * w.num_blocks * Hkv * 16 * (D + 4 if fp8 else 2 * D) + C * Hq * D * 6
+    R = max(1, math.ceil((1 << 30) / per_rep))
+    T = ctx + C
+    slots = torch.from_numpy((table[0][np.arange(T) // 16].astype(np.int64) * 16 + np.arange(T) % 16)
+                             .astype(np.int32)).to(dev)
+    calls = []
+    for r in range(R):
+        q = torch.randn((C, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+        out = torch.empty((C, Hq, D), dtype=torch.float32, device=dev)
+        if fp8:
+            k, v, ks, vs = ops.fp8_cache(w.num_blocks, Hkv, D, device=dev)
+            kr = torch.randn((T, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+            vr = torch.randn((T, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+            ops.paged_cache_append_fp8(k, v, ks, vs, kr, vr, slots)
+            del kr, vr
+            calls.append(lambda out=out, q=q, k=k, v=v, ks=ks, vs=vs:
+                         ops.paged_attention_prefill_chunk_fp8(out, q, k, v, ks, vs, tb, ctx, w.scale))
+        else:
+            k = torch.randn((w.num_blocks, Hkv, 16 * D), generator=g, device=dev).to(torch.bfloat16)
+            v = torch.randn((w.num_blocks, Hkv, 16 * D), generator=g, device=dev).to(torch.bfloat16)
+            calls.append(lambda out=out, q=q, k=k, v=v: ops.paged_attention_prefill_chunk(out, q, k, v, tb, ctx,
+                                                                                            w.scale))
+    fn = lambda i: calls[i % R]()  # noqa: E731
     for i in range(5):
         fn(i)
     us = _events_avg_us(torch, torch.cuda.current_stream(), fn, max(20, args.steps // 4))
@@ -252,6 +262,7 @@ def measure_prefill(args, dev, fp8=False):
         "workload": f"prefill_chunk_{C}_after_{ctx}_gqa{Hq}x{Hkv}_d{D}_" + ("fp8_cache_bf16_query" if fp8 else "bf16"),
         "us_per_call": round(us, 3),
         "flops_per_call": flops,
+        "replicas": R,
         "roofline": {"bound": "mfma", "kernel": "prefill_fp8_kernel" if fp8 else "prefill_mfma_kernel",
                      "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4),

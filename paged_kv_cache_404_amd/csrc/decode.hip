@@ -49,43 +49,55 @@ __global__ void __launch_bounds__(64) decode_valu_kernel(DecodeArgs a) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Log-sum-exp merge of partitions.  grid = (Hq, B), 128 threads.  MAXP >= max_parts (up to 64).
-// The context length comes first: rows of single-partition sequences were written by the
-// partition pass and end here, and the others load only their own partitions' partials (all at
-// once: (m, l) through LDS, one dimension of every partial per thread), not max_parts of them.
+// Log-sum-exp merge of partitions.  grid = (Hq, B), D threads (D = 64 or 128, so the partials'
+// offsets are constants).  MAXP >= max_parts (up to 64).  The context length comes first: rows
+// of single-partition sequences were written by the partition pass and end here, and the others
+// read only their own partitions' partials, all at once (one dimension of every partial per
+// thread).  The maximum over the partitions and each partition's weight are formed once per
+// workgroup; the sums run over the partitions in order, as in the loop form below.
 // ------------------------------------------------------------------------------------------
-template <int DT_OUT, int MAXP>
-__global__ void __launch_bounds__(128) decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ part_ml,
-                                                            const float* __restrict__ part_o,
-                                                            const int32_t* __restrict__ lens, int32_t Hq, int32_t D,
-                                                            int32_t max_parts, int32_t part_size) {
+template <int DT_OUT, int MAXP, int D>
+__global__ void __launch_bounds__(D) decode_reduce_kernel(void* __restrict__ out, const float* __restrict__ part_ml,
+                                                          const float* __restrict__ part_o,
+                                                          const int32_t* __restrict__ lens, int32_t Hq,
+                                                          int32_t max_parts, int32_t part_size) {
+  static_assert(MAXP <= D && MAXP <= 64, "one lane of the first wave per partition for (m, l)");
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int d = threadIdx.x;
   const int L = min(lens[b], max_parts * part_size);
   const int nparts = (L + part_size - 1) / part_size;
-  if (nparts <= 1) return;
+  if (nparts <= 1) return;  // uniform over the workgroup
   const int64_t row0 = (static_cast<int64_t>(b) * Hq + h) * max_parts;
-  __shared__ float sm[MAXP], sl[MAXP];
-  // Thread p fetches partition p's (m, l); every thread fetches its dimension of every partial.
-  if (d < MAXP) {
-    const bool in = d < nparts;
-    sm[d] = in ? part_ml[(row0 + d) * 2] : -INFINITY;
-    sl[d] = in ? part_ml[(row0 + d) * 2 + 1] : 0.f;
+  const float* __restrict__ po = part_o + row0 * D;  // this row's partials, partition-major
+  // Lane p of the first wave fetches partition p's (m, l); every thread fetches its dimension of
+  // every partial (slots past the sequence's own partitions re-read its last one: one load per
+  // slot, no branch, no extra line).
+  float pm = -INFINITY, pl = 0.f;
+  if (d < nparts) {
+    pm = part_ml[(row0 + d) * 2];
+    pl = part_ml[(row0 + d) * 2 + 1];
   }
   float o[MAXP];
 #pragma unroll
-  for (int p = 0; p < MAXP; ++p) o[p] = (p < nparts && d < D) ? part_o[(row0 + p) * D + d] : 0.f;
+  for (int p = 0; p < MAXP; ++p) o[p] = po[min(p, nparts - 1) * D + d];
+  // The first wave forms the maximum of the partitions' maxima and each partition's weight
+  // exp2(m_p - M) once; every thread then sums over the partitions in order.
+  __shared__ float sf[MAXP], sl[MAXP];
+  if (d < 64) {
+    const bool in = d < MAXP && d < nparts;
+    const float M = wave_max(in ? pm : -INFINITY);
+    if (d < MAXP) {
+      sf[d] = in ? fast_exp2(pm - M) : 0.f;
+      sl[d] = in ? pl : 0.f;
+    }
+  }
   __syncthreads();
-  if (d >= D) return;
-  float M = -INFINITY;
-#pragma unroll
-  for (int p = 0; p < MAXP; ++p) M = p < nparts ? fmaxf(M, sm[p]) : M;
   float acc = 0.f, lsum = 0.f;
 #pragma unroll
   for (int p = 0; p < MAXP; ++p) {
     if (p < nparts) {
-      const float f = fast_exp2(sm[p] - M);
+      const float f = sf[p];
       acc += f * o[p];
       lsum += f * sl[p];
     }
@@ -181,25 +193,35 @@ int launch_partitions(const DecodeArgs& a, int32_t dtype, int32_t out_dtype, int
   }
 }
 
+template <int DT_OUT, int D>
+void launch_reduce_d(void* out, const float* ml, const float* po, const int32_t* lens, int B, int Hq, int max_parts,
+                     int part_size, hipStream_t s) {
+  const dim3 grid(Hq, B), block(D);
+  if (max_parts <= 4)
+    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 4, D>), grid, block, 0, s, out, ml, po, lens, Hq, max_parts,
+                       part_size);
+  else if (max_parts <= 8)
+    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 8, D>), grid, block, 0, s, out, ml, po, lens, Hq, max_parts,
+                       part_size);
+  else if (max_parts <= 16)
+    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 16, D>), grid, block, 0, s, out, ml, po, lens, Hq, max_parts,
+                       part_size);
+  else if (max_parts <= 32)
+    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 32, D>), grid, block, 0, s, out, ml, po, lens, Hq, max_parts,
+                       part_size);
+  else
+    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 64, D>), grid, block, 0, s, out, ml, po, lens, Hq, max_parts,
+                       part_size);
+}
+
 template <int DT_OUT>
 void launch_reduce_t(void* out, const float* ml, const float* po, const int32_t* lens, int B, int Hq, int D,
                      int max_parts, int part_size, hipStream_t s) {
-  const dim3 grid(Hq, B), block(128);
-  if (max_parts <= 4)
-    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 4>), grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
-                       part_size);
-  else if (max_parts <= 8)
-    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 8>), grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
-                       part_size);
-  else if (max_parts <= 16)
-    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 16>), grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
-                       part_size);
-  else if (max_parts <= 32)
-    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 32>), grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
-                       part_size);
-  else if (max_parts <= 64)
-    hipLaunchKernelGGL((decode_reduce_kernel<DT_OUT, 64>), grid, block, 0, s, out, ml, po, lens, Hq, D, max_parts,
-                       part_size);
+  const dim3 grid(Hq, B);
+  if (max_parts <= 64 && D == 64)
+    launch_reduce_d<DT_OUT, 64>(out, ml, po, lens, B, Hq, max_parts, part_size, s);
+  else if (max_parts <= 64 && D == 128)
+    launch_reduce_d<DT_OUT, 128>(out, ml, po, lens, B, Hq, max_parts, part_size, s);
   else
     hipLaunchKernelGGL((decode_reduce_loop_kernel<DT_OUT>), grid, dim3(D), 0, s, out, ml, po, lens, Hq, D,
                        max_parts, part_size);
