@@ -83,15 +83,35 @@ __device__ __forceinline__ void decode_valu_part(const DecodeArgs& a, const int 
   for (int i = 0; i < DPL; ++i) o[i] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
   __shared__ float sp[64];        // the chunk's weights
-  __shared__ int64_t stile[8];    // the tile of each 8-token group of the chunk
 
   for (int c0 = pstart; c0 < pend; c0 += 64) {
     const int t = c0 + lane;
     const bool valid = t < pend;
+    const int n = min(64, pend - c0);
     int64_t tile = 0;
+    if (valid) tile = (static_cast<int64_t>(clamp_blk(a, table[t / kBlock])) * a.Hkv + g) * kBlock * D;
+    // The chunk's V: each lane's dimensions of every 8-token group, requested before the scores
+    // (an 8-token group shares its block and half; its tile comes from the group's first lane).
+    u32x4 vr[8][DPL][VW];
+#pragma unroll
+    for (int g8 = 0; g8 < 8; ++g8) {
+      const int64_t gt = (static_cast<int64_t>(__builtin_amdgcn_readlane(static_cast<int>(tile >> 32), 8 * g8)) << 32) |
+                         static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(tile), 8 * g8));
+      const int half = ((c0 + 8 * g8) & 15) >> 3;
+#pragma unroll
+      for (int k = 0; k < DPL; ++k) {
+        const int d = lane + 64 * k;
+#pragma unroll
+        for (int wv = 0; wv < VW; ++wv) vr[g8][k][wv] = u32x4{0, 0, 0, 0};
+        if (8 * g8 < n && d < D) {
+          const uint8_t* vb = static_cast<const uint8_t*>(a.v) + (gt + (static_cast<int64_t>(half) * D + d) * 8) * ES;
+#pragma unroll
+          for (int wv = 0; wv < VW; ++wv) vr[g8][k][wv] = *reinterpret_cast<const u32x4*>(vb + 16 * wv);
+        }
+      }
+    }
     float s = -INFINITY;
     if (valid) {
-      tile = (static_cast<int64_t>(clamp_blk(a, table[t / kBlock])) * a.Hkv + g) * kBlock * D;
       const int off = t % kBlock;
       float acc = 0.f;
       if (fused && t == tn) {
@@ -117,35 +137,30 @@ __device__ __forceinline__ void decode_valu_part(const DecodeArgs& a, const int 
 #pragma unroll
     for (int i = 0; i < DPL; ++i) o[i] *= alpha;
     sp[lane] = pt;
-    if ((lane & 7) == 0) stile[lane >> 3] = tile;  // an 8-token group shares its block and half
     __syncthreads();
     // Weighted sum, token by token in order: each lane's dimension d of 8 consecutive tokens is
-    // 8 contiguous elements of the V tile ([half][D][8]), fetched for every group at once.
-    const int n = min(64, pend - c0);
-    for (int g8 = 0; g8 * 8 < n; ++g8) {
-      const int64_t gt = stile[g8];
-      const int half = ((c0 + 8 * g8) & 15) >> 3;
+    // 8 contiguous elements of the V tile ([half][D][8]).
 #pragma unroll
-      for (int k = 0; k < DPL; ++k) {
-        const int d = lane + 64 * k;
-        if (d < D) {
-          const uint8_t* vb = static_cast<const uint8_t*>(a.v) + (gt + (static_cast<int64_t>(half) * D + d) * 8) * ES;
-          u32x4 vr[VW];
+    for (int g8 = 0; g8 < 8; ++g8) {
+      if (8 * g8 < n) {
 #pragma unroll
-          for (int wv = 0; wv < VW; ++wv) vr[wv] = *reinterpret_cast<const u32x4*>(vb + 16 * wv);
+        for (int k = 0; k < DPL; ++k) {
+          const int d = lane + 64 * k;
+          if (d < D) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int i = 8 * g8 + e;
-            if (i < n) {
-              const float v = (fused && c0 + i == tn) ? elem_to_float<DT>(a.new_v, nrow + d)
-                                                      : chunk_elem<DT>(vr[e / E], e % E);
-              o[k] += sp[i] * v;
+            for (int e = 0; e < 8; ++e) {
+              const int i = 8 * g8 + e;
+              if (i < n) {
+                const float v = (fused && c0 + i == tn) ? elem_to_float<DT>(a.new_v, nrow + d)
+                                                        : chunk_elem<DT>(vr[g8][k][e / E], e % E);
+                o[k] += sp[i] * v;
+              }
             }
           }
         }
       }
     }
-    __syncthreads();  // the weights and tiles are rewritten by the next chunk
+    __syncthreads();  // the weights are rewritten by the next chunk
     m_run = m_new;
   }
 #pragma unroll
