@@ -110,6 +110,13 @@ __device__ __forceinline__ void decode_valu_part(const DecodeArgs& a, const int 
         }
       }
     }
+    // Fused append: the new token's V elements of this lane's dimensions, requested with the rest.
+    float nvv[DPL];
+#pragma unroll
+    for (int k = 0; k < DPL; ++k) {
+      const int d = lane + 64 * k;
+      nvv[k] = (fused && tn >= c0 && tn < c0 + n && d < D) ? elem_to_float<DT>(a.new_v, nrow + d) : 0.f;
+    }
     float s = -INFINITY;
     if (valid) {
       const int off = t % kBlock;
@@ -151,8 +158,7 @@ __device__ __forceinline__ void decode_valu_part(const DecodeArgs& a, const int 
             for (int e = 0; e < 8; ++e) {
               const int i = 8 * g8 + e;
               if (i < n) {
-                const float v = (fused && c0 + i == tn) ? elem_to_float<DT>(a.new_v, nrow + d)
-                                                        : chunk_elem<DT>(vr[g8][k][e / E], e % E);
+                const float v = (fused && c0 + i == tn) ? nvv[k] : chunk_elem<DT>(vr[g8][k][e / E], e % E);
                 o[k] += sp[i] * v;
               }
             }
