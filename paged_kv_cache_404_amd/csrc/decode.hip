@@ -105,28 +105,52 @@ __global__ void __launch_bounds__(D) decode_reduce_kernel(void* __restrict__ out
   store_from_float<DT_OUT>(out, (static_cast<int64_t>(b) * Hq + h) * D + d, acc / lsum);
 }
 
-// Any number of partitions: the same merge, loads in a loop.
-template <int DT_OUT>
-__global__ void __launch_bounds__(128) decode_reduce_loop_kernel(void* __restrict__ out,
-                                                                 const float* __restrict__ part_ml,
-                                                                 const float* __restrict__ part_o,
-                                                                 const int32_t* __restrict__ lens, int32_t Hq,
-                                                                 int32_t D, int32_t max_parts, int32_t part_size) {
+// Any number of partitions: the same merge, 64 partitions at a time (M first, over all of them;
+// then each slice's weights formed once and its partials requested at once, the sums in order).
+template <int DT_OUT, int D>
+__global__ void __launch_bounds__(D) decode_reduce_loop_kernel(void* __restrict__ out,
+                                                               const float* __restrict__ part_ml,
+                                                               const float* __restrict__ part_o,
+                                                               const int32_t* __restrict__ lens, int32_t Hq,
+                                                               int32_t max_parts, int32_t part_size) {
   const int h = blockIdx.x;
   const int b = blockIdx.y;
   const int d = threadIdx.x;
   const int L = min(lens[b], max_parts * part_size);
   const int nparts = (L + part_size - 1) / part_size;
-  if (nparts <= 1 || d >= D) return;
+  if (nparts <= 1) return;  // uniform over the workgroup
   const int64_t row0 = (static_cast<int64_t>(b) * Hq + h) * max_parts;
-  const float* ml = part_ml + row0 * 2;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
+  __shared__ float sf[64], sl[64], sM;
+  if (d < 64) {
+    float x = -INFINITY;
+    for (int p = d; p < nparts; p += 64) x = fmaxf(x, part_ml[(row0 + p) * 2]);
+    x = wave_max(x);
+    if (d == 0) sM = x;
+  }
+  __syncthreads();
+  const float M = sM;
   float acc = 0.f, lsum = 0.f;
-  for (int p = 0; p < nparts; ++p) {
-    const float f = fast_exp2(ml[2 * p] - M);
-    acc += f * part_o[(row0 + p) * D + d];
-    lsum += f * ml[2 * p + 1];
+  for (int p0 = 0; p0 < nparts; p0 += 64) {
+    const int cnt = min(64, nparts - p0);
+    const float* __restrict__ po = part_o + (row0 + p0) * D;
+    float o[64];
+#pragma unroll
+    for (int p = 0; p < 64; ++p) o[p] = po[min(p, cnt - 1) * D + d];
+    if (d < 64) {
+      const bool in = d < cnt;
+      sf[d] = in ? fast_exp2(part_ml[(row0 + p0 + d) * 2] - M) : 0.f;
+      sl[d] = in ? part_ml[(row0 + p0 + d) * 2 + 1] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < 64; ++p) {
+      if (p < cnt) {
+        const float f = sf[p];
+        acc += f * o[p];
+        lsum += f * sl[p];
+      }
+    }
+    __syncthreads();  // sf and sl are rewritten by the next slice
   }
   store_from_float<DT_OUT>(out, (static_cast<int64_t>(b) * Hq + h) * D + d, acc / lsum);
 }
@@ -222,8 +246,11 @@ void launch_reduce_t(void* out, const float* ml, const float* po, const int32_t*
     launch_reduce_d<DT_OUT, 64>(out, ml, po, lens, B, Hq, max_parts, part_size, s);
   else if (max_parts <= 64 && D == 128)
     launch_reduce_d<DT_OUT, 128>(out, ml, po, lens, B, Hq, max_parts, part_size, s);
+  else if (D == 64)
+    hipLaunchKernelGGL((decode_reduce_loop_kernel<DT_OUT, 64>), grid, dim3(64), 0, s, out, ml, po, lens, Hq,
+                       max_parts, part_size);
   else
-    hipLaunchKernelGGL((decode_reduce_loop_kernel<DT_OUT>), grid, dim3(D), 0, s, out, ml, po, lens, Hq, D,
+    hipLaunchKernelGGL((decode_reduce_loop_kernel<DT_OUT, 128>), grid, dim3(128), 0, s, out, ml, po, lens, Hq,
                        max_parts, part_size);
 }
 

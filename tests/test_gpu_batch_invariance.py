@@ -114,3 +114,27 @@ def test_adaptive_single_pass():
         tables, lens_a = m.tables(seqs)
         ref = oatt.paged_decode(t.q, m.cache, tables, lens_a, w.scale)
         assert float(np.abs(got.cpu().numpy().astype(np.float64) - ref).max()) <= ATOL
+
+
+@pytest.mark.parametrize("ps", [16, 32])
+def test_merge_kernel_choice_is_bitwise_invisible(ps):
+    """The split-K merge has a form for up to 64 partitions per sequence and a sliced form for
+    more; which one runs depends on the batch (max_context_len).  A sequence's bits must not: the
+    same sequences merged by the first form (alone, or a batch whose longest context stays within
+    64 partitions) and by the second (max_context_len padded past 64 partitions, or a long
+    batch-mate) agree bit for bit."""
+    lens = [40 * 16, 64 * ps, 3, 17 * ps + 5]  # at most 64 partitions each
+    w = wl.custom_decode(370 + ps, lens + [64 * ps + 1, 130 * ps], 32, 8, 128, "bf16", partition_size=ps)
+    t = wl.decode_tensors(w)
+    m, seqs = build_decode(w, t)
+    short = list(range(len(lens)))
+    small = _decode(m, [seqs[i] for i in short], t.q[short], w.Hq, w.scale, ps, "bf16")
+    tables, _ = m.tables(seqs)
+    padded = _decode(m, [seqs[i] for i in short], t.q[short], w.Hq, w.scale, ps, "bf16",
+                     max_blocks=tables.shape[1], max_context_len=tables.shape[1] * 16)
+    full = _decode(m, seqs, t.q, w.Hq, w.scale, ps, "bf16")
+    assert torch.equal(padded.view(torch.int32), small.view(torch.int32))
+    assert torch.equal(full[short].view(torch.int32), small.view(torch.int32))
+    tables_a, lens_a = m.tables(seqs)
+    ref = oatt.paged_decode(t.q, m.cache, tables_a, lens_a, w.scale)
+    assert float(np.abs(full.cpu().numpy().astype(np.float64) - ref).max()) <= ATOL
