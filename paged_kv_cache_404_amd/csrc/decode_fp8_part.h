@@ -524,11 +524,11 @@ inline int fp8_setup(const char* fn, Fp8Args& a, bool& wide, bool& empty, void* 
   int32_t part_size, max_parts;
   size_t ml_bytes = 0, need = 0;
   if (partition_size <= 0) {
-    part_size = std::max(kBlock, ((max_ctx + kBlock - 1) / kBlock) * kBlock);
+    part_size = std::max(kBlock, static_cast<int32_t>(((static_cast<int64_t>(max_ctx) + kBlock - 1) / kBlock) * kBlock));
     max_parts = 1;
   } else {
     part_size = partition_size;
-    max_parts = (max_ctx + partition_size - 1) / partition_size;
+    max_parts = static_cast<int32_t>((static_cast<int64_t>(max_ctx) + partition_size - 1) / partition_size);
     ml_bytes = align256_f8(static_cast<size_t>(B) * Hq * max_parts * 2 * sizeof(float));
     need = ml_bytes + static_cast<size_t>(B) * Hq * max_parts * D * sizeof(float);
   }

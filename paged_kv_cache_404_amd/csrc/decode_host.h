@@ -23,14 +23,14 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 Plan make_plan(int32_t B, int32_t Hq, int32_t D, int32_t max_ctx, int32_t partition_size) {
   Plan pl{};
   if (partition_size <= 0) {
-    pl.part_size = ((max_ctx + kBlock - 1) / kBlock) * kBlock;
+    pl.part_size = static_cast<int32_t>(((static_cast<int64_t>(max_ctx) + kBlock - 1) / kBlock) * kBlock);
     if (pl.part_size < kBlock) pl.part_size = kBlock;
     pl.max_parts = 1;
     pl.ml_bytes = 0;
     pl.need_bytes = 0;
   } else {
     pl.part_size = partition_size;
-    pl.max_parts = (max_ctx + partition_size - 1) / partition_size;
+    pl.max_parts = static_cast<int32_t>((static_cast<int64_t>(max_ctx) + partition_size - 1) / partition_size);
     pl.ml_bytes = align256(static_cast<size_t>(B) * Hq * pl.max_parts * 2 * sizeof(float));
     pl.need_bytes = pl.ml_bytes + static_cast<size_t>(B) * Hq * pl.max_parts * D * sizeof(float);
   }

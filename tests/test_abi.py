@@ -94,6 +94,11 @@ def test_workspace_size_formula():
     ml = 8 * 32 * parts * 2 * 4
     assert n == ((ml + 255) // 256) * 256 + 8 * 32 * parts * 128 * 4
     assert pkv.lib.paged_attention_decode_workspace_bytes(8, 32, 128, 32768, 0) == 0
+    # a context length at the top of the int32 range: the partition count is formed without
+    # overflow (ceil((2^31 - 1) / 16) = 2^27 partitions)
+    n = pkv.lib.paged_attention_decode_workspace_bytes(1, 1, 64, 2 ** 31 - 1, 16)
+    parts = 2 ** 27
+    assert n == ((parts * 2 * 4 + 255) // 256) * 256 + parts * 64 * 4
 
 
 def test_append_and_prefill_host_validation():
