@@ -126,3 +126,31 @@ def test_random_prefill(i):
     got = out.cpu().numpy().astype(np.float64)
     assert np.isfinite(got).all()
     assert float(np.abs(got - ref).max()) <= ATOL
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_mixed(i):
+    """The mixed launch on random scenes (decode batch and chunks, either part possibly empty):
+    bit for bit the separate decode and prefill launches, within 2e-3 of the oracle."""
+    from .test_gpu_mixed import _check_oracle, _run, _scene
+
+    rng = np.random.default_rng(8000 + i)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    dtype = ["bf16", "f16", "f32"][i % 3]
+    B = int(rng.integers(0, 10))
+    dec_lens = _lengths(rng, B)
+    S = int(rng.integers(0 if B else 1, 4))
+    cmax = 64 if dtype == "f32" else 200
+    chunks = [(int(rng.choice([0, int(rng.integers(1, 60)), int(rng.integers(60, 1200))])),
+               int(rng.integers(1, cmax + 1))) for _ in range(S)]
+    ps = int(rng.choice([0, 0, 64, 256, 512, 1024]))
+    ns = 1
+    if dtype != "f32" and B and i % 2:
+        ns = {1: 8, 2: 4, 4: 2, 8: 2}[G]
+    m, dseqs, pseqs, q_dec, q_pre = _scene(9000 + i, dec_lens, chunks, Hkv * G, Hkv, D, dtype)
+    scale = 1 / np.sqrt(D)
+    dec, pre, dtab, dlens, ptab = _run(m, dseqs, pseqs, chunks, q_dec, q_pre, Hkv * G, D, dtype, scale,
+                                       host_lens=bool(i % 3), ps=ps, ns=ns)
+    _check_oracle(m, dec, pre, dtab, dlens, ptab, q_dec, q_pre, chunks, scale)
