@@ -154,3 +154,22 @@ def test_random_mixed(i):
     dec, pre, dtab, dlens, ptab = _run(m, dseqs, pseqs, chunks, q_dec, q_pre, Hkv * G, D, dtype, scale,
                                        host_lens=bool(i % 3), ps=ps, ns=ns)
     _check_oracle(m, dec, pre, dtab, dlens, ptab, q_dec, q_pre, chunks, scale)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_random_mixed_fp8(i):
+    """paged_attention_mixed_fp8 on random scenes: bit for bit the separate FP8 decode and prefill
+    launches, within 2e-3 of the oracle over code * scale."""
+    from .test_gpu_fp8 import test_mixed_fp8_equals_separate_launches as mixed_fp8_case
+
+    rng = np.random.default_rng(8500 + i)
+    Hkv = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    D = int(rng.choice([64, 128]))
+    B = int(rng.integers(0, 9))
+    dec_lens = _lengths(rng, B)
+    S = int(rng.integers(0 if B else 1, 4))
+    chunks = [(int(rng.choice([0, int(rng.integers(1, 60)), int(rng.integers(60, 1200))])),
+               int(rng.integers(1, 200))) for _ in range(S)]
+    ps = int(rng.choice([0, 0, 64, 256, 512, 1024]))
+    mixed_fp8_case(100 + i, dec_lens, chunks, Hkv * G, Hkv, D, "f16" if i % 3 == 0 else "bf16", ps)
